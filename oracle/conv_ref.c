@@ -1,0 +1,263 @@
+/*
+ * conv_ref.c -- the oracle: a plain, slow, obviously correct CPU convolution.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the package smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or helper with the HIP
+ * library: every formula below is written out again from the pages' definitions.
+ *
+ * Arithmetic: inputs arrive as doubles (bf16 and fp32 values convert to double
+ * exactly), every product and sum is formed in IEEE double, summation runs in
+ * the plain loop order of the definition, with no blocking or reordering.
+ *
+ * Citations name the page and its section:
+ *   [Hand-writing Conv2D, 1.1]  the index map y[n][oc][oh][ow] = bias[oc] +
+ *        sum over (ic, kh, kw) of x[n][ic][oh*s+kh-p][ow*s+kw-p] * w[oc][ic][kh][kw]
+ *        and the output size floor((H + 2p - K)/s) + 1.
+ *   [Hand-writing Conv2D, 1.2]  padding by bounds checks: a tap whose input
+ *        coordinate falls outside [0, H) x [0, W) contributes nothing.
+ *   [Why use matrix multiplication for convolution, 2.2]  the X_col layout:
+ *        row = (ic, kh, kw) flattened, column = output position, width fastest.
+ *   [Why use matrix multiplication for convolution, 3.1]  column index
+ *        n*(H_out*W_out) + oh*W_out + ow.
+ *   [PyTorch tensor products and conv2d/conv3d dimension semantics, 5.1, 5.2]
+ *        NCDHW input, (C_out, C_in, kD, kH, kW) weights, the same size formula
+ *        applied independently to D, H and W.
+ *
+ * Besides y, each convolution returns S = sum over the same taps of |x * w|
+ * (bias excluded), the scale against which a low-precision result is judged.
+ *
+ * Parity pins live in tests/test_oracle_pins.py; every function here is pinned.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <math.h>
+#include <time.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Output length along one spatial dimension: floor((in + 2p - k)/s) + 1
+ * [Hand-writing Conv2D, 1.1].  Returns -1 when the window does not fit even
+ * once (in + 2p < k) or a parameter is out of range; C integer division
+ * truncates toward zero, so the negative numerator is rejected explicitly
+ * rather than silently yielding 1 [Conv2d from the official docs, 3.2]. */
+int64_t oracle_out_dim(int64_t in, int64_t k, int64_t s, int64_t p)
+{
+    if (in < 1 || k < 1 || s < 1 || p < 0) return -1;
+    int64_t num = in + 2 * p - k;
+    if (num < 0) return -1;
+    return num / s + 1;          /* num >= 0 here, so '/' is floor */
+}
+
+/* bf16 bit pattern -> double, exactly: a bf16 is the top 16 bits of a binary32. */
+void oracle_bf16_to_f64(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t bits = ((uint32_t)src[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        dst[i] = (double)f;
+    }
+}
+
+/* binary32 -> double, exactly. */
+void oracle_f32_to_f64(const float *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = (double)src[i];
+}
+
+/* One output element of a 3D convolution (2D is the case D = 1, kd range {0}).
+ * x: (N, C, D, H, W), w: (Co, C, Kd, K, K); kd_size = 1 and pd = 0 for 2D.
+ * Loop order is the definition's: ic, then kd, kh, kw. */
+static void one_output(const double *x, const double *w, int64_t n, int64_t oc,
+                       int64_t od, int64_t oh, int64_t ow,
+                       int64_t C, int64_t D, int64_t H, int64_t W,
+                       int64_t Kd, int64_t K, int64_t s, int64_t sd,
+                       int64_t p, int64_t pd, double *acc_out, double *S_out)
+{
+    double acc = 0.0, S = 0.0;
+    for (int64_t ic = 0; ic < C; ++ic) {
+        for (int64_t kd = 0; kd < Kd; ++kd) {
+            int64_t id = od * sd + kd - pd;
+            if (!(0 <= id && id < D)) continue;          /* [Hand-writing Conv2D, 1.2] */
+            for (int64_t kh = 0; kh < K; ++kh) {
+                int64_t ih = oh * s + kh - p;
+                if (!(0 <= ih && ih < H)) continue;
+                for (int64_t kw = 0; kw < K; ++kw) {
+                    int64_t iw = ow * s + kw - p;
+                    if (!(0 <= iw && iw < W)) continue;
+                    double xv = x[(((n * C + ic) * D + id) * H + ih) * W + iw];
+                    double wv = w[(((oc * C + ic) * Kd + kd) * K + kh) * K + kw];
+                    double t = xv * wv;
+                    acc += t;
+                    S += fabs(t);
+                }
+            }
+        }
+    }
+    *acc_out = acc;
+    *S_out = S;
+}
+
+/* Full 2D convolution, NCHW x OIHW -> NCHW [Hand-writing Conv2D, 1.1 and 2.1].
+ * bias may be NULL (no bias).  S may be NULL.  Returns 0, or -1 on bad shape. */
+int oracle_conv2d(const double *x, const double *w, const double *bias,
+                  double *y, double *S,
+                  int64_t N, int64_t C, int64_t H, int64_t W,
+                  int64_t Co, int64_t K, int64_t s, int64_t p)
+{
+    int64_t Ho = oracle_out_dim(H, K, s, p), Wo = oracle_out_dim(W, K, s, p);
+    if (Ho < 0 || Wo < 0 || N < 1 || C < 1 || Co < 1) return -1;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t oc = 0; oc < Co; ++oc)
+            for (int64_t oh = 0; oh < Ho; ++oh)
+                for (int64_t ow = 0; ow < Wo; ++ow) {
+                    double acc, sa;
+                    one_output(x, w, n, oc, 0, oh, ow, C, 1, H, W, 1, K, s, 1, p, 0, &acc, &sa);
+                    int64_t o = ((n * Co + oc) * Ho + oh) * Wo + ow;
+                    y[o] = acc + (bias ? bias[oc] : 0.0);
+                    if (S) S[o] = sa;
+                }
+    return 0;
+}
+
+/* Full 3D convolution, NCDHW x (Co, C, K, K, K) -> NCDHW, one K, s, p for all
+ * three dimensions [PyTorch tensor products and conv2d/conv3d dimension
+ * semantics, 5.1 and 5.2]. */
+int oracle_conv3d(const double *x, const double *w, const double *bias,
+                  double *y, double *S,
+                  int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                  int64_t Co, int64_t K, int64_t s, int64_t p)
+{
+    int64_t Do = oracle_out_dim(D, K, s, p);
+    int64_t Ho = oracle_out_dim(H, K, s, p), Wo = oracle_out_dim(W, K, s, p);
+    if (Do < 0 || Ho < 0 || Wo < 0 || N < 1 || C < 1 || Co < 1) return -1;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t oc = 0; oc < Co; ++oc)
+            for (int64_t od = 0; od < Do; ++od)
+                for (int64_t oh = 0; oh < Ho; ++oh)
+                    for (int64_t ow = 0; ow < Wo; ++ow) {
+                        double acc, sa;
+                        one_output(x, w, n, oc, od, oh, ow, C, D, H, W, K, K, s, s, p, p, &acc, &sa);
+                        int64_t o = (((n * Co + oc) * Do + od) * Ho + oh) * Wo + ow;
+                        y[o] = acc + (bias ? bias[oc] : 0.0);
+                        if (S) S[o] = sa;
+                    }
+    return 0;
+}
+
+/* Selected outputs only, for checks at sizes where the full tensor is too slow.
+ * idx holds flat NC(D)HW output indices; ndim is 2 or 3 (D ignored for 2). */
+int oracle_conv_points(int ndim, const double *x, const double *w, const double *bias,
+                       const int64_t *idx, int64_t npts, double *y, double *S,
+                       int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                       int64_t Co, int64_t K, int64_t s, int64_t p)
+{
+    int64_t Dd = (ndim == 3) ? D : 1, Kd = (ndim == 3) ? K : 1;
+    int64_t sd = (ndim == 3) ? s : 1, pd = (ndim == 3) ? p : 0;
+    int64_t Do = (ndim == 3) ? oracle_out_dim(D, K, s, p) : 1;
+    int64_t Ho = oracle_out_dim(H, K, s, p), Wo = oracle_out_dim(W, K, s, p);
+    if ((ndim != 2 && ndim != 3) || Do < 0 || Ho < 0 || Wo < 0) return -1;
+    int64_t total = N * Co * Do * Ho * Wo;
+    for (int64_t i = 0; i < npts; ++i)
+        if (idx[i] < 0 || idx[i] >= total) return -1;
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < npts; ++i) {
+        int64_t o = idx[i];
+        int64_t ow = o % Wo; o /= Wo;
+        int64_t oh = o % Ho; o /= Ho;
+        int64_t od = o % Do; o /= Do;
+        int64_t oc = o % Co; o /= Co;
+        int64_t n = o;
+        double acc, sa;
+        one_output(x, w, n, oc, od, oh, ow, C, Dd, H, W, Kd, K, s, sd, p, pd, &acc, &sa);
+        y[i] = acc + (bias ? bias[oc] : 0.0);
+        if (S) S[i] = sa;
+    }
+    return 0;
+}
+
+/* Explicit im2col, 2D [Why use matrix multiplication for convolution, 2.2 and
+ * 3.1]: col has shape (C*K*K, N*Ho*Wo), row r = (ic*K + kh)*K + kw, column
+ * j = n*Ho*Wo + oh*Wo + ow; an out-of-range tap is 0 (zero padding). */
+int oracle_im2col2d(const double *x, double *col,
+                    int64_t N, int64_t C, int64_t H, int64_t W,
+                    int64_t K, int64_t s, int64_t p)
+{
+    int64_t Ho = oracle_out_dim(H, K, s, p), Wo = oracle_out_dim(W, K, s, p);
+    if (Ho < 0 || Wo < 0) return -1;
+    int64_t cols = N * Ho * Wo;
+    for (int64_t ic = 0; ic < C; ++ic)
+        for (int64_t kh = 0; kh < K; ++kh)
+            for (int64_t kw = 0; kw < K; ++kw) {
+                int64_t r = (ic * K + kh) * K + kw;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t oh = 0; oh < Ho; ++oh)
+                        for (int64_t ow = 0; ow < Wo; ++ow) {
+                            int64_t ih = oh * s + kh - p, iw = ow * s + kw - p;
+                            double v = 0.0;
+                            if (0 <= ih && ih < H && 0 <= iw && iw < W)
+                                v = x[((n * C + ic) * H + ih) * W + iw];
+                            col[r * cols + (n * Ho + oh) * Wo + ow] = v;
+                        }
+            }
+    return 0;
+}
+
+/* Explicit im2col, 3D: row r = ((ic*K + kd)*K + kh)*K + kw, column
+ * j = ((n*Do + od)*Ho + oh)*Wo + ow. */
+int oracle_im2col3d(const double *x, double *col,
+                    int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                    int64_t K, int64_t s, int64_t p)
+{
+    int64_t Do = oracle_out_dim(D, K, s, p);
+    int64_t Ho = oracle_out_dim(H, K, s, p), Wo = oracle_out_dim(W, K, s, p);
+    if (Do < 0 || Ho < 0 || Wo < 0) return -1;
+    int64_t cols = N * Do * Ho * Wo;
+    for (int64_t ic = 0; ic < C; ++ic)
+      for (int64_t kd = 0; kd < K; ++kd)
+        for (int64_t kh = 0; kh < K; ++kh)
+          for (int64_t kw = 0; kw < K; ++kw) {
+            int64_t r = ((ic * K + kd) * K + kh) * K + kw;
+            for (int64_t n = 0; n < N; ++n)
+              for (int64_t od = 0; od < Do; ++od)
+                for (int64_t oh = 0; oh < Ho; ++oh)
+                  for (int64_t ow = 0; ow < Wo; ++ow) {
+                    int64_t id = od * s + kd - p, ih = oh * s + kh - p, iw = ow * s + kw - p;
+                    double v = 0.0;
+                    if (0 <= id && id < D && 0 <= ih && ih < H && 0 <= iw && iw < W)
+                        v = x[(((n * C + ic) * D + id) * H + ih) * W + iw];
+                    col[r * cols + ((n * Do + od) * Ho + oh) * Wo + ow] = v;
+                  }
+          }
+    return 0;
+}
+
+/* Plain matrix product C (M x Nn) = A (M x Kk) @ B (Kk x Nn), row-major, fp64,
+ * the GEMM step Y = W_row @ X_col [Why use matrix multiplication for
+ * convolution, 2.3]. */
+void oracle_matmul(const double *A, const double *B, double *Cm,
+                   int64_t M, int64_t Kk, int64_t Nn)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < Nn; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < Kk; ++k) acc += A[i * Kk + k] * B[k * Nn + j];
+            Cm[i * Nn + j] = acc;
+        }
+}
+
+/* Threads the OpenMP runtime will use (1 when built without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

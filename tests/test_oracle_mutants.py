@@ -1,0 +1,50 @@
+"""Planted mistakes in a copy of the oracle must fail the pins.
+
+Each case edits one line of a temporary copy of oracle/conv_ref.c (a plausible
+slip: sign of the padding offset, kh/kw swapped, bias dropped, X_col columns
+transposed, a depth offset lost, |x*w| replaced by x*w, ceil for floor, an
+off-by-one bounds check), builds it with gcc, and runs tests/test_oracle_pins.py
+against that build in a subprocess.  The run must fail.  Runs on the CPU only.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "conv_ref.c")
+
+MUTANTS = {
+    "pad_sign": ("int64_t ih = oh * s + kh - p;", "int64_t ih = oh * s + kh + p;"),
+    "kh_kw_swapped": ("double wv = w[(((oc * C + ic) * Kd + kd) * K + kh) * K + kw];",
+                      "double wv = w[(((oc * C + ic) * Kd + kd) * K + kw) * K + kh];"),
+    "bias_dropped": ("y[o] = acc + (bias ? bias[oc] : 0.0);\n                    if (S) S[o] = sa;\n                }\n    return 0;\n}\n\n/* Full 3D",
+                     "y[o] = acc;\n                    if (S) S[o] = sa;\n                }\n    return 0;\n}\n\n/* Full 3D"),
+    "xcol_columns_transposed": ("col[r * cols + (n * Ho + oh) * Wo + ow] = v;",
+                                "col[r * cols + (n * Wo + ow) * Ho + oh] = v;"),
+    "depth_pad_lost": ("int64_t id = od * sd + kd - pd;", "int64_t id = od * sd + kd;"),
+    "S_signed": ("S += fabs(t);", "S += t;"),
+    "ceil_size": ("return num / s + 1;", "return (num + s - 1) / s + 1;"),
+    "lower_bound_strict": ("if (!(0 <= ih && ih < H)) continue;", "if (!(0 < ih && ih < H)) continue;"),
+    "stride_dropped_w": ("int64_t iw = ow * s + kw - p;\n                    if (!(0 <= iw",
+                         "int64_t iw = ow + kw - p;\n                    if (!(0 <= iw"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found once: %s" % name
+    mutant_c = tmp_path / "conv_ref_mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                           "-o", str(so), str(mutant_c), "-lm"])
+    env = dict(os.environ, CONV_ORACLE_LIB_OVERRIDE=str(so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "planted mistake %r passed every pin:\n%s" % (name, r.stdout[-2000:])
