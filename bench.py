@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: convolution forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--route auto|mfma|valu|explicit]
+                    [--no-cpu-baseline] [--report]
+
+A step is one full forward pass of the convolution (every kernel of the chosen
+route) over one batch of seeded synthetic input that is already resident in
+device memory.  W untimed steps, then exactly K timed steps bracketed by
+torch.cuda.synchronize().  The default workload is the 3x3 layer (N=64,
+C_in=C_out=128, 56x56, stride 1, pad 1, bf16 in, fp32 out).
+
+One JSON line on stdout:
+  value        FLOP/s of the whole job (2*N*C_out*H_out*W_out*C_in*K^2, padded
+               taps included) / measured time, in TFLOP/s
+  roofline     the dominant kernel: algorithmic FLOP (or bytes) per launch over
+               its average launch time from HIP events recorded on the stream
+               the library launches on, against the MI355X peak
+  cpu_baseline the CPU oracle (plain fp64 loops, OpenMP) timed on a bounded
+               sample of the same workload on this host
+--report prints one more line per workload to stderr (all five, every route).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv fwd TFLOP/s + % bf16 MFMA peak (3x3 s1p1, N=64 C=128 56x56)"
+PEAK_BF16_TFLOPS = 2516.6          # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP32_VALU_TFLOPS = 157.3      # packed; 78.6 without packed FMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="conv3x3_bf16")
+    ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-images", type=int, default=0,
+                    help="images in the oracle's timed sample (0 = pick ~10 s of work)")
+    ap.add_argument("--report", action="store_true", help="also time every workload/route (stderr)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl):
+    """x, w, bias read once + y written once (fp32 output)."""
+    esz = 4 if wl.dtype == "f32" else 2
+    x = int(np.prod(wl.x_shape)) * esz
+    w = int(np.prod(wl.w_shape)) * esz
+    b = wl.C_out * 4
+    y = int(np.prod(wl.y_shape)) * 4
+    return x + w + b + y
+
+
+def bound_of(wl, route):
+    if wl.dtype == "f32" or route == "valu":
+        return "alu" if wl.flops() / algorithmic_bytes(wl) > PEAK_FP32_VALU_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return "mfma" if wl.flops() / algorithmic_bytes(wl) > ridge else "hbm"
+
+
+class Runner:
+    """Device-resident inputs and one callable step for a workload/route."""
+
+    def __init__(self, wl, route, seed=None):
+        import torch
+        from cnn_convolution_forward_amd import binding as B
+        from cnn_convolution_forward_amd import synth
+        self.wl, self.route = wl, route
+        self.t = synth.make_inputs(wl, seed=seed)
+        t = self.t
+        if t.x.dtype == np.uint16:
+            self.x = torch.from_numpy(t.x.view(np.int16)).cuda()
+            self.w = torch.from_numpy(t.w.view(np.int16)).cuda()
+        else:
+            self.x = torch.from_numpy(t.x).cuda()
+            self.w = torch.from_numpy(t.w).cuda()
+        self.b = None if t.b is None else torch.from_numpy(t.b).cuda()
+        self.y = torch.empty(wl.y_shape, dtype=torch.float32, device="cuda")
+        self.ws = None
+        if route == "explicit":
+            nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
+                                         wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.B = B
+
+    def step(self):
+        if self.route == "explicit":
+            self.B.conv_explicit(self.x, self.w, self.b, self.wl.stride, self.wl.pad,
+                                 workspace=self.ws, out=self.y)
+        else:
+            self.B.conv(self.x, self.w, self.b, self.wl.stride, self.wl.pad, algo=self.route, out=self.y)
+
+
+def time_steps(runner, steps, warmup):
+    """Wall time of `steps` steps (synchronised on both sides) and per-step HIP
+    event durations recorded on the stream the library launches on."""
+    import torch
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        runner.step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3     # seconds
+    return wall, per
+
+
+def cpu_baseline(wl, runner, sample_images):
+    """Time the oracle on the first `sample_images` images of the same inputs;
+    also report the parity of the GPU output on that sample."""
+    import oracle
+    t = runner.t
+    n = sample_images
+    xs = t.x[:n]
+    f = oracle.conv2d if wl.ndim == 2 else oracle.conv3d
+    t0 = time.perf_counter()
+    y_ref, S = f(xs, t.w, t.b, wl.stride, wl.pad)
+    dt = time.perf_counter() - t0
+    flops = wl.flops() * n / wl.N
+    y_gpu = runner.y[:n].cpu().numpy().astype(np.float64)
+    d = np.abs(y_gpu - y_ref)
+    tau = 1e-3 if wl.dtype == "bf16" else 1e-5
+    ok = bool(np.all(d <= tau * S))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = float(np.max(np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d of %d images of the same seeded inputs, one full pass, fp64" % (n, wl.N),
+            "parity_on_sample": {"max_abs_delta_over_S": rel, "tau": tau, "pass": ok}}
+
+
+def describe(wl):
+    return {"workload": wl.name, "x": list(wl.x_shape), "w": list(wl.w_shape), "y": list(wl.y_shape),
+            "stride": wl.stride, "pad": wl.pad, "in_dtype": wl.dtype, "out_dtype": "f32",
+            "seed": wl.seed, "flop_per_step": wl.flops(), "algorithmic_bytes_per_step": algorithmic_bytes(wl)}
+
+
+def measure(wl, route, steps, warmup):
+    runner = Runner(wl, route)
+    wall, per = time_steps(runner, steps, warmup)
+    return runner, wall, per
+
+
+def report_all(steps, warmup):
+    from cnn_convolution_forward_amd import synth
+    for name, wl in synth.WORKLOADS.items():
+        routes = ["valu"] if wl.dtype == "f32" else ["auto", "mfma", "valu", "explicit"]
+        for route in routes:
+            _, wall, per = measure(wl, route, steps, warmup)
+            t = float(np.mean(per))
+            line = {"workload": name, "route": route, "us_per_call": round(t * 1e6, 2),
+                    "TFLOP/s": round(wl.flops() / t / 1e12, 2),
+                    "pct_bf16_mfma_peak": round(100 * wl.flops() / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "algorithmic_GB/s": round(algorithmic_bytes(wl) / t / 1e9, 1),
+                    "pct_hbm_peak": round(100 * algorithmic_bytes(wl) / t / 1e9 / PEAK_HBM_GBS, 2)}
+            print(json.dumps(line), file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this engine has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    from cnn_convolution_forward_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    print("bench: %s route=%s steps=%d warmup=%d" % (wl.name, args.route, args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+    runner, wall, per = measure(wl, args.route, args.steps, args.warmup)
+    flops = wl.flops()
+    value = flops * args.steps / wall / 1e12
+    kern = float(np.mean(per))
+    bound = bound_of(wl, args.route)
+    if bound == "mfma":
+        ach, peak, unit = flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "alu":
+        ach, peak, unit = flops / kern / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
+    else:
+        ach, peak, unit = algorithmic_bytes(wl) / kern / 1e9, PEAK_HBM_GBS, "GB/s"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded PCG64; x N(0,1), w N(0,1/sqrt(fan_in)), b U[-1,1]; bf16 by RNE)",
+        "config": describe(wl) | {"route": args.route},
+        "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4), "traffic": None,
+                     "kernel_avg_us": round(kern * 1e6, 3), "kernel_median_us": round(float(np.median(per)) * 1e6, 3),
+                     "timing": "HIP events around each launch on the library's stream"},
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_images or max(1, min(wl.N, 16))
+        out["cpu_baseline"] = cpu_baseline(wl, runner, n)
+    print(json.dumps(out), flush=True)
+    if args.report:
+        report_all(max(5, args.steps // 5), max(2, args.warmup // 2))
+
+
+if __name__ == "__main__":
+    main()

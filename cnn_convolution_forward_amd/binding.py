@@ -1,0 +1,264 @@
+"""Thin ctypes binding to libconvfwd.so (argument marshalling only).
+
+The functions named like the C ABI (``conv2d_fwd_bf16`` ...) take raw device
+pointers (ints) and sizes, exactly as declared in ``include/conv_fwd.h``, and
+return the status code.  The ``conv2d`` / ``conv3d`` / ``im2col`` helpers take
+torch tensors that already live on the GPU, allocate the output with torch
+(device memory and streams are all torch is used for), pass pointers and the
+current HIP stream, and raise :class:`ConvError` on a non-OK status.  Every
+arithmetic step runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libconvfwd.so")
+
+CONV_OK = 0
+STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_NULL", 2: "CONV_ERR_PARAM", 3: "CONV_ERR_SHAPE",
+                4: "CONV_ERR_OVERFLOW", 5: "CONV_ERR_ALIAS", 6: "CONV_ERR_WORKSPACE",
+                7: "CONV_ERR_ALGO", 8: "CONV_ERR_HIP"}
+ALGO = {"auto": 0, "mfma": 1, "valu": 2}
+
+# Every symbol include/conv_fwd.h declares.
+EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
+           "conv2d_fwd_bf16", "conv2d_fwd_f32", "conv3d_fwd_bf16", "conv3d_fwd_f32",
+           "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
+           "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit")
+
+
+class ConvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS_NAMES.get(status, status), status_str(status)))
+
+
+_lib = None
+_vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+
+def lib():
+    """Load libconvfwd.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libconvfwd.so is not built (%s); run "
+                              "`python -m cnn_convolution_forward_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.conv_out_dim.restype = _i64
+        L.conv_out_dim.argtypes = [_i64] * 4
+        L.conv_status_str.restype = ctypes.c_char_p
+        L.conv_status_str.argtypes = [_i]
+        L.conv_version.restype = _i
+        L.conv_version.argtypes = []
+        d2 = [_vp, _vp, _vp, _vp] + [_i] * 9 + [_vp]
+        d3 = [_vp, _vp, _vp, _vp] + [_i] * 10 + [_vp]
+        for name, args in (("conv2d_fwd_bf16", d2), ("conv2d_fwd_f32", d2),
+                           ("conv3d_fwd_bf16", d3), ("conv3d_fwd_f32", d3)):
+            getattr(L, name).restype = _i
+            getattr(L, name).argtypes = args
+        L.conv_im2col_bytes.restype = _sz
+        L.conv_im2col_bytes.argtypes = [_i] * 9
+        L.conv2d_im2col_bf16.restype = _i
+        L.conv2d_im2col_bf16.argtypes = [_vp, _vp] + [_i] * 7 + [_vp]
+        L.conv3d_im2col_bf16.restype = _i
+        L.conv3d_im2col_bf16.argtypes = [_vp, _vp] + [_i] * 8 + [_vp]
+        L.conv2d_fwd_bf16_explicit.restype = _i
+        L.conv2d_fwd_bf16_explicit.argtypes = [_vp] * 5 + [_sz] + [_i] * 8 + [_vp]
+        L.conv3d_fwd_bf16_explicit.restype = _i
+        L.conv3d_fwd_bf16_explicit.argtypes = [_vp] * 5 + [_sz] + [_i] * 9 + [_vp]
+        _lib = L
+    return _lib
+
+
+# ---- the C ABI, same names, raw pointers -------------------------------------
+
+def conv_out_dim(n, k, stride, pad):
+    return int(lib().conv_out_dim(n, k, stride, pad))
+
+
+def status_str(status):
+    return lib().conv_status_str(int(status)).decode()
+
+
+def conv_status_str(status):
+    return status_str(status)
+
+
+def conv_version():
+    return int(lib().conv_version())
+
+
+def conv2d_fwd_bf16(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv2d_fwd_bf16(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv2d_fwd_f32(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv2d_fwd_f32(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv3d_fwd_bf16(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv3d_fwd_bf16(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv3d_fwd_f32(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv3d_fwd_f32(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv_im2col_bytes(ndim, N, C_in, D, H, W, K, stride, pad):
+    return int(lib().conv_im2col_bytes(ndim, N, C_in, D, H, W, K, stride, pad))
+
+
+def conv2d_im2col_bf16(x, xcol, N, C_in, H, W, K, stride, pad, stream=None):
+    return lib().conv2d_im2col_bf16(x, xcol, N, C_in, H, W, K, stride, pad, stream)
+
+
+def conv3d_im2col_bf16(x, xcol, N, C_in, D, H, W, K, stride, pad, stream=None):
+    return lib().conv3d_im2col_bf16(x, xcol, N, C_in, D, H, W, K, stride, pad, stream)
+
+
+def conv2d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad,
+                             stream=None):
+    return lib().conv2d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K,
+                                          stride, pad, stream)
+
+
+def conv3d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, D, H, W, C_out, K, stride, pad,
+                             stream=None):
+    return lib().conv3d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, D, H, W, C_out, K,
+                                          stride, pad, stream)
+
+
+# ---- torch-tensor helpers (device memory + stream plumbing only) --------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(t, name, dtypes):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (NCHW / OIHW dense)" % name)
+    _ = torch
+
+
+def _dims(x, w, ndim):
+    if x.dim() != ndim + 2 or w.dim() != ndim + 2:
+        raise ValueError("expected %d-D x and w, got %s and %s" % (ndim + 2, tuple(x.shape), tuple(w.shape)))
+    K = w.shape[2]
+    if any(k != K for k in w.shape[2:]):
+        raise ValueError("only square/cubic kernels are supported")
+    if w.shape[1] != x.shape[1]:
+        raise ValueError("w.shape[1]=%d != C_in=%d" % (w.shape[1], x.shape[1]))
+    return K
+
+
+def _out_shape(x, w, stride, pad, ndim):
+    K = w.shape[2]
+    outs = [conv_out_dim(d, K, stride, pad) for d in x.shape[2:]]
+    return (x.shape[0], w.shape[0], *outs)
+
+
+def conv(x, w, bias=None, stride=1, pad=0, algo="auto", out=None):
+    """y = conv(x, w) + bias on the GPU.  x/w: bf16 (torch.bfloat16 or int16/uint16
+    bit patterns) or float32, dense NC(D)HW / OI(D)HW; bias float32 or None.
+    Returns float32 y.  2D or 3D by x.dim()."""
+    torch = _torch()
+    ndim = x.dim() - 2
+    if ndim not in (2, 3):
+        raise ValueError("x must be 4-D (NCHW) or 5-D (NCDHW)")
+    f32 = x.dtype == torch.float32
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_tensor(x, "x", (torch.float32,) if f32 else half)
+    _check_tensor(w, "w", (torch.float32,) if f32 else half)
+    _check_tensor(bias, "bias", (torch.float32,))
+    K = _dims(x, w, ndim)
+    shape = _out_shape(x, w, stride, pad, ndim)
+    if min(shape[2:]) < 1:
+        raise ConvError(3, "conv")
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check_tensor(y, "out", (torch.float32,))
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    args = [_ptr(x), _ptr(w), _ptr(bias), _ptr(y), x.shape[0], x.shape[1], *x.shape[2:],
+            w.shape[0], K, stride, pad, a, _stream()]
+    if ndim == 2:
+        st = (conv2d_fwd_f32 if f32 else conv2d_fwd_bf16)(*args)
+    else:
+        st = (conv3d_fwd_f32 if f32 else conv3d_fwd_bf16)(*args)
+    if st != CONV_OK:
+        raise ConvError(st, "conv%dd_fwd" % ndim)
+    return y
+
+
+def im2col(x, K, stride=1, pad=0, out=None):
+    """Explicit X_col (C_in*K^dims, N*prod(out)) as int16 bf16 bit patterns."""
+    torch = _torch()
+    ndim = x.dim() - 2
+    _check_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    N, C = x.shape[:2]
+    sp = list(x.shape[2:])
+    D = sp[0] if ndim == 3 else 1
+    nbytes = conv_im2col_bytes(ndim, N, C, D, sp[-2], sp[-1], K, stride, pad)
+    if nbytes == 0:
+        raise ConvError(2, "conv_im2col_bytes")
+    outs = [conv_out_dim(d, K, stride, pad) for d in sp]
+    cols = N
+    for o in outs:
+        cols *= o
+    rows = C * K ** ndim
+    col = out if out is not None else torch.empty((rows, cols), dtype=torch.int16, device=x.device)
+    if ndim == 2:
+        st = conv2d_im2col_bf16(_ptr(x), _ptr(col), N, C, sp[0], sp[1], K, stride, pad, _stream())
+    else:
+        st = conv3d_im2col_bf16(_ptr(x), _ptr(col), N, C, D, sp[1], sp[2], K, stride, pad, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv%dd_im2col_bf16" % ndim)
+    return col
+
+
+def conv_explicit(x, w, bias=None, stride=1, pad=0, workspace=None, out=None):
+    """im2col into a workspace, then the MFMA GEMM; returns float32 y."""
+    torch = _torch()
+    ndim = x.dim() - 2
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_tensor(x, "x", half)
+    _check_tensor(w, "w", half)
+    _check_tensor(bias, "bias", (torch.float32,))
+    K = _dims(x, w, ndim)
+    N, C = x.shape[:2]
+    sp = list(x.shape[2:])
+    D = sp[0] if ndim == 3 else 1
+    nbytes = conv_im2col_bytes(ndim, N, C, D, sp[-2], sp[-1], K, stride, pad)
+    if nbytes == 0:
+        raise ConvError(2, "conv_im2col_bytes")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    shape = _out_shape(x, w, stride, pad, ndim)
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    wsb = ws.numel() * ws.element_size()
+    if ndim == 2:
+        st = conv2d_fwd_bf16_explicit(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(ws), wsb, N, C,
+                                      sp[0], sp[1], w.shape[0], K, stride, pad, _stream())
+    else:
+        st = conv3d_fwd_bf16_explicit(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(ws), wsb, N, C,
+                                      D, sp[1], sp[2], w.shape[0], K, stride, pad, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv%dd_fwd_bf16_explicit" % ndim)
+    return y

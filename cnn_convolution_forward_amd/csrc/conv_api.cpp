@@ -1,0 +1,241 @@
+// conv_api.cpp -- the extern "C" entry points of libconvfwd.so.
+//
+// Every entry point validates its arguments on the host first (no HIP call
+// before validation passes), then picks a kernel route and launches on the
+// caller's stream.  The public contract is in include/conv_fwd.h.
+#include "conv_fwd.h"
+#include "conv_internal.h"
+
+#include <stdint.h>
+#include <string.h>
+
+using convfwd::Shape;
+
+namespace {
+
+constexpr int64_t kMaxElems = INT64_C(2147483647);   // tensors must stay below 2^31 elements
+
+// floor((in + 2p - K)/s) + 1 with an explicit reject of in + 2p < K
+// ("Hand-writing Conv2D", 1.1; "Conv2d from the official docs", 3.2).
+int64_t out_dim(int64_t in, int64_t K, int64_t s, int64_t p) {
+    if (in < 1 || K < 1 || s < 1 || p < 0) return -1;
+    int64_t num = in + 2 * p - K;
+    if (num < 0) return -1;
+    return num / s + 1;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Fill `sh` from the arguments.  Returns CONV_OK or the first violated rule.
+conv_status_t make_shape(int ndim, int N, int C, int D, int H, int W, int Co,
+                         int K, int s, int p, Shape &sh) {
+    if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1 || Co < 1 || K < 1 || s < 1 || p < 0)
+        return CONV_ERR_PARAM;
+    int64_t Ho = out_dim(H, K, s, p), Wo = out_dim(W, K, s, p);
+    int64_t Do = ndim == 3 ? out_dim(D, K, s, p) : 1;
+    if (Ho < 1 || Wo < 1 || Do < 1) return CONV_ERR_SHAPE;
+    sh.ndim = ndim;
+    sh.N = N; sh.C = C; sh.D = D; sh.H = H; sh.W = W; sh.Co = Co;
+    sh.K = K; sh.s = s; sh.p = p;
+    sh.Kd = ndim == 3 ? K : 1;
+    sh.sd = ndim == 3 ? s : 1;
+    sh.pd = ndim == 3 ? p : 0;
+    sh.Do = (int)Do; sh.Ho = (int)Ho; sh.Wo = (int)Wo;
+    // Element counts in int64: each factor is < 2^31, so each pairwise product
+    // fits; stop as soon as a running product passes the limit.
+    int64_t taps = (int64_t)sh.Kd * K;
+    if (taps > kMaxElems / K) return CONV_ERR_OVERFLOW;
+    taps *= K;
+    const int64_t fx[] = {N, C, D, H, W};
+    const int64_t fw[] = {Co, C, taps};
+    const int64_t fy[] = {N, Co, Do, Ho, Wo};
+    int64_t acc = 1;
+    for (int64_t f : fx) { if (acc > kMaxElems / f) return CONV_ERR_OVERFLOW; acc *= f; }
+    acc = 1;
+    for (int64_t f : fw) { if (acc > kMaxElems / f) return CONV_ERR_OVERFLOW; acc *= f; }
+    acc = 1;
+    for (int64_t f : fy) { if (acc > kMaxElems / f) return CONV_ERR_OVERFLOW; acc *= f; }
+    return CONV_OK;
+}
+
+conv_status_t check_alias(const Shape &sh, int esize, const void *x, const void *w,
+                          const void *bias, const void *y, const void *ws, size_t ws_bytes) {
+    int64_t yb = sh.y_elems() * 4;
+    if (overlaps(y, yb, x, sh.x_elems() * esize) || overlaps(y, yb, w, sh.w_elems() * esize) ||
+        overlaps(y, yb, bias, (int64_t)sh.Co * 4) || overlaps(y, yb, ws, (int64_t)ws_bytes))
+        return CONV_ERR_ALIAS;
+    if (ws && (overlaps(ws, (int64_t)ws_bytes, x, sh.x_elems() * esize) ||
+               overlaps(ws, (int64_t)ws_bytes, w, sh.w_elems() * esize)))
+        return CONV_ERR_ALIAS;
+    return CONV_OK;
+}
+
+conv_status_t to_status(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_ERR_HIP; }
+
+// Thin stem layers (C_in*K^dims <= 32) have too little reduction to feed the
+// matrix cores well; they go to the direct VALU kernel.
+constexpr int64_t kValuMaxK = 32;
+
+conv_status_t fwd_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                       int N, int C, int D, int H, int W, int Co, int K, int s, int p,
+                       int algo, void *stream) {
+    if (!x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
+    if (st != CONV_OK) return st;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    if ((st = check_alias(sh, 2, x, w, bias, y, nullptr, 0)) != CONV_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    int route = algo;
+    if (route == CONV_ALGO_AUTO) route = sh.kgemm() <= kValuMaxK ? CONV_ALGO_VALU : CONV_ALGO_MFMA;
+    if (route == CONV_ALGO_VALU) return to_status(convfwd::launch_valu_bf16(sh, x, w, bias, y, hs));
+    return to_status(convfwd::launch_igemm_bf16(sh, x, w, bias, y, hs));
+}
+
+conv_status_t fwd_f32(int ndim, const float *x, const float *w, const float *bias, float *y,
+                      int N, int C, int D, int H, int W, int Co, int K, int s, int p,
+                      int algo, void *stream) {
+    if (!x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
+    if (st != CONV_OK) return st;
+    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    if ((st = check_alias(sh, 4, x, w, bias, y, nullptr, 0)) != CONV_OK) return st;
+    return to_status(convfwd::launch_valu_f32(sh, x, w, bias, y, (hipStream_t)stream));
+}
+
+conv_status_t im2col_bf16(int ndim, const uint16_t *x, uint16_t *xcol, int N, int C, int D, int H,
+                          int W, int K, int s, int p, void *stream) {
+    if (!x || !xcol) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(ndim, N, C, D, H, W, 1, K, s, p, sh);
+    if (st != CONV_OK) return st;
+    if (sh.kgemm() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
+    if (overlaps(xcol, sh.xcol_elems() * 2, x, sh.x_elems() * 2)) return CONV_ERR_ALIAS;
+    return to_status(convfwd::launch_im2col_bf16(sh, x, xcol, (hipStream_t)stream));
+}
+
+conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias,
+                            float *y, void *ws, size_t ws_bytes, int N, int C, int D, int H, int W,
+                            int Co, int K, int s, int p, void *stream) {
+    if (!x || !w || !y || !ws) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
+    if (st != CONV_OK) return st;
+    if (sh.kgemm() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
+    if ((uint64_t)ws_bytes < (uint64_t)sh.xcol_elems() * 2) return CONV_ERR_WORKSPACE;
+    if ((st = check_alias(sh, 2, x, w, bias, y, ws, ws_bytes)) != CONV_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    uint16_t *xcol = (uint16_t *)ws;
+    hipError_t e = convfwd::launch_im2col_bf16(sh, x, xcol, hs);
+    if (e != hipSuccess) return CONV_ERR_HIP;
+    return to_status(convfwd::launch_gemm_xcol_bf16(sh, w, xcol, bias, y, hs));
+}
+
+}  // namespace
+
+namespace convfwd {
+
+// MFMA route: a specialised kernel when the shape matches one, else the
+// general implicit GEMM.
+hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                             const float *bias, float *y, hipStream_t st) {
+    return launch_igemm_generic_bf16(sh, x, w, bias, y, st);
+}
+
+// VALU route for bf16 inputs.
+hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                            const float *bias, float *y, hipStream_t st) {
+    return launch_valu_generic_bf16(sh, x, w, bias, y, st);
+}
+
+}  // namespace convfwd
+
+extern "C" {
+
+int64_t conv_out_dim(int64_t in, int64_t K, int64_t stride, int64_t pad) {
+    return out_dim(in, K, stride, pad);
+}
+
+const char *conv_status_str(int status) {
+    switch (status) {
+        case CONV_OK: return "ok";
+        case CONV_ERR_NULL: return "a required pointer is NULL";
+        case CONV_ERR_PARAM: return "a size, kernel or stride < 1, or pad < 0";
+        case CONV_ERR_SHAPE: return "kernel larger than the padded input (no output position)";
+        case CONV_ERR_OVERFLOW: return "a tensor would hold 2^31 or more elements";
+        case CONV_ERR_ALIAS: return "output overlaps an input or the workspace";
+        case CONV_ERR_WORKSPACE: return "workspace too small for X_col";
+        case CONV_ERR_ALGO: return "algorithm not available for this dtype or shape";
+        case CONV_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int conv_version(void) { return 100; }
+
+conv_status_t conv2d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                              int N, int C_in, int H, int W, int C_out, int K, int stride, int pad,
+                              int algo, void *stream) {
+    return fwd_bf16(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream);
+}
+
+conv_status_t conv2d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
+                             int N, int C_in, int H, int W, int C_out, int K, int stride, int pad,
+                             int algo, void *stream) {
+    return fwd_f32(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream);
+}
+
+conv_status_t conv3d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                              int N, int C_in, int D, int H, int W, int C_out, int K, int stride,
+                              int pad, int algo, void *stream) {
+    return fwd_bf16(3, x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream);
+}
+
+conv_status_t conv3d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
+                             int N, int C_in, int D, int H, int W, int C_out, int K, int stride,
+                             int pad, int algo, void *stream) {
+    return fwd_f32(3, x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream);
+}
+
+size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W, int K, int stride,
+                         int pad) {
+    if (ndim != 2 && ndim != 3) return 0;
+    Shape sh;
+    if (make_shape(ndim, N, C_in, ndim == 3 ? D : 1, H, W, 1, K, stride, pad, sh) != CONV_OK)
+        return 0;
+    if (sh.kgemm() > kMaxElems / sh.pixels()) return 0;
+    return (size_t)sh.xcol_elems() * 2;
+}
+
+conv_status_t conv2d_im2col_bf16(const uint16_t *x, uint16_t *xcol, int N, int C_in, int H, int W,
+                                 int K, int stride, int pad, void *stream) {
+    return im2col_bf16(2, x, xcol, N, C_in, 1, H, W, K, stride, pad, stream);
+}
+
+conv_status_t conv3d_im2col_bf16(const uint16_t *x, uint16_t *xcol, int N, int C_in, int D, int H,
+                                 int W, int K, int stride, int pad, void *stream) {
+    return im2col_bf16(3, x, xcol, N, C_in, D, H, W, K, stride, pad, stream);
+}
+
+conv_status_t conv2d_fwd_bf16_explicit(const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, void *workspace, size_t workspace_bytes,
+                                       int N, int C_in, int H, int W, int C_out, int K,
+                                       int stride, int pad, void *stream) {
+    return explicit_bf16(2, x, w, bias, y, workspace, workspace_bytes, N, C_in, 1, H, W, C_out,
+                         K, stride, pad, stream);
+}
+
+conv_status_t conv3d_fwd_bf16_explicit(const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, void *workspace, size_t workspace_bytes,
+                                       int N, int C_in, int D, int H, int W, int C_out, int K,
+                                       int stride, int pad, void *stream) {
+    return explicit_bf16(3, x, w, bias, y, workspace, workspace_bytes, N, C_in, D, H, W, C_out,
+                         K, stride, pad, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// conv_internal.h -- shapes and kernel launchers shared inside libconvfwd.so.
+// Not part of the public ABI (that is include/conv_fwd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convfwd {
+
+// One convolution problem.  2D problems are carried as 3D with D = Do = 1,
+// Kd = 1, pad_d = 0, stride_d = 1, so every kernel indexes (d, h, w).
+struct Shape {
+    int ndim;               // 2 or 3
+    int N, C, D, H, W;      // input  N x C x D x H x W
+    int Co;                 // output channels
+    int K, s, p;            // square/cubic kernel, one stride, one symmetric pad
+    int Kd, sd, pd;         // depth kernel/stride/pad: (K, s, p) in 3D, (1, 1, 0) in 2D
+    int Do, Ho, Wo;         // output spatial extents (Do = 1 in 2D)
+
+    __host__ __device__ int64_t taps() const { return (int64_t)Kd * K * K; }            // K^ndim
+    __host__ __device__ int64_t kgemm() const { return (int64_t)C * taps(); }          // C_in * K^ndim
+    __host__ __device__ int64_t in_plane() const { return (int64_t)D * H * W; }
+    __host__ __device__ int64_t out_plane() const { return (int64_t)Do * Ho * Wo; }
+    __host__ __device__ int64_t pixels() const { return (int64_t)N * out_plane(); }    // GEMM N dimension
+    __host__ __device__ int64_t x_elems() const { return (int64_t)N * C * in_plane(); }
+    __host__ __device__ int64_t w_elems() const { return (int64_t)Co * kgemm(); }
+    __host__ __device__ int64_t y_elems() const { return (int64_t)Co * pixels(); }
+    __host__ __device__ int64_t xcol_elems() const { return kgemm() * pixels(); }
+};
+
+// Kernel launchers.  Each enqueues on `st` and returns hipGetLastError().
+hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol, hipStream_t st);
+hipError_t launch_gemm_xcol_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol,
+                                 const float *bias, float *y, hipStream_t st);
+hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                             const float *bias, float *y, hipStream_t st);
+hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                            const float *bias, float *y, hipStream_t st);
+// Route-specific launchers behind the two dispatchers above.
+hipError_t launch_igemm_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                                     const float *bias, float *y, hipStream_t st);
+hipError_t launch_valu_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                                    const float *bias, float *y, hipStream_t st);
+hipError_t launch_valu_f32(const Shape &sh, const float *x, const float *w,
+                           const float *bias, float *y, hipStream_t st);
+
+}  // namespace convfwd

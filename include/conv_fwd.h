@@ -1,0 +1,158 @@
+/*
+ * conv_fwd.h -- C ABI of libconvfwd.so, a convolution forward engine for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For a 2D convolution with one square kernel size K, one
+ * stride s and one symmetric zero pad p (page "Hand-writing Conv2D", 1.1-1.2):
+ *
+ *     y[n][oc][oh][ow] = bias[oc] + sum_{ic, kh, kw}
+ *                        x[n][ic][oh*s + kh - p][ow*s + kw - p] * w[oc][ic][kh][kw]
+ *
+ * where a tap whose input coordinate falls outside the input contributes 0
+ * (zero padding by bounds checks, no padded copy).  The output size per
+ * spatial dimension is  out = floor((in + 2p - K)/s) + 1  (same section).
+ * The engine evaluates it as the product  W_row (C_out x C_in*K*K) @ X_col
+ * (C_in*K*K x N*H_out*W_out)  of the page "Why use matrix multiplication for
+ * convolution", 2.2-2.3, either with X_col materialised in device memory
+ * (the *_explicit and *_im2col entry points) or gathered tile by tile inside
+ * the GEMM kernel and never stored (implicit GEMM, same page, 4.3).  The 3D
+ * form adds a depth dimension with the same K, s, p (page "PyTorch tensor
+ * products and conv2d/conv3d dimension semantics", 5.1-5.2).
+ *
+ * Conventions for every entry point below:
+ *   Layout     x is dense NCHW (2D) or NCDHW (3D); w is dense OIHW / OIDHW,
+ *              i.e. (C_out, C_in, K, K[, K]); bias is (C_out); y is dense
+ *              N C_out H_out W_out (or N C_out D_out H_out W_out).  Strided
+ *              views are not accepted: pass contiguous buffers.
+ *   Types      "bf16" pointers hold raw bfloat16 bit patterns (uint16_t).
+ *              The output is always fp32; accumulation is fp32; bias is fp32.
+ *   Memory     every tensor pointer is a DEVICE pointer owned by the caller.
+ *              The library allocates nothing, frees nothing and keeps no
+ *              pointer after the call returns.
+ *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *              enqueued on it and the call returns before the work finishes;
+ *              the caller synchronises.  Calls on one stream run in order.
+ *   Errors     arguments are validated on the host BEFORE any HIP call; on a
+ *              validation error nothing is launched and y is not written.  A
+ *              status other than CONV_OK is returned, never an exit or abort.
+ *              CONV_ERR_HIP reports a failed launch (the HIP error is then
+ *              also left in the runtime's last-error slot).
+ *   Limits     each tensor (x, w, y, X_col) must hold fewer than 2^31
+ *              elements; N, C_in, C_out, spatial sizes and K >= 1; stride >= 1;
+ *              pad >= 0; every padded input extent must be >= K.
+ *   Aliasing   y must not overlap x, w, bias (or the workspace).
+ */
+#ifndef CONV_FWD_H
+#define CONV_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+/* Only the functions below are exported from the shared library. */
+#define CONV_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_NULL = 1,       /* a required pointer (x, w, y, workspace) is NULL            */
+    CONV_ERR_PARAM = 2,      /* a size < 1, K < 1, stride < 1 or pad < 0                    */
+    CONV_ERR_SHAPE = 3,      /* in + 2*pad < K in some spatial dimension (no output)        */
+    CONV_ERR_OVERFLOW = 4,   /* a tensor would hold 2^31 or more elements                   */
+    CONV_ERR_ALIAS = 5,      /* y overlaps x, w, bias or the workspace                      */
+    CONV_ERR_WORKSPACE = 6,  /* workspace smaller than conv*_im2col_bytes() requires        */
+    CONV_ERR_ALGO = 7,       /* the requested algorithm does not exist for this dtype/shape */
+    CONV_ERR_HIP = 8         /* a HIP launch failed                                         */
+} conv_status_t;
+
+/* Kernel route.  AUTO picks by shape: bf16 with C_in*K^dims <= 32 (the thin
+ * stem layer) -> VALU direct kernel; other bf16 -> MFMA implicit GEMM; fp32 ->
+ * VALU.  MFMA is bf16-only (CONV_ERR_ALGO for fp32). */
+typedef enum {
+    CONV_ALGO_AUTO = 0,
+    CONV_ALGO_MFMA = 1,      /* implicit GEMM on bf16 matrix cores, fp32 accumulate */
+    CONV_ALGO_VALU = 2       /* direct convolution, fp32 FMA on the vector ALUs       */
+} conv_algo_t;
+
+/* floor((in + 2*pad - K)/stride) + 1, or -1 if in < 1, K < 1, stride < 1,
+ * pad < 0 or in + 2*pad < K ("Hand-writing Conv2D", 1.1; the explicit reject
+ * of a negative numerator follows "Conv2d from the official docs", 3.2, which
+ * warns that C division truncates rather than floors for negatives). */
+CONV_API int64_t conv_out_dim(int64_t in, int64_t K, int64_t stride, int64_t pad);
+
+/* Static, NUL-terminated text for a status code; never NULL. */
+CONV_API const char *conv_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+CONV_API int conv_version(void);
+
+/* ---- direct entry points: y = conv(x, w) + bias ------------------------- */
+
+/* 2D, bf16 inputs and weights, fp32 bias (NULL = no bias) and output.
+ * Shapes: x (N, C_in, H, W), w (C_out, C_in, K, K), y (N, C_out, H_out, W_out). */
+CONV_API conv_status_t conv2d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                              int N, int C_in, int H, int W, int C_out,
+                              int K, int stride, int pad, int algo, void *stream);
+
+/* 2D, fp32 everywhere (VALU route only).  Same shapes. */
+CONV_API conv_status_t conv2d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
+                             int N, int C_in, int H, int W, int C_out,
+                             int K, int stride, int pad, int algo, void *stream);
+
+/* 3D, bf16 inputs: x (N, C_in, D, H, W), w (C_out, C_in, K, K, K),
+ * y (N, C_out, D_out, H_out, W_out). */
+CONV_API conv_status_t conv3d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                              int N, int C_in, int D, int H, int W, int C_out,
+                              int K, int stride, int pad, int algo, void *stream);
+
+/* 3D, fp32 everywhere (VALU route only). */
+CONV_API conv_status_t conv3d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
+                             int N, int C_in, int D, int H, int W, int C_out,
+                             int K, int stride, int pad, int algo, void *stream);
+
+/* ---- explicit im2col path ("Why use matrix multiplication for convolution",
+ *      2.2 and 3.1): X_col is materialised in caller-owned device memory. ---- */
+
+/* Bytes of the bf16 X_col matrix, (C_in*K*K) x (N*H_out*W_out) elements, for
+ * these arguments; 0 if the arguments are invalid or X_col would hold 2^31 or
+ * more elements.  D = 1 and the 2D formula apply when ndim == 2. */
+CONV_API size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W,
+                         int K, int stride, int pad);
+
+/* X_col[r][j] = x[n][ic][oh*s+kh-p][ow*s+kw-p] (0 outside the input), with
+ * row r = (ic*K + kh)*K + kw and column j = (n*H_out + oh)*W_out + ow, stored
+ * row-major as bf16 into xcol (which must hold conv_im2col_bytes() bytes).
+ * The copy is exact (bit for bit). */
+CONV_API conv_status_t conv2d_im2col_bf16(const uint16_t *x, uint16_t *xcol,
+                                 int N, int C_in, int H, int W,
+                                 int K, int stride, int pad, void *stream);
+
+/* 3D twin: row r = ((ic*K + kd)*K + kh)*K + kw, column
+ * j = ((n*D_out + od)*H_out + oh)*W_out + ow. */
+CONV_API conv_status_t conv3d_im2col_bf16(const uint16_t *x, uint16_t *xcol,
+                                 int N, int C_in, int D, int H, int W,
+                                 int K, int stride, int pad, void *stream);
+
+/* im2col into `workspace`, then one MFMA GEMM  W_row @ X_col  whose epilogue
+ * adds bias and writes y directly in N C_out H_out W_out order (the reshape and
+ * axis swap of "Why use matrix multiplication for convolution", 3.2, fused
+ * into the store).  workspace: device memory of at least
+ * conv_im2col_bytes(2, ...) bytes, owned by the caller, clobbered. */
+CONV_API conv_status_t conv2d_fwd_bf16_explicit(const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, void *workspace, size_t workspace_bytes,
+                                       int N, int C_in, int H, int W, int C_out,
+                                       int K, int stride, int pad, void *stream);
+
+/* 3D twin of conv2d_fwd_bf16_explicit; workspace of conv_im2col_bytes(3, ...). */
+CONV_API conv_status_t conv3d_fwd_bf16_explicit(const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, void *workspace, size_t workspace_bytes,
+                                       int N, int C_in, int D, int H, int W, int C_out,
+                                       int K, int stride, int pad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_FWD_H */

@@ -1,0 +1,118 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, computes output sizes like the pages' formula, and rejects
+every invalid argument before any HIP call (so no kernel is ever launched
+here: all pointers below are fake and never dereferenced)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from cnn_convolution_forward_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv_fwd.h")
+
+# Fake, distinct, non-overlapping "device" addresses for validation-only calls.
+X, Wp, BIAS, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = text.split("#define CONV_API", 1)[1]
+    return sorted(set(re.findall(r"CONV_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_symbols() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = os.popen("nm -D --defined-only %s" % B.LIB_PATH).read()
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(declared_symbols()) == exported
+
+
+def test_version_and_status_strings():
+    assert B.conv_version() >= 100
+    for s in range(9):
+        assert B.status_str(s) and B.status_str(s) != "unknown status"
+    assert B.status_str(99) == "unknown status"
+
+
+def test_out_dim_matches_page_table(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "output_sizes.json")))
+    for c in g["cases"]:
+        assert B.conv_out_dim(c["in"], c["k"], c["s"], c["p"]) == c["out"], c
+    assert B.conv_out_dim(5, 3, 0, 1) == -1
+    assert B.conv_out_dim(5, 3, 1, -1) == -1
+
+
+def _c2(x=X, w=Wp, b=BIAS, y=Y, N=2, C=3, H=9, W=11, Co=4, K=3, s=2, p=1, algo=0):
+    return B.conv2d_fwd_bf16(x, w, b, y, N, C, H, W, Co, K, s, p, algo, None)
+
+
+def test_null_pointers():
+    assert _c2(x=None) == 1
+    assert _c2(w=None) == 1
+    assert _c2(y=None) == 1
+    assert B.conv2d_fwd_f32(X, None, None, Y, 2, 3, 9, 11, 4, 3, 2, 1, 0, None) == 1
+    assert B.conv2d_im2col_bf16(None, Y, 2, 3, 9, 11, 3, 2, 1, None) == 1
+    assert B.conv2d_fwd_bf16_explicit(X, Wp, None, Y, None, 1 << 20, 2, 3, 9, 11, 4, 3, 2, 1, None) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(C=0), dict(H=0), dict(W=-1), dict(Co=0), dict(K=0),
+                                dict(s=0), dict(s=-2), dict(p=-1)])
+def test_bad_params(kw):
+    assert _c2(**kw) == 2
+
+
+def test_kernel_larger_than_padded_input():
+    assert _c2(H=1, W=1, K=3, s=1, p=0) == 3
+    assert _c2(H=5, W=1, K=3, s=1, p=0) == 3
+    assert B.conv3d_fwd_bf16(X, Wp, BIAS, Y, 1, 1, 1, 5, 5, 1, 3, 1, 0, 0, None) == 3
+    # pad >= K is legal (fully padded border windows)
+    assert B.conv_im2col_bytes(2, 1, 1, 1, 1, 1, 1, 1, 2) == 25 * 2
+
+
+def test_overflow_rejected():
+    # x with 2^31 elements
+    assert _c2(N=2, C=1024, H=1024, W=1024, Co=1, K=1, s=1, p=0) == 4
+    # y with >= 2^31 elements while x is small
+    assert _c2(N=1, C=1, H=46341, W=46341, Co=1, K=1, s=1, p=0) == 4
+    assert B.conv_im2col_bytes(2, 64, 128, 1, 256, 256, 3, 1, 1) == 0     # X_col >= 2^31
+
+
+def test_alias_rejected():
+    assert _c2(y=X) == 5
+    assert _c2(y=X + 16) == 5
+    assert _c2(y=BIAS - 8) == 5
+    assert _c2(y=Wp + 2) == 5
+    ws_bytes = B.conv_im2col_bytes(2, 2, 3, 1, 9, 11, 3, 2, 1)
+    assert B.conv2d_fwd_bf16_explicit(X, Wp, None, Y, Y + 4, ws_bytes, 2, 3, 9, 11, 4, 3, 2, 1, None) == 5
+    assert B.conv2d_fwd_bf16_explicit(X, Wp, None, Y, X, ws_bytes, 2, 3, 9, 11, 4, 3, 2, 1, None) == 5
+
+
+def test_bad_algo():
+    assert _c2(algo=3) == 7
+    assert _c2(algo=-1) == 7
+    assert B.conv2d_fwd_f32(X, Wp, BIAS, Y, 2, 3, 9, 11, 4, 3, 2, 1, 1, None) == 7   # MFMA is bf16-only
+
+
+def test_workspace_size():
+    need = B.conv_im2col_bytes(2, 2, 3, 1, 9, 11, 3, 2, 1)
+    assert need == 27 * (2 * 5 * 6) * 2
+    assert B.conv2d_fwd_bf16_explicit(X, Wp, None, Y, WS, need - 1, 2, 3, 9, 11, 4, 3, 2, 1, None) == 6
+    assert B.conv_im2col_bytes(3, 8, 3, 16, 64, 64, 3, 1, 1) == 81 * 8 * 16 * 64 * 64 * 2
+    assert B.conv_im2col_bytes(4, 8, 3, 16, 64, 64, 3, 1, 1) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,210 @@
+"""GPU parity: every route of the HIP library against the oracle.
+
+All calls go through the C ABI (ctypes binding).  Sizes: small shapes that span
+several tiles with ragged tails, the five full-size workloads (full-tensor
+comparison: the oracle finishes them in seconds), integer-valued inputs at the
+full sizes (bit-exact), and the degenerate cases (1x1 inputs, pad >= K,
+stride > K, a single output channel).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cnn_convolution_forward_amd import binding as B
+from cnn_convolution_forward_amd import synth
+from parity import TAU, compare, dev, poisoned, reference, run
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny_f32", "stem_bf16", "conv3x3_bf16", "conv1x1_bf16", "conv3d_bf16"]
+
+
+def _routes(wl):
+    if wl.dtype == "f32":
+        return ["valu"]
+    return ["auto", "mfma", "valu", "explicit"]
+
+
+def _go(wl, t, route):
+    return run(wl, t, algo=route if route != "explicit" else "auto", explicit=route == "explicit")
+
+
+# ---- small shapes: several tiles, ragged edges --------------------------------
+
+SMALL_2D = [
+    # (N, C, H, W, Co, K, s, p)
+    (3, 20, 13, 17, 70, 3, 1, 1),
+    (2, 16, 12, 12, 130, 3, 2, 1),
+    (1, 7, 9, 11, 5, 5, 2, 2),
+    (2, 33, 7, 6, 64, 1, 1, 0),
+    (1, 3, 10, 10, 4, 2, 3, 0),      # stride > K
+    (1, 2, 1, 1, 3, 3, 2, 1),        # single-point receptive field
+    (1, 4, 3, 3, 9, 1, 1, 2),        # pad > K: fully padded border = bias exactly
+    (2, 128, 8, 8, 128, 3, 1, 1),
+    (1, 40, 5, 9, 1, 3, 1, 1),       # one output channel
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_2D, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("route", ["mfma", "valu", "explicit"])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_small_2d_bf16(shape, route, with_bias):
+    N, C, H, W, Co, K, s, p = shape
+    wl = synth.Workload("small", 2, N, C, (H, W), Co, K, s, p, "bf16", "normal", 100)
+    t = synth.make_inputs(wl, seed=sum(shape), with_bias=with_bias)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, route), y_ref, S, TAU["bf16"], label="%s %s" % (shape, route))
+
+
+SMALL_3D = [
+    (2, 3, 5, 6, 7, 10, 3, 1, 1),
+    (1, 5, 4, 9, 8, 70, 3, 2, 1),
+    (1, 16, 3, 4, 5, 33, 1, 1, 0),
+    (1, 2, 2, 3, 3, 4, 2, 1, 2),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_3D, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("route", ["mfma", "valu", "explicit"])
+def test_small_3d_bf16(shape, route):
+    N, C, D, H, W, Co, K, s, p = shape
+    wl = synth.Workload("small3d", 3, N, C, (D, H, W), Co, K, s, p, "bf16", "uniform", 200)
+    t = synth.make_inputs(wl, seed=sum(shape))
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, route), y_ref, S, TAU["bf16"], label="%s %s" % (shape, route))
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 9, 11, 4, 3, 2, 1), (1, 5, 7, 7, 6, 5, 1, 2), (2, 2, 5, 4, 3, 1, 1, 0)])
+def test_small_f32(shape):
+    N, C, H, W, Co, K, s, p = shape
+    wl = synth.Workload("smallf32", 2, N, C, (H, W), Co, K, s, p, "f32", "uniform", 300)
+    t = synth.make_inputs(wl, seed=sum(shape))
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "valu"), y_ref, S, TAU["f32"], label=str(shape))
+    wl3 = synth.Workload("smallf32_3d", 3, N, C, (3, H, W), Co, K, s, p, "f32", "uniform", 301)
+    t3 = synth.make_inputs(wl3, seed=sum(shape) + 1)
+    y_ref, S = reference(wl3, t3)
+    compare(_go(wl3, t3, "valu"), y_ref, S, TAU["f32"], label="3d " + str(shape))
+
+
+# ---- the five workloads at full size ------------------------------------------
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(name):
+    wl = synth.WORKLOADS[name]
+    t = synth.make_inputs(wl)
+    y_ref, S = reference(wl, t)
+    for route in _routes(wl):
+        r = compare(_go(wl, t, route), y_ref, S, TAU[wl.dtype], label="%s %s" % (name, route))
+        print("%s %s max|d|/S = %.3g" % (name, route, r))
+
+
+def test_tiny_without_bias():
+    wl = synth.WORKLOADS["tiny_f32"]
+    t = synth.make_inputs(wl, with_bias=False)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "valu"), y_ref, S, TAU["f32"], label="tiny no bias")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_integer_exact(name):
+    """x, w in {-2..2}, b in {-3..3}: every partial sum is an exact integer, so
+    every route must reproduce the oracle bit for bit (catches any missing or
+    misplaced tap)."""
+    wl = synth.WORKLOADS[name]
+    t = synth.make_inputs(wl, integer=True)
+    y_ref, S = reference(wl, t)
+    for route in _routes(wl):
+        compare(_go(wl, t, route), y_ref, S, 0, exact=True, label="%s %s int" % (name, route))
+
+
+# ---- worked examples from the pages -------------------------------------------
+
+def test_pages_worked_examples_on_gpu():
+    x = synth.f32_to_bf16_bits(np.arange(25, dtype=np.float32).reshape(1, 1, 5, 5))
+    w = synth.f32_to_bf16_bits(np.ones((1, 1, 3, 3), np.float32))
+    expect = np.array([[12, 21, 27, 33, 24], [33, 54, 63, 72, 51], [63, 99, 108, 117, 81],
+                       [93, 144, 153, 162, 111], [72, 111, 117, 123, 84]], np.float32)
+    for algo in ("mfma", "valu"):
+        y = B.conv(dev(x, None), dev(w, None), None, 1, 1, algo=algo)
+        np.testing.assert_array_equal(y.cpu().numpy()[0, 0], expect)
+    x = synth.f32_to_bf16_bits(np.arange(75, dtype=np.float32).reshape(1, 3, 5, 5))
+    w = synth.f32_to_bf16_bits(np.ones((2, 3, 3, 3), np.float32))
+    for algo in ("mfma", "valu"):
+        y = B.conv(dev(x, None), dev(w, None), None, 2, 1, algo=algo).cpu().numpy()
+        assert y.shape == (1, 2, 3, 3)
+        for oc in range(2):
+            np.testing.assert_array_equal(y[0, oc], [[336, 531, 372], [639, 999, 693], [516, 801, 552]])
+
+
+# ---- explicit X_col: bit-exact copy ------------------------------------------
+
+@pytest.mark.parametrize("shape", [(2, 3, 9, 11, 3, 2, 1), (3, 20, 13, 17, 3, 1, 1), (1, 5, 8, 6, 5, 2, 2),
+                                   (2, 7, 5, 5, 1, 1, 0), (1, 2, 4, 4, 2, 3, 3)])
+def test_im2col_bit_exact_2d(shape):
+    N, C, H, W, K, s, p = shape
+    rng = np.random.default_rng(sum(shape))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((N, C, H, W)).astype(np.float32))
+    col = B.im2col(dev(x, None), K, s, p).cpu().numpy().view(np.uint16)
+    ref = oracle.im2col2d(x, K, s, p)
+    np.testing.assert_array_equal(oracle.decode(col), ref)
+
+
+def test_im2col_bit_exact_3d():
+    rng = np.random.default_rng(5)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, 3, 4, 6, 5)).astype(np.float32))
+    col = B.im2col(dev(x, None), 3, 1, 1).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.decode(col), oracle.im2col3d(x, 3, 1, 1))
+
+
+@pytest.mark.parametrize("name", ["stem_bf16", "conv3x3_bf16", "conv1x1_bf16", "conv3d_bf16"])
+def test_im2col_full_size_blocks(name):
+    """Full-size X_col; the column block of image n depends only on x[n], so the
+    oracle checks the first and last image's blocks exactly."""
+    wl = synth.WORKLOADS[name]
+    t = synth.make_inputs(wl)
+    col = B.im2col(dev(t.x, None), wl.K, wl.stride, wl.pad)
+    rows = wl.fan_in
+    per = int(np.prod(wl.out_spatial()))
+    assert tuple(col.shape) == (rows, wl.N * per)
+    f = oracle.im2col2d if wl.ndim == 2 else oracle.im2col3d
+    for n in (0, wl.N - 1):
+        blk = col[:, n * per:(n + 1) * per].cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(oracle.decode(blk), f(t.x[n:n + 1], wl.K, wl.stride, wl.pad))
+    del col
+    torch.cuda.empty_cache()
+
+
+# ---- run-to-run determinism and streams ----------------------------------------
+
+@pytest.mark.parametrize("name", ["conv3x3_bf16", "stem_bf16", "conv3d_bf16", "conv1x1_bf16"])
+def test_deterministic(name):
+    wl = synth.WORKLOADS[name]
+    t = synth.make_inputs(wl)
+    for route in ("auto", "explicit"):
+        a = _go(wl, t, route)
+        b = _go(wl, t, route)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), route
+
+
+def test_runs_on_caller_stream():
+    wl = synth.workload("conv3x3_bf16", N=4)
+    t = synth.make_inputs(wl)
+    y_ref, S = reference(wl, t)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x, w, b = dev(t.x, None), dev(t.w, None), dev(t.b, np.float32)
+        y = B.conv(x, w, b, 1, 1)
+    s.synchronize()
+    compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], label="side stream")
+
+
+def test_validation_error_leaves_output_untouched():
+    x = torch.zeros((1, 3, 5, 5), dtype=torch.int16, device="cuda")
+    w = torch.zeros((2, 3, 3, 3), dtype=torch.int16, device="cuda")
+    y = poisoned((1, 2, 3, 3))
+    st = B.conv2d_fwd_bf16(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), 1, 3, 5, 5, 2, 3, 0, 1, 0, None)
+    assert st == 2
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
