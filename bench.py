@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images in the oracle's timed sample (0 = pick ~10 s of work)")
     ap.add_argument("--report", action="store_true", help="also time every workload/route (stderr)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times): the "
+                         "reference dispatch for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -186,6 +189,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "dispatches": 3}))
+        return
     from cnn_convolution_forward_amd import synth
 
     wl = synth.WORKLOADS[args.workload]

@@ -144,6 +144,7 @@ namespace convfwd {
 // general implicit GEMM.
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                              const float *bias, float *y, hipStream_t st) {
+    if (conv3x3s1_supported(sh, x, w)) return launch_conv3x3s1_bf16(sh, x, w, bias, y, st);
     return launch_igemm_generic_bf16(sh, x, w, bias, y, st);
 }
 

@@ -39,6 +39,9 @@ hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *
 // Route-specific launchers behind the two dispatchers above.
 hipError_t launch_igemm_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                      const float *bias, float *y, hipStream_t st);
+bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);
+hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                                 const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                     const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_f32(const Shape &sh, const float *x, const float *w,

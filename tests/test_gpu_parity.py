@@ -208,3 +208,28 @@ def test_validation_error_leaves_output_untouched():
     assert st == 2
     torch.cuda.synchronize()
     assert torch.isnan(y).all()
+
+
+# ---- the dedicated 3x3 stride-1 kernel across widths, heights and tile plans ----
+
+FAST3x3 = [
+    # (N, C, H, W, Co): K=3, s=1, p=1, C % 16 == 0, Co % 128 == 0, W % 8 == 0, W <= 64
+    (2, 16, 56, 56, 128),
+    (3, 32, 7, 64, 128),
+    (1, 16, 8, 8, 256),
+    (2, 48, 12, 16, 128),
+    (2, 16, 30, 40, 128),
+    (1, 32, 5, 24, 128),
+    (5, 16, 9, 48, 128),
+    (16, 16, 56, 56, 128),     # enough tiles for the chunk-pair plan and the XCD remap
+]
+
+
+@pytest.mark.parametrize("shape", FAST3x3, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("integer", [True, False])
+def test_conv3x3_fast_kernel(shape, integer):
+    N, C, H, W, Co = shape
+    wl = synth.Workload("fast3x3", 2, N, C, (H, W), Co, 3, 1, 1, "bf16", "normal", 400)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "mfma"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
