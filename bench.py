@@ -93,6 +93,11 @@ class Runner:
         self.b = None if t.b is None else torch.from_numpy(t.b).cuda()
         self.y = torch.empty(wl.y_shape, dtype=torch.float32, device="cuda")
         self.ws = None
+        self.work = None
+        if route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16":
+            # device workspace for repacked weights (allocated once; the repack
+            # itself runs inside every step)
+            self.work = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
         if route == "explicit":
             nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
                                          wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
@@ -104,7 +109,8 @@ class Runner:
             self.B.conv_explicit(self.x, self.w, self.b, self.wl.stride, self.wl.pad,
                                  workspace=self.ws, out=self.y)
         else:
-            self.B.conv(self.x, self.w, self.b, self.wl.stride, self.wl.pad, algo=self.route, out=self.y)
+            self.B.conv(self.x, self.w, self.b, self.wl.stride, self.wl.pad, algo=self.route, out=self.y,
+                        workspace=self.work)
 
 
 def time_steps(runner, steps, warmup):

@@ -25,6 +25,7 @@ ALGO = {"auto": 0, "mfma": 1, "valu": 2}
 # Every symbol include/conv_fwd.h declares.
 EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv2d_fwd_bf16", "conv2d_fwd_f32", "conv3d_fwd_bf16", "conv3d_fwd_f32",
+           "conv2d_fwd_workspace_bytes", "conv2d_fwd_bf16_ws",
            "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
            "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit")
 
@@ -59,6 +60,10 @@ def lib():
                            ("conv3d_fwd_bf16", d3), ("conv3d_fwd_f32", d3)):
             getattr(L, name).restype = _i
             getattr(L, name).argtypes = args
+        L.conv2d_fwd_workspace_bytes.restype = _sz
+        L.conv2d_fwd_workspace_bytes.argtypes = [_i] * 9
+        L.conv2d_fwd_bf16_ws.restype = _i
+        L.conv2d_fwd_bf16_ws.argtypes = [_vp] * 5 + [_sz] + [_i] * 9 + [_vp]
         L.conv_im2col_bytes.restype = _sz
         L.conv_im2col_bytes.argtypes = [_i] * 9
         L.conv2d_im2col_bf16.restype = _i
@@ -105,6 +110,16 @@ def conv3d_fwd_bf16(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo
 
 def conv3d_fwd_f32(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo=0, stream=None):
     return lib().conv3d_fwd_f32(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv2d_fwd_workspace_bytes(N, C_in, H, W, C_out, K, stride, pad, algo=0):
+    return int(lib().conv2d_fwd_workspace_bytes(N, C_in, H, W, C_out, K, stride, pad, algo))
+
+
+def conv2d_fwd_bf16_ws(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad, algo=0,
+                       stream=None):
+    return lib().conv2d_fwd_bf16_ws(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad,
+                                    algo, stream)
 
 
 def conv_im2col_bytes(ndim, N, C_in, D, H, W, K, stride, pad):
@@ -177,10 +192,22 @@ def _out_shape(x, w, stride, pad, ndim):
     return (x.shape[0], w.shape[0], *outs)
 
 
-def conv(x, w, bias=None, stride=1, pad=0, algo="auto", out=None):
+def workspace_for(x, w, stride=1, pad=0, algo="auto"):
+    """A device workspace tensor sized for conv(..., workspace=...) (or None)."""
+    torch = _torch()
+    if x.dim() != 4 or x.dtype == torch.float32:
+        return None
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    n = conv2d_fwd_workspace_bytes(x.shape[0], x.shape[1], x.shape[2], x.shape[3], w.shape[0],
+                                   w.shape[2], stride, pad, a)
+    return torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+
+
+def conv(x, w, bias=None, stride=1, pad=0, algo="auto", out=None, workspace=None):
     """y = conv(x, w) + bias on the GPU.  x/w: bf16 (torch.bfloat16 or int16/uint16
     bit patterns) or float32, dense NC(D)HW / OI(D)HW; bias float32 or None.
-    Returns float32 y.  2D or 3D by x.dim()."""
+    Returns float32 y.  2D or 3D by x.dim().  `workspace` (2D bf16 only, see
+    workspace_for) selects conv2d_fwd_bf16_ws."""
     torch = _torch()
     ndim = x.dim() - 2
     if ndim not in (2, 3):
@@ -199,7 +226,10 @@ def conv(x, w, bias=None, stride=1, pad=0, algo="auto", out=None):
     a = ALGO[algo] if isinstance(algo, str) else int(algo)
     args = [_ptr(x), _ptr(w), _ptr(bias), _ptr(y), x.shape[0], x.shape[1], *x.shape[2:],
             w.shape[0], K, stride, pad, a, _stream()]
-    if ndim == 2:
+    if ndim == 2 and workspace is not None and not f32:
+        wsb = workspace.numel() * workspace.element_size()
+        st = conv2d_fwd_bf16_ws(args[0], args[1], args[2], args[3], _ptr(workspace), wsb, *args[4:])
+    elif ndim == 2:
         st = (conv2d_fwd_f32 if f32 else conv2d_fwd_bf16)(*args)
     else:
         st = (conv3d_fwd_f32 if f32 else conv3d_fwd_bf16)(*args)

@@ -80,20 +80,29 @@ conv_status_t to_status(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_
 // matrix cores well; they go to the direct VALU kernel.
 constexpr int64_t kValuMaxK = 32;
 
+int pick_route(const Shape &sh, int algo) {
+    if (algo != CONV_ALGO_AUTO) return algo;
+    return sh.kgemm() <= kValuMaxK ? CONV_ALGO_VALU : CONV_ALGO_MFMA;
+}
+
 conv_status_t fwd_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
                        int N, int C, int D, int H, int W, int Co, int K, int s, int p,
-                       int algo, void *stream) {
+                       int algo, void *stream, bool with_ws, void *ws, size_t ws_bytes) {
     if (!x || !w || !y) return CONV_ERR_NULL;
     Shape sh;
     conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
     if (st != CONV_OK) return st;
     if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
-    if ((st = check_alias(sh, 2, x, w, bias, y, nullptr, 0)) != CONV_OK) return st;
+    const int route = pick_route(sh, algo);
+    if (with_ws) {
+        const size_t need = route == CONV_ALGO_MFMA ? convfwd::igemm_workspace_bytes(sh, x, w) : 0;
+        if (need && (!ws || ws_bytes < need || (uintptr_t)ws % 16)) return CONV_ERR_WORKSPACE;
+        if (!need) ws = nullptr, ws_bytes = 0;
+    }
+    if ((st = check_alias(sh, 2, x, w, bias, y, ws, ws_bytes)) != CONV_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
-    int route = algo;
-    if (route == CONV_ALGO_AUTO) route = sh.kgemm() <= kValuMaxK ? CONV_ALGO_VALU : CONV_ALGO_MFMA;
     if (route == CONV_ALGO_VALU) return to_status(convfwd::launch_valu_bf16(sh, x, w, bias, y, hs));
-    return to_status(convfwd::launch_igemm_bf16(sh, x, w, bias, y, hs));
+    return to_status(convfwd::launch_igemm_bf16(sh, x, w, bias, y, hs, ws, ws_bytes));
 }
 
 conv_status_t fwd_f32(int ndim, const float *x, const float *w, const float *bias, float *y,
@@ -143,9 +152,16 @@ namespace convfwd {
 // MFMA route: a specialised kernel when the shape matches one, else the
 // general implicit GEMM.
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
-                             const float *bias, float *y, hipStream_t st) {
-    if (conv3x3s1_supported(sh, x, w)) return launch_conv3x3s1_bf16(sh, x, w, bias, y, st);
+                             const float *bias, float *y, hipStream_t st, void *ws, size_t ws_bytes) {
+    if (conv3x3s1_supported(sh, x, w)) {
+        uint16_t *wp = (ws && ws_bytes >= conv3x3s1_workspace_bytes(sh)) ? (uint16_t *)ws : nullptr;
+        return launch_conv3x3s1_bf16(sh, x, w, wp, bias, y, st);
+    }
     return launch_igemm_generic_bf16(sh, x, w, bias, y, st);
+}
+
+size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w) {
+    return conv3x3s1_supported(sh, x, w) ? conv3x3s1_workspace_bytes(sh) : 0;
 }
 
 // VALU route for bf16 inputs.
@@ -182,7 +198,8 @@ int conv_version(void) { return 100; }
 conv_status_t conv2d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
                               int N, int C_in, int H, int W, int C_out, int K, int stride, int pad,
                               int algo, void *stream) {
-    return fwd_bf16(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream);
+    return fwd_bf16(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream, false,
+                    nullptr, 0);
 }
 
 conv_status_t conv2d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
@@ -194,13 +211,30 @@ conv_status_t conv2d_fwd_f32(const float *x, const float *w, const float *bias, 
 conv_status_t conv3d_fwd_bf16(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
                               int N, int C_in, int D, int H, int W, int C_out, int K, int stride,
                               int pad, int algo, void *stream) {
-    return fwd_bf16(3, x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream);
+    return fwd_bf16(3, x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream, false,
+                    nullptr, 0);
 }
 
 conv_status_t conv3d_fwd_f32(const float *x, const float *w, const float *bias, float *y,
                              int N, int C_in, int D, int H, int W, int C_out, int K, int stride,
                              int pad, int algo, void *stream) {
     return fwd_f32(3, x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo, stream);
+}
+
+size_t conv2d_fwd_workspace_bytes(int N, int C_in, int H, int W, int C_out, int K, int stride,
+                                  int pad, int algo) {
+    Shape sh;
+    if (make_shape(2, N, C_in, 1, H, W, C_out, K, stride, pad, sh) != CONV_OK) return 0;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU || pick_route(sh, algo) != CONV_ALGO_MFMA) return 0;
+    // pointer alignment is checked at call time; assume aligned tensors here
+    return convfwd::igemm_workspace_bytes(sh, (const void *)256, (const void *)256);
+}
+
+conv_status_t conv2d_fwd_bf16_ws(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                                 void *workspace, size_t workspace_bytes, int N, int C_in, int H,
+                                 int W, int C_out, int K, int stride, int pad, int algo, void *stream) {
+    return fwd_bf16(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream, true,
+                    workspace, workspace_bytes);
 }
 
 size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W, int K, int stride,

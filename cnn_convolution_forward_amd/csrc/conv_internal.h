@@ -33,14 +33,21 @@ hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol
 hipError_t launch_gemm_xcol_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol,
                                  const float *bias, float *y, hipStream_t st);
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
-                             const float *bias, float *y, hipStream_t st);
+                             const float *bias, float *y, hipStream_t st, void *ws = nullptr,
+                             size_t ws_bytes = 0);
+// Workspace bytes the MFMA route can use for this shape (0: none).
+size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w);
 hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                             const float *bias, float *y, hipStream_t st);
 // Route-specific launchers behind the two dispatchers above.
 hipError_t launch_igemm_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                      const float *bias, float *y, hipStream_t st);
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);
-hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+// Workspace for the repacked weights of the 3x3 kernel (bytes).
+size_t conv3x3s1_workspace_bytes(const Shape &sh);
+// wpack: NULL (weights transposed in the kernel) or a 16-byte aligned buffer of
+// conv3x3s1_workspace_bytes() bytes that receives the repacked weights first.
+hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
                                  const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                     const float *bias, float *y, hipStream_t st);

@@ -32,7 +32,7 @@
 // Epilogue: + bias[oc], fp32 stores straight into NCHW (coalesced along ow).
 //
 // Requirements (checked by the launcher): K = 3, stride 1, pad 1, C_in % 16
-// == 0, C_out % 128 == 0, W % 8 == 0, 8 <= W <= 64, 16-byte aligned x and w.
+// == 0, C_in >= 32, C_out % 128 == 0, W % 8 == 0, 8 <= W <= 64, 16-byte aligned x and w.
 // The kernel is instantiated for row pitches ROWPX = 10, 18, 34, 66 pixels.
 #include "conv_internal.h"
 #include "mfma_common.h"
@@ -50,43 +50,41 @@ constexpr int kWBufBytes = 9 * kOcTile * 32; // 36864
 constexpr int kInBufBytes = 40960;
 constexpr int kPixB = 48;                    // LDS bytes per input pixel (16 bf16 + pad)
 
-// Tile plan.  Tiles are whole output rows [r0, r0 + R) of one image.  With
-// Rb == 0 each image is cut into ceil(H/Ra) tiles (the last may be short).
-// With Rb > 0 each image is cut into chunks of Ra + Rb rows; every chunk gives
-// one tile of its first Ra rows (group A) and one of its last Rb rows (group
-// B).  The kernel is persistent: workgroup b runs tiles b, b + G, b + 2G, ...
-// (G = grid size), so with G = number of chunks each workgroup runs one A and
-// one B tile.
+// Tile plan.  Tiles are whole output rows [r0, r0 + R) of one image.  Each
+// image is cut into chunks of `rows` rows; a chunk is split into `nparts` (1 to
+// 3) tiles of part[0] >= part[1] >= part[2] rows.  With nparts == 1 the last
+// chunk of an image may be short (the tile is clipped at H).  All first parts
+// are dispatched, then all second parts, then all third parts; the kernel is
+// persistent (workgroup b runs tiles b, b + G, b + 2G, ... for grid size G),
+// so with G = number of chunks every workgroup runs one tile of each part,
+// big ones first: the outputs of the early tiles stream out while the later
+// ones compute, and only the small last tiles' stores remain at the end.
 struct Plan {
-    int Ra, Rb;
-    int tiles_per_img;   // tiles (Rb == 0) or chunks (Rb > 0) per image
-    int ntiles;          // total tiles
+    int part[3];
+    int nparts;
+    int rows;            // rows per chunk (sum of the parts)
+    int chunks_per_img;
+    int ntiles;          // total tiles = nparts * N * chunks_per_img
     int xcd_remap;       // 1: tiles that run at the same time on one XCD are neighbours
 };
 
 struct Tile { int n, r0, R; };
 
-__device__ __forceinline__ Tile decode_tile(const Plan &pl, int H, int b) {
+__host__ __device__ inline Tile decode_tile(const Plan &pl, int H, int b) {
     int t = b;
-    if (pl.xcd_remap) {
-        const int per = pl.ntiles >> 3;
-        t = (b & 7) * per + (b >> 3);
-    }
+    const int per = pl.xcd_remap ? (pl.ntiles >> 3) : pl.ntiles;
+    if (pl.xcd_remap) t = (b & 7) * per + (b >> 3);
+    // within each range of `per` tiles: its chunks' first parts, then second, ...
+    const int base = (t / per) * per, k = t - base, cpr = per / pl.nparts;
+    const int part = k / cpr;
+    const int chunk = base / pl.nparts + (k - part * cpr);
     Tile tl;
-    if (pl.Rb == 0) {
-        tl.n = t / pl.tiles_per_img;
-        tl.r0 = (t - tl.n * pl.tiles_per_img) * pl.Ra;
-        tl.R = min(pl.Ra, H - tl.r0);
-    } else {
-        // within each XCD's contiguous range: first its A tiles, then its B tiles
-        const int per = pl.xcd_remap ? (pl.ntiles >> 3) : pl.ntiles;
-        const int base = (t / per) * per, k = t - base, half = per >> 1;
-        const int chunk = (base >> 1) + (k < half ? k : k - half);
-        tl.n = chunk / pl.tiles_per_img;
-        const int c = chunk - tl.n * pl.tiles_per_img;
-        tl.r0 = c * (pl.Ra + pl.Rb) + (k < half ? 0 : pl.Ra);
-        tl.R = k < half ? pl.Ra : pl.Rb;
-    }
+    tl.n = chunk / pl.chunks_per_img;
+    const int c = chunk - tl.n * pl.chunks_per_img;
+    int off = 0;
+    for (int q = 0; q < part; ++q) off += pl.part[q];
+    tl.r0 = c * pl.rows + off;
+    tl.R = pl.part[part] < H - tl.r0 ? pl.part[part] : H - tl.r0;
     return tl;
 }
 
@@ -120,9 +118,15 @@ struct LoadCtx {
 };
 
 // Per-thread state shared by every tile of the workgroup.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 struct KCtx {
     uint8_t *wbuf0, *ibuf0;
+    lds_u8 *wlds0;               // wbuf0 as an LDS-space pointer (direct-to-LDS loads)
     __amdgpu_buffer_rsrc_t wr;   // this workgroup's 128 weight rows
+    __amdgpu_buffer_rsrc_t wpr;  // packed weights of this workgroup's channel block
+    uint32_t lane16;             // lane * 16
+    int wave;                    // wave index (uniform)
     uint32_t w_voff;             // byte offset of (oc_l, ic group) at stage 0
     uint32_t w_dst;              // LDS byte offset of (tap 0, oc_l) with swizzle
     uint32_t stage_x_bytes;      // 16 channels of input: 16 * H * W * 2
@@ -150,15 +154,30 @@ __device__ __forceinline__ LoadCtx make_load_ctx(const uint16_t *x, int C, int H
 
 struct Stage { uint4 w[9]; uint4 in[8]; };
 
-// Issue the global (buffer) loads of stage s.
-__device__ __forceinline__ void issue_loads(const KCtx &k, const LoadCtx &l, int s, Stage &st) {
-    const uint32_t ws = (uint32_t)s * (kIcStage * 9 * 2);
+// Packed weights: stage s of this workgroup's weights is stored in global
+// memory as the exact 36 KB LDS image, so it is copied by 9 direct-to-LDS
+// loads per wave (1 KB contiguous each) with no registers or VALU work.
+__device__ __forceinline__ void dma_w_stage(const KCtx &k, int s, int buf) {
 #pragma unroll
-    for (int q = 0; q < 9; ++q) st.w[q] = bload16(k.wr, k.w_voff + q * 16, ws);
-    const uint32_t xs = (uint32_t)s * k.stage_x_bytes;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.in[e] = bload16(l.xr, l.ivoff, xs + e * k.chan_bytes);
+    for (int q = 0; q < 9; ++q) {
+        const int blk = k.wave * 9 + q;
+        // Issued as inline assembly: the instruction has no register result
+        // (it writes LDS), and the compiler's own waits after the builtin form
+        // would also wait for the unrelated input loads in flight.  Completion
+        // is awaited explicitly (vmcnt) before the barrier that publishes the
+        // buffer; nothing reads the target buffer before that barrier.
+        const uint32_t m0v = (uint32_t)(uintptr_t)(k.wlds0 + buf * kWBufBytes + blk * 1024);
+        const int soff = s * kWBufBytes + blk * 1024;
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(m0v)), "v"(k.lane16), "s"(k.wpr),
+                       "s"(__builtin_amdgcn_readfirstlane(soff))
+                     : "m0", "memory");
+    }
 }
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64).
+#define CONV3X3_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Transposed LDS writes of a loaded stage, in four parts so they can be spread
 // between MFMAs: parts 0-1 weights (taps 0-4, 5-8), parts 2-3 input (pixels 0-3, 4-7).
@@ -196,95 +215,175 @@ __device__ __forceinline__ void store_part(const KCtx &k, const LoadCtx &l, int 
     }
 }
 
-// All K stages of one tile for a wave that owns NJ pixel columns (ROWPX: the
-// LDS row pitch of the input tile).  Stage s computes from LDS buffer `buf`
-// while the loads of the next stage -- stage s+1 of this tile, or stage 0 of
-// the next tile -- are in flight and then written, transposed, into buf ^ 1
-// between the MFMAs of taps 4-7.
-template <int NJ, int ROWPX>
-__device__ __forceinline__ void run_tile(const KCtx &k, const LoadCtx &lcur, const LoadCtx &lnext,
-                                         bool has_next, int S, int &buf, const uint32_t (&b_off)[kNJ],
-                                         uint32_t a_off, const float *bias_rows, int lane,
-                                         __amdgpu_buffer_rsrc_t yr, uint32_t ylane, uint32_t half_rows,
-                                         uint32_t row_bytes, int wm, int pbeg, int pend) {
-    constexpr int NB = NJ > 0 ? NJ : 1;
-    // accumulators start from the bias of their output channel
-    f32x16_t acc[2][NB];
+// Split issue: weights and input loads of one stage separately, so each can
+// go out as soon as the registers it overwrites have been consumed.
+__device__ __forceinline__ void issue_w_loads(const KCtx &k, int s, Stage &st) {
+    const uint32_t ws = (uint32_t)s * (kIcStage * 9 * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int q = 0; q < 9; ++q) st.w[q] = bload16(k.wr, k.w_voff + q * 16, ws);
+}
+__device__ __forceinline__ void issue_x_loads(const KCtx &k, const LoadCtx &l, int s, Stage &st) {
+    const uint32_t xs = (uint32_t)s * k.stage_x_bytes;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float bv = bias_rows ? bias_rows[i * 32 + mfma32_row(r, lane)] : 0.f;
+    for (int e = 0; e < 8; ++e) st.in[e] = bload16(l.xr, l.ivoff, xs + e * k.chan_bytes);
+}
+
+// Column count a wave actually runs for nj pixel columns: one of the
+// instantiated 7, 6, 4, 2 (extra columns compute on padding and are not stored).
+__host__ __device__ constexpr int nj_variant(int nj) { return nj >= 7 ? 7 : nj >= 5 ? 6 : nj >= 3 ? 4 : 2; }
+
+// One tile for a wave that runs NJ pixel columns (ROWPX: LDS row pitch of the
+// input tile).  On entry LDS buffer `buf` holds stage 0 of this tile.  While
+// stage s is multiplied out of `buf`, registers `st` hold stage s+1, which is
+// written transposed into buf ^ 1 between the MFMAs of taps 5-8; right after
+// each part is written, the loads of stage s+2 go out into the freed
+// registers, so every load has about eight taps of MFMA work to arrive.
+// Within a tap, the next tap's A fragments are read first; B fragments live in
+// one rotating set (column j's fragment is re-read for the next tap right
+// after its two MFMAs).  After the last stage, the next tile's stage 0 is
+// loaded while this tile's outputs are stored, then written to LDS, so on
+// exit `buf` holds the next tile's stage 0.  Requires S >= 2.
+template <int NJ, int ROWPX, bool PACKED>
+__device__ __forceinline__ void tile_body(const KCtx &k, const LoadCtx &lc, const LoadCtx &lcn,
+                                          bool has_next, int S, int &buf, uint32_t a_off,
+                                          const uint32_t (&b_off)[kNJ], __amdgpu_buffer_rsrc_t br,
+                                          uint32_t bvoff, int lane,
+                                          int wm, int pbeg, int pend, __amdgpu_buffer_rsrc_t yr,
+                                          uint32_t half_rows, uint32_t row_bytes) {
+    // Accumulator tile (i, j) is D = X_tile (32 pixels x 16 k) * W_tile (16 k x
+    // 32 channels): lane l holds channel l%32 and pixels 8*(r/4) + 4*(l/32) +
+    // r%4 in slot r, so slots 4k..4k+3 are four consecutive output pixels of
+    // one channel.  Accumulators start from that channel's bias (a buffer
+    // with no records when there is no bias: the loads return 0).
+    f32x16_t acc[2][NJ];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j][r] = bv;
-        }
+    for (int i = 0; i < 2; ++i) {
+        const float bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, (int)(bvoff + i * 32 * 4), 0, 0));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = bv;
+    }
+    Stage st;
+    if (!PACKED) issue_w_loads(k, 1, st);
+    issue_x_loads(k, lc, 1, st);
     for (int s = 0; s < S; ++s) {
-        const bool pf = (s + 1 < S) || has_next;
-        const LoadCtx &lp = (s + 1 < S) ? lcur : lnext;
-        const int ps = (s + 1 < S) ? s + 1 : 0;
-        Stage st;
-        if (pf) issue_loads(k, lp, ps, st);
+        const bool st_ok = s + 1 < S;          // registers hold stage s+1
+        const bool ld_ok = s + 2 < S;          // stage s+2 to load
+        // packed weights of stage s+1 go straight to buf ^ 1 (free since the
+        // barrier that ended stage s-1) and must land before this stage's barrier
+        if (PACKED && st_ok) dma_w_stage(k, s + 1, buf ^ 1);
         const uint8_t *wb = k.wbuf0 + buf * kWBufBytes + a_off;
-        const uint8_t *ib[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) ib[j] = k.ibuf0 + buf * kInBufBytes + b_off[j];
-        uint4 a[2][2], b[2][NB];
-        auto fetch = [&](int t, int set) {
-            const int toff = ((t / 3) * ROWPX + (t % 3)) * kPixB;     // compile-time per tap
+        const uint8_t *ib = k.ibuf0 + buf * kInBufBytes;
+        uint4 a[2][2], b[NJ];
+        auto fetch_a = [&](int t, int set) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 a[set][i] = *reinterpret_cast<const uint4 *>(wb + t * (kOcTile * 32) + i * 32 * 32);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) b[set][j] = *reinterpret_cast<const uint4 *>(ib[j] + toff);
         };
-        fetch(0, 0);
+        auto fetch_b = [&](int t, int j) {
+            const int toff = ((t / 3) * ROWPX + (t % 3)) * kPixB;     // compile-time per tap
+            b[j] = *reinterpret_cast<const uint4 *>(ib + b_off[j] + toff);
+        };
+        fetch_a(0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fetch_b(0, j);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 9; ++t) {
-            if (t + 1 < 9) fetch(t + 1, (t + 1) & 1);
+            if (t + 1 < 9) fetch_a(t + 1, (t + 1) & 1);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i][j] = mfma32x32x16(a[t & 1][i], b[t & 1][j], acc[i][j]);
-            if (pf) {
-                if (t == 4) store_part<0>(k, lp, buf ^ 1, st);
-                if (t == 5) store_part<1>(k, lp, buf ^ 1, st);
-                if (t == 6) store_part<2>(k, lp, buf ^ 1, st);
-                if (t == 7) store_part<3>(k, lp, buf ^ 1, st);
+                for (int i = 0; i < 2; ++i) acc[i][j] = mfma32x32x16(b[j], a[t & 1][i], acc[i][j]);
+                if (t + 1 < 9) fetch_b(t + 1, j);
             }
-            // Within a tap: the next tap's operand reads first, then this tap's
-            // MFMAs (whose operands arrived during the previous tap).  Nothing
-            // moves across the tap boundary.
-            if (t + 1 < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2 + NJ, 0);   // DS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ, 0);                  // MFMAs
+            if (st_ok) {
+                if (!PACKED && t == 5) store_part<0>(k, lc, buf ^ 1, st);
+                if (!PACKED && t == 6) {
+                    store_part<1>(k, lc, buf ^ 1, st);
+                    if (ld_ok) issue_w_loads(k, s + 2, st);
+                }
+                if (t == 7) store_part<2>(k, lc, buf ^ 1, st);
+                if (t == 8) {
+                    store_part<3>(k, lc, buf ^ 1, st);
+                    if (ld_ok) issue_x_loads(k, lc, s + 2, st);
+                }
+            }
+            // Pin the order within a tap: the two A reads for tap t+1, then for
+            // each column its two MFMAs followed by its B read for tap t+1.
+            // Nothing moves across the tap boundary.
+            if (t + 1 < 9) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        if (PACKED) {
+            // the weight copy into buf ^ 1 was issued before the 8 input loads
+            // of stage s+2 (vector-memory counters complete in order)
+            if (ld_ok) CONV3X3_WAIT_VMCNT(8);
+            else CONV3X3_WAIT_VMCNT(0);
         }
         __syncthreads();
         buf ^= 1;
     }
-    // ---- epilogue: y[n][oc][r0 + p/W][p%W] = acc.  Buffer stores with the
-    // row offset in soffset and the column in the immediate; lanes past the
-    // tile get an out-of-range offset and their stores are dropped.
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const bool ok = pbeg + j * 32 + (lane & 31) < pend;
-        const uint32_t vo = ok ? ylane + j * 128 + half_rows : kOob;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t row = (uint32_t)(wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3));   // + 4*half via voffset
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), yr, (int)vo,
-                                                      (int)(row * row_bytes), 0);
-            }
+
+    // ---- next tile's stage 0 in flight while this tile's outputs are stored
+    if (has_next) {
+        if (PACKED) dma_w_stage(k, 0, buf);
+        else issue_w_loads(k, 0, st);
+        issue_x_loads(k, lcn, 0, st);
     }
+    // y[n][oc][r0 + p/W][p%W] = acc: one 16-byte store per 4 consecutive
+    // pixels (56 stores per wave for 7 columns, few enough to stay in flight
+    // while the next tile computes).  Channel row offset in soffset, pixel
+    // offset in the immediate; groups past the tile (always whole, since the
+    // tile's pixel count is a multiple of 8) get an out-of-range offset and
+    // their stores are dropped.
+    const int half = (lane >> 5) & 1;
+    const uint32_t ylane = (uint32_t)(lane & 31) * row_bytes + (uint32_t)(pbeg + 4 * half) * 4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = pbeg + j * 32 + q * 8 + 4 * half < pend;
+            const uint32_t vo = ok ? ylane : kOob;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const u32x4_t v = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                                   __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)(vo + (uint32_t)(j * 32 + q * 8) * 4),
+                                                       (int)((uint32_t)(wm * 64 + i * 32) * row_bytes), 0);
+            }
+        }
+    if (has_next) {
+        if (!PACKED) {
+            store_part<0>(k, lcn, buf, st);
+            store_part<1>(k, lcn, buf, st);
+        }
+        store_part<2>(k, lcn, buf, st);
+        store_part<3>(k, lcn, buf, st);
+    }
+    if (PACKED) CONV3X3_WAIT_VMCNT(0);
+    __syncthreads();
 }
 
-template <int ROWPX>
+// The kernel: a persistent loop over this workgroup's tiles.  PACKED: `wp`
+// holds the weights repacked by pack_w3x3_kernel (per channel block and
+// stage, the LDS image), loaded without transposes; otherwise `w` (OIHW) is
+// transposed on the way into LDS.
+template <int ROWPX, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1)
 void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                      const float *__restrict__ bias, float *__restrict__ y,
-                      int C, int H, int W, int Co, Plan plan) {
+                      const uint16_t *__restrict__ wp, const float *__restrict__ bias,
+                      float *__restrict__ y, int C, int H, int W, int Co, Plan plan) {
     __shared__ __align__(16) uint8_t smem[2 * kWBufBytes + 2 * kInBufBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -297,6 +396,12 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     KCtx k;
     k.wbuf0 = smem;
     k.ibuf0 = smem + 2 * kWBufBytes;
+    k.wlds0 = (lds_u8 *)smem;
+    k.wave = wave;
+    k.lane16 = (uint32_t)lane * 16;
+    if (PACKED)
+        k.wpr = __builtin_amdgcn_make_buffer_rsrc((void *)(wp + (int64_t)ocb * C * 9), (short)0,
+                                                  kOcTile * C * 9 * 2, 0x00020000);
     k.wr = __builtin_amdgcn_make_buffer_rsrc((void *)(w + (int64_t)ocb * C * 9), (short)0,
                                              kOcTile * C * 9 * 2, 0x00020000);
     const int w_ocl = tid & (kOcTile - 1), w_g = tid >> 7;
@@ -305,8 +410,12 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     k.chan_bytes = (uint32_t)(HW * 2);
     k.stage_x_bytes = (uint32_t)(HW * 2 * kIcStage);
     const uint32_t a_off = (uint32_t)((wm * 64 + l32) * 32 + ((half ^ wswz(l32)) * 16));
-
-    const float *bias_rows = bias ? bias + ocb + wm * 64 : nullptr;
+    // bias rows of this wave: 64 channels from ocb + wm*64; lane half adds 4 rows
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(bias ? bias + ocb + wm * 64 : y), (short)0, bias ? 64 * 4 : 0, 0x00020000);
+    const uint32_t bvoff = (uint32_t)l32 * 4;
+    const uint32_t row_bytes = (uint32_t)(HW * 4);
+    const uint32_t half_rows = (uint32_t)half * 4 * row_bytes;
 
     // Zero both input buffers once: the edge columns (0 and W+1) are never
     // written again and stay zero for every stage (left/right padding).
@@ -319,13 +428,18 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     int f = blockIdx.x;
     Tile cur = decode_tile(plan, H, f);
     LoadCtx lc = make_load_ctx(x, C, H, W, cur, ROWPX);
-    {   // prologue: stage 0 of the first tile
+    {   // prologue: stage 0 of the first tile into LDS buffer 0
         Stage st;
-        issue_loads(k, lc, 0, st);
-        store_part<0>(k, lc, 0, st);
-        store_part<1>(k, lc, 0, st);
+        if (PACKED) dma_w_stage(k, 0, 0);
+        else issue_w_loads(k, 0, st);
+        issue_x_loads(k, lc, 0, st);
+        if (!PACKED) {
+            store_part<0>(k, lc, 0, st);
+            store_part<1>(k, lc, 0, st);
+        }
         store_part<2>(k, lc, 0, st);
         store_part<3>(k, lc, 0, st);
+        if (PACKED) CONV3X3_WAIT_VMCNT(0);
         __syncthreads();
     }
     int buf = 0;
@@ -350,28 +464,20 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
             const int pr = p / W;
             b_off[j] = (uint32_t)((pr * ROWPX + (p - pr * W)) * kPixB + half * 16);
         }
-
         const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(y + ((int64_t)cur.n * Co + ocb) * HW + (int64_t)cur.r0 * W), (short)0,
             (int)((int64_t)kOcTile * HW * 4 - (int64_t)cur.r0 * W * 4), 0x00020000);
-        const uint32_t ylane = (uint32_t)((pbeg + l32) * 4);
-        const uint32_t row_bytes = (uint32_t)(HW * 4);
-        const uint32_t half_rows = (uint32_t)half * 4 * row_bytes;
 
-#define CONV3X3_RUN(NJV)                                                                        \
-    run_tile<NJV, ROWPX>(k, lc, lcn, has_next, S, buf, b_off, a_off, bias_rows, lane, yr, ylane, \
-                         half_rows, row_bytes, wm, pbeg, pend)
-        switch (nj) {
-            case 7: CONV3X3_RUN(7); break;
-            case 6: CONV3X3_RUN(6); break;
-            case 5: CONV3X3_RUN(5); break;
-            case 4: CONV3X3_RUN(4); break;
-            case 3: CONV3X3_RUN(3); break;
-            case 2: CONV3X3_RUN(2); break;
-            case 1: CONV3X3_RUN(1); break;
-            default: CONV3X3_RUN(0); break;
+#define CONV3X3_TILE(NJV)                                                                       \
+    tile_body<NJV, ROWPX, PACKED>(k, lc, lcn, has_next, S, buf, a_off, b_off, br, bvoff, lane, wm, pbeg, \
+                          pend, yr, half_rows, row_bytes)
+        switch (nj_variant(nj)) {
+            case 7: CONV3X3_TILE(7); break;
+            case 6: CONV3X3_TILE(6); break;
+            case 4: CONV3X3_TILE(4); break;
+            default: CONV3X3_TILE(2); break;
         }
-#undef CONV3X3_RUN
+#undef CONV3X3_TILE
         if (!has_next) break;
         f = fn;
         cur = nxt;
@@ -379,8 +485,37 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     }
 }
 
-// MFMA column steps (32 pixels each) of a tile's busier pixel-wave.
-int tile_steps(int npx) { return (npx + 63) / 64; }
+// Repack OIHW 3x3 weights for the PACKED kernel: for every 128-channel block
+// and 16-channel stage, the 36 KB image that stage occupies in LDS
+// ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  One thread
+// writes one 16-byte unit.
+__global__ __launch_bounds__(256)
+void pack_w3x3_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wp, int C, int Co) {
+    const int S = C / kIcStage;
+    const int64_t units = (int64_t)Co * C * 9 / 8;
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const int64_t chunk = u / (9 * kOcTile * 2);
+    const int rem = (int)(u - chunk * (9 * kOcTile * 2));
+    const int t = rem / (kOcTile * 2), r2 = rem - t * (kOcTile * 2);
+    const int ocl = r2 >> 1, slot = r2 & 1;
+    const int h = slot ^ wswz(ocl);
+    const int ocb = (int)(chunk / S), st = (int)(chunk - (int64_t)ocb * S);
+    const int64_t oc = (int64_t)ocb * kOcTile + ocl;
+    const int ic0 = st * kIcStage + h * 8;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = w[(oc * C + ic0 + e) * 9 + t];
+    *reinterpret_cast<uint4 *>(wp + u * 8) = pack8(v);
+}
+
+// MFMA column steps (32 pixels each) that the busier pixel-wave of a tile runs.
+int tile_steps(int npx) {
+    const int wsplit = ((npx + 63) / 64) * 32;
+    const int nj0 = (wsplit < npx ? wsplit : npx + 31) / 32, nj1 = (npx - wsplit + 31) / 32;
+    const int v0 = nj_variant(nj0 > 0 ? nj0 : 0), v1 = nj_variant(nj1 > 0 ? nj1 : 0);
+    return v0 > v1 ? v0 : v1;
+}
 
 // LDS row pitch (pixels) of the input tile for a width W: the smallest
 // instantiated pitch that holds W + 2 columns.
@@ -392,76 +527,95 @@ int row_px_for(int W) { return W <= 8 ? 10 : W <= 16 ? 18 : W <= 32 ? 34 : 66; }
 int tile_lds_bytes(int R, int W) {
     const int rowpx = row_px_for(W);
     const int npx = R * W, wsplit = ((npx + 63) / 64) * 32;
-    const int pmax = wsplit + ((npx - wsplit + 31) / 32) * 32 - 1;
+    const int nj1 = (npx - wsplit + 31) / 32;
+    const int nj0 = (npx < wsplit ? npx : wsplit) / 32 + ((npx < wsplit && npx % 32) ? 1 : 0);
+    const int pmax0 = nj_variant(nj0) * 32 - 1;
+    const int pmax1 = wsplit + nj_variant(nj1 > 0 ? nj1 : 0) * 32 - 1;
+    const int pmax = pmax0 > pmax1 ? pmax0 : pmax1;
     const int q = (pmax / W + 2) * rowpx + (W - 1) + 2;
     const int q_store = (R + 1) * rowpx + W;
     return (q > q_store ? q : q_store) * kPixB + 32;
 }
 
-// Makespan of a plan on the persistent grid: workgroup b runs tiles b, b + G,
-// ... (G = grid size, one workgroup per CU, all resident at once); a tile
-// costs its MFMA column steps plus a fixed overhead for the pipeline fill and
-// the output stores.
+// Estimated time of a plan on the persistent grid (workgroup b runs tiles b,
+// b + G, ...; one workgroup per CU, all resident).  Unit: one MFMA column step
+// over all K stages as the kernel runs it (about twice the bare MFMA time).
+//  - a tile costs its busier pixel-wave's column steps, but no less than a
+//    floor: every stage also moves a whole 36 KB weight image into LDS and
+//    passes two barriers, whatever the tile's width;
+//  - a tile that is not its workgroup's last ends with a stall: the vector
+//    memory counter retires in order, so the first wait on a load issued
+//    after the tile's output stores also waits for those stores, and all
+//    workgroups reach that point together (chip-wide burst at ~6 TB/s);
+//  - the outputs of the last tiles drain after compute ends.
 int grid_size(const Plan &pl, int slots) { return pl.ntiles < slots ? pl.ntiles : slots; }
 
-double makespan(const Shape &sh, const Plan &pl, int slots) {
+double plan_cost(const Shape &sh, const Plan &pl, int slots) {
+    constexpr double kMinTileSteps = 4.0, kTileOverhead = 0.3, kDrainBps = 6.0e12;
     const int G = grid_size(pl, slots);
-    double worst = 0;
+    const int ncb = sh.Co / kOcTile;
+    const double unit_s = 2.0 * 18.0 * (sh.C / kIcStage) * 32.0 / 2.0e9;   // 18*S MFMAs, 32 clk at ~2 GHz, x2
+    const double burst = (double)kOcTile * 4.0 * G * ncb / kDrainBps / unit_s;  // per output pixel of a tile
+    double worst = 0, last_px = 0;
     for (int b = 0; b < G; ++b) {
         double load = 0;
+        int lastR = 0;
         for (int f = b; f < pl.ntiles; f += G) {
-            int t = f;
-            if (pl.xcd_remap) t = (f & 7) * (pl.ntiles >> 3) + (f >> 3);
-            int R;
-            if (pl.Rb == 0) {
-                const int r0 = (t % pl.tiles_per_img) * pl.Ra;
-                R = pl.Ra < sh.H - r0 ? pl.Ra : sh.H - r0;
-            } else {
-                const int per = pl.xcd_remap ? (pl.ntiles >> 3) : pl.ntiles;
-                R = (t % per) < (per >> 1) ? pl.Ra : pl.Rb;
-            }
-            load += tile_steps(R * sh.W) + 0.3;
+            const Tile tl = decode_tile(pl, sh.H, f);
+            const double st = tile_steps(tl.R * sh.W);
+            load += (st > kMinTileSteps ? st : kMinTileSteps) + kTileOverhead;
+            if (f + G < pl.ntiles) load += burst * tl.R * sh.W;
+            lastR = tl.R;
         }
         if (load > worst) worst = load;
+        last_px += (double)lastR * sh.W;
     }
-    return worst;
+    return worst + last_px * kOcTile * 4.0 * ncb / kDrainBps / unit_s;
 }
 
 void set_remap(Plan &p) {
-    p.xcd_remap = (p.ntiles % 8 == 0 && (p.Rb == 0 || (p.ntiles / 8) % 2 == 0)) ? 1 : 0;
+    p.xcd_remap = (p.ntiles % 8 == 0 && (p.ntiles / 8) % p.nparts == 0) ? 1 : 0;
 }
 
-// Choose the row tiling among uniform tiles of R rows and (Ra, Rb) chunk pairs
-// that divide each image's rows, by the smallest simulated makespan.
 // Resident workgroups per output-channel block: one per CU in total.
 int slots_for(const Shape &sh, int num_cu) {
     const int ncb = sh.Co / kOcTile;
     return num_cu / ncb > 0 ? num_cu / ncb : 1;
 }
 
-Plan make_plan(const Shape &sh, int num_cu) {
+// Choose the row tiling among uniform tiles of R rows and chunks of two or
+// three decreasing parts that divide each image's rows, by the smallest
+// estimated time.
+Plan make_plan(const Shape &sh, int slots) {
     const int W = sh.W, H = sh.H, N = sh.N;
     int rmax = kTilePx / W;
     while (rmax > 1 && tile_lds_bytes(rmax, W) > kInBufBytes) --rmax;
     Plan best{};
     double best_cost = 1e300;
-    for (int R = 1; R <= rmax && R <= H; ++R) {
-        if (tile_lds_bytes(R, W) > kInBufBytes) continue;
-        Plan p{R, 0, (H + R - 1) / R, 0, 0};
-        p.ntiles = N * p.tiles_per_img;
-        set_remap(p);
-        const double c = makespan(sh, p, num_cu);
-        if (c < best_cost * 0.999) { best_cost = c; best = p; }
-    }
-    for (int Ra = 1; Ra <= rmax; ++Ra)
-        for (int Rb = 1; Rb < Ra; ++Rb) {
-            if (H % (Ra + Rb) || tile_lds_bytes(Ra, W) > kInBufBytes) continue;
-            Plan p{Ra, Rb, H / (Ra + Rb), 0, 0};
-            p.ntiles = 2 * N * p.tiles_per_img;
-            set_remap(p);
-            const double c = makespan(sh, p, num_cu);
-            if (c < best_cost * 0.999) { best_cost = c; best = p; }
+    auto consider = [&](int r0, int r1, int r2) {
+        Plan p{};
+        p.part[0] = r0; p.part[1] = r1; p.part[2] = r2;
+        p.nparts = 1 + (r1 > 0) + (r2 > 0);
+        p.rows = r0 + r1 + r2;
+        if (p.nparts == 1) {
+            p.chunks_per_img = (H + r0 - 1) / r0;
+        } else {
+            if (H % p.rows) return;
+            p.chunks_per_img = H / p.rows;
         }
+        p.ntiles = p.nparts * N * p.chunks_per_img;
+        set_remap(p);
+        const double c = plan_cost(sh, p, slots);
+        if (c < best_cost * 0.999) { best_cost = c; best = p; }
+    };
+    for (int a = 1; a <= rmax && a <= H; ++a) {
+        if (tile_lds_bytes(a, W) > kInBufBytes) continue;
+        consider(a, 0, 0);
+        for (int b = 1; b <= a; ++b) {
+            consider(a, b, 0);
+            for (int c = 1; c <= b; ++c) consider(a, b, c);
+        }
+    }
     return best;
 }
 
@@ -470,6 +624,7 @@ Plan make_plan(const Shape &sh, int num_cu) {
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t HW = (int64_t)sh.H * sh.W;
     return sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIcStage == 0 &&
+           sh.C >= 2 * kIcStage &&
            sh.Co % kOcTile == 0 && sh.W % 8 == 0 && sh.W >= 8 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&            // one image within a buffer range
            (int64_t)kOcTile * HW * 4 < (INT64_C(1) << 31) &&         // one output block within a buffer range
@@ -477,7 +632,11 @@ bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
            ((uintptr_t)x % 16) == 0 && ((uintptr_t)w % 16) == 0 && tile_lds_bytes(1, sh.W) <= kInBufBytes;
 }
 
-hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+size_t conv3x3s1_workspace_bytes(const Shape &sh) {
+    return (size_t)sh.Co * sh.C * 9 * 2;
+}
+
+hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
                                  const float *bias, float *y, hipStream_t st) {
     static int num_cu = 0;
     if (num_cu == 0) {
@@ -495,25 +654,28 @@ hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint1
         last_n = sh.N; last_h = sh.H; last_w = sh.W;
     }
     const Plan pl = last;
-    dim3 grid((unsigned)grid_size(pl, slots_for(sh, num_cu)), (unsigned)(sh.Co / kOcTile));
-    switch (row_px_for(sh.W)) {
-        case 10:
-            hipLaunchKernelGGL(conv3x3s1_kernel<10>, grid, dim3(kThreads), 0, st, x, w, bias, y, sh.C,
-                               sh.H, sh.W, sh.Co, pl);
-            break;
-        case 18:
-            hipLaunchKernelGGL(conv3x3s1_kernel<18>, grid, dim3(kThreads), 0, st, x, w, bias, y, sh.C,
-                               sh.H, sh.W, sh.Co, pl);
-            break;
-        case 34:
-            hipLaunchKernelGGL(conv3x3s1_kernel<34>, grid, dim3(kThreads), 0, st, x, w, bias, y, sh.C,
-                               sh.H, sh.W, sh.Co, pl);
-            break;
-        default:
-            hipLaunchKernelGGL(conv3x3s1_kernel<66>, grid, dim3(kThreads), 0, st, x, w, bias, y, sh.C,
-                               sh.H, sh.W, sh.Co, pl);
-            break;
+    if (wpack) {
+        const int64_t units = (int64_t)sh.Co * sh.C * 9 / 8;
+        hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, wpack,
+                           sh.C, sh.Co);
     }
+    dim3 grid((unsigned)grid_size(pl, slots_for(sh, num_cu)), (unsigned)(sh.Co / kOcTile));
+#define CONV3X3_LAUNCH(RP)                                                                          \
+    do {                                                                                            \
+        if (wpack)                                                                                  \
+            hipLaunchKernelGGL((conv3x3s1_kernel<RP, true>), grid, dim3(kThreads), 0, st, x, w, wpack, \
+                               bias, y, sh.C, sh.H, sh.W, sh.Co, pl);                               \
+        else                                                                                        \
+            hipLaunchKernelGGL((conv3x3s1_kernel<RP, false>), grid, dim3(kThreads), 0, st, x, w, w,   \
+                               bias, y, sh.C, sh.H, sh.W, sh.Co, pl);                               \
+    } while (0)
+    switch (row_px_for(sh.W)) {
+        case 10: CONV3X3_LAUNCH(10); break;
+        case 18: CONV3X3_LAUNCH(18); break;
+        case 34: CONV3X3_LAUNCH(34); break;
+        default: CONV3X3_LAUNCH(66); break;
+    }
+#undef CONV3X3_LAUNCH
     return hipGetLastError();
 }
 

@@ -112,6 +112,28 @@ CONV_API conv_status_t conv3d_fwd_f32(const float *x, const float *w, const floa
                              int N, int C_in, int D, int H, int W, int C_out,
                              int K, int stride, int pad, int algo, void *stream);
 
+/* ---- with a workspace --------------------------------------------------- */
+
+/* Bytes of device workspace conv2d_fwd_bf16_ws can use for these arguments:
+ * the 3x3 stride-1 pad-1 MFMA kernel (C_in % 16 == 0, C_in >= 32,
+ * C_out % 128 == 0, W % 8 == 0, 8 <= W <= 64) repacks the weights once per
+ * call into C_out*C_in*9*2 bytes laid out as the per-stage LDS images, so
+ * that it streams them with coalesced direct-to-LDS loads instead of
+ * transposing OIHW in every workgroup.  0 when no route uses a workspace. */
+CONV_API size_t conv2d_fwd_workspace_bytes(int N, int C_in, int H, int W, int C_out,
+                                           int K, int stride, int pad, int algo);
+
+/* conv2d_fwd_bf16 plus a caller-owned device workspace (16-byte aligned, at
+ * least conv2d_fwd_workspace_bytes() bytes; may be NULL when that is 0).  The
+ * workspace is overwritten; the result equals conv2d_fwd_bf16's.  Returns
+ * CONV_ERR_WORKSPACE if it is needed and missing, too small or misaligned,
+ * CONV_ERR_ALIAS if it overlaps x, w or y.  Two calls in flight at once must
+ * not share a workspace. */
+CONV_API conv_status_t conv2d_fwd_bf16_ws(const uint16_t *x, const uint16_t *w, const float *bias,
+                                          float *y, void *workspace, size_t workspace_bytes,
+                                          int N, int C_in, int H, int W, int C_out,
+                                          int K, int stride, int pad, int algo, void *stream);
+
 /* ---- explicit im2col path ("Why use matrix multiplication for convolution",
  *      2.2 and 3.1): X_col is materialised in caller-owned device memory. ---- */
 

@@ -116,3 +116,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_workspace_entry_point_validation():
+    need = B.conv2d_fwd_workspace_bytes(64, 128, 56, 56, 128, 3, 1, 1, 0)
+    assert need == 128 * 128 * 9 * 2
+    assert B.conv2d_fwd_workspace_bytes(64, 128, 56, 56, 128, 3, 1, 1, 2) == 0     # VALU route
+    assert B.conv2d_fwd_workspace_bytes(2, 3, 9, 11, 4, 3, 2, 1, 0) == 0          # no route needs one
+    assert B.conv2d_fwd_workspace_bytes(2, 16, 56, 56, 128, 3, 1, 1, 0) == 0      # one stage: general kernel
+    args = (64, 128, 56, 56, 128, 3, 1, 1, 0, None)
+    assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, None, 0, *args) == 6
+    assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS, need - 2, *args) == 6
+    assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS + 8, need, *args) == 6          # misaligned
+    assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, Y + 64, need, *args) == 5          # overlaps y
+    assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS, need, 64, 128, 56, 56, 128, 3, 1, 1, 5, None) == 7

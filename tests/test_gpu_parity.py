@@ -213,23 +213,49 @@ def test_validation_error_leaves_output_untouched():
 # ---- the dedicated 3x3 stride-1 kernel across widths, heights and tile plans ----
 
 FAST3x3 = [
-    # (N, C, H, W, Co): K=3, s=1, p=1, C % 16 == 0, Co % 128 == 0, W % 8 == 0, W <= 64
-    (2, 16, 56, 56, 128),
+    # (N, C, H, W, Co): K=3, s=1, p=1, C % 16 == 0, C >= 32, Co % 128 == 0, W % 8 == 0, W <= 64
+    (2, 32, 56, 56, 128),
     (3, 32, 7, 64, 128),
-    (1, 16, 8, 8, 256),
+    (1, 32, 8, 8, 256),
     (2, 48, 12, 16, 128),
-    (2, 16, 30, 40, 128),
+    (2, 32, 30, 40, 128),
     (1, 32, 5, 24, 128),
-    (5, 16, 9, 48, 128),
-    (16, 16, 56, 56, 128),     # enough tiles for the chunk-pair plan and the XCD remap
+    (5, 64, 9, 48, 128),
+    (16, 32, 56, 56, 128),     # enough tiles for the chunk-pair plan and the XCD remap
+    (2, 16, 56, 56, 128),      # C = 16: one stage, served by the general kernel
 ]
 
 
 @pytest.mark.parametrize("shape", FAST3x3, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("integer", [True, False])
-def test_conv3x3_fast_kernel(shape, integer):
+@pytest.mark.parametrize("ws", [False, True])
+def test_conv3x3_fast_kernel(shape, integer, ws):
+    """The 3x3 kernel, with weights transposed in the kernel (no workspace) or
+    repacked into a workspace first (conv2d_fwd_bf16_ws)."""
     N, C, H, W, Co = shape
     wl = synth.Workload("fast3x3", 2, N, C, (H, W), Co, 3, 1, 1, "bf16", "normal", 400)
-    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer, with_bias=(sum(shape) % 2 == 0))
     y_ref, S = reference(wl, t)
-    compare(_go(wl, t, "mfma"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
+    x, w, b = dev(t.x, None), dev(t.w, None), dev(t.b, np.float32)
+    work = B.workspace_for(x, w, 1, 1, "mfma") if ws else None
+    if ws and C >= 32:
+        assert work is not None and work.numel() == Co * C * 9 * 2
+    y = poisoned(wl.y_shape)
+    B.conv(x, w, b, 1, 1, algo="mfma", out=y, workspace=work)
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], exact=integer,
+            label="%s int=%s ws=%s" % (shape, integer, ws))
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_headline_workload_with_workspace(integer):
+    wl = synth.WORKLOADS["conv3x3_bf16"]
+    t = synth.make_inputs(wl, integer=integer)
+    y_ref, S = reference(wl, t)
+    x, w, b = dev(t.x, None), dev(t.w, None), dev(t.b, np.float32)
+    work = B.workspace_for(x, w, 1, 1)
+    for _ in range(2):          # the workspace is rewritten on every call
+        y = poisoned(wl.y_shape)
+        B.conv(x, w, b, 1, 1, out=y, workspace=work)
+        torch.cuda.synchronize()
+        compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], exact=integer, label="headline ws int=%s" % integer)
