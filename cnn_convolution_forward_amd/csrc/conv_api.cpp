@@ -76,12 +76,14 @@ conv_status_t check_alias(const Shape &sh, int esize, const void *x, const void 
 
 conv_status_t to_status(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_ERR_HIP; }
 
-// Thin stem layers (C_in*K^dims <= 32) have too little reduction to feed the
-// matrix cores well; they go to the direct VALU kernel.
+// AUTO: the matrix cores, except for a thin reduction (C_in*K^dims <= 32)
+// whose input patch is too wide for the short-reduction kernel's LDS tile;
+// that goes to the direct VALU kernel.
 constexpr int64_t kValuMaxK = 32;
 
 int pick_route(const Shape &sh, int algo) {
     if (algo != CONV_ALGO_AUTO) return algo;
+    if (convfwd::smallk_supported(sh)) return CONV_ALGO_MFMA;
     return sh.kgemm() <= kValuMaxK ? CONV_ALGO_VALU : CONV_ALGO_MFMA;
 }
 
@@ -149,14 +151,16 @@ conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, cons
 
 namespace convfwd {
 
-// MFMA route: a specialised kernel when the shape matches one, else the
-// general implicit GEMM.
+// MFMA route: a specialised kernel when the shape matches one (3x3 stride 1,
+// pointwise, short reduction), else the general implicit GEMM.
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                              const float *bias, float *y, hipStream_t st, void *ws, size_t ws_bytes) {
     if (conv3x3s1_supported(sh, x, w)) {
         uint16_t *wp = (ws && ws_bytes >= conv3x3s1_workspace_bytes(sh)) ? (uint16_t *)ws : nullptr;
         return launch_conv3x3s1_bf16(sh, x, w, wp, bias, y, st);
     }
+    if (conv1x1_supported(sh, x, w)) return launch_conv1x1_bf16(sh, x, w, bias, y, st);
+    if (smallk_supported(sh)) return launch_smallk_bf16(sh, x, w, bias, y, st);
     return launch_igemm_generic_bf16(sh, x, w, bias, y, st);
 }
 

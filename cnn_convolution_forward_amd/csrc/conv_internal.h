@@ -49,6 +49,14 @@ size_t conv3x3s1_workspace_bytes(const Shape &sh);
 // conv3x3s1_workspace_bytes() bytes that receives the repacked weights first.
 hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
                                  const float *bias, float *y, hipStream_t st);
+// Pointwise (K = 1, stride 1, pad 0) GEMM kernel.
+bool conv1x1_supported(const Shape &sh, const void *x, const void *w);
+hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                               const float *bias, float *y, hipStream_t st);
+// Short-reduction (C_in * K^dims <= 128) implicit GEMM: stems and first 3D layers.
+bool smallk_supported(const Shape &sh);
+hipError_t launch_smallk_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                              float *y, hipStream_t st);
 hipError_t launch_valu_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                     const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_f32(const Shape &sh, const float *x, const float *w,

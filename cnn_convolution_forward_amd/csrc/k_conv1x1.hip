@@ -1,0 +1,191 @@
+// k_conv1x1.hip -- pointwise convolution (K = 1, stride 1, pad 0), bf16 in,
+// fp32 accumulate and out, on the gfx950 matrix cores.
+//
+// With K = 1 the patch matrix X_col of "Why use matrix multiplication for
+// convolution" (2.2) is the input itself: column (n, q) of X_col is the
+// C_in-vector x[n, :, q], so Y_n = W_row @ X_n for every image, with W_row the
+// (C_out, C_in) weight view (same page, 2.3) and X_n the (C_in, plane) slice
+// of x.  No gather and no padding: the kernel is a plain GEMM whose B operand
+// is read in NCHW order.
+//
+// Tiling: a workgroup computes 128 output channels x 128 output pixels (the
+// pixel axis runs over N * plane, so a tile may straddle two images); four
+// waves in a 2 x 2 grid, each 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K loop in
+// stages of 32 input channels, double-buffered in LDS and prefetched into
+// registers one stage ahead.  Both operands land in LDS in memory order:
+//   A  [oc 128][ic 32] (+8 pad) -- a 16-byte read gives a lane its 8 k;
+//   B  [ic 32][px 128] (+16 pad) -- pixels contiguous as in NCHW; the
+//      transposing LDS read ds_read_b64_tr_b16 turns four rows of 4-pixel
+//      chunks into 4 consecutive k per pixel, two reads per fragment.
+// Epilogue: bias is the accumulators' initial value; fp32 stores go to
+// y[n][oc][q], 32 lanes on 32 consecutive pixels of one channel.
+//
+// The layer is bound by its output bytes (4 * C_out per pixel against 2 * C_in
+// read), so the goal is a steady store stream: small LDS footprint (38 KB) and
+// ~128 VGPRs let several workgroups share a CU, and block indices are mapped
+// so that the C_out / 128 tiles of one pixel range run on the same XCD and
+// read that pixel range from its L2 once.
+//
+// Requirements (checked by the launcher): K = 1, stride 1, pad 0, C_in % 32
+// == 0, plane % 8 == 0, 16-byte aligned x and w, x and w below 2 GiB.
+#include "conv_internal.h"
+#include "mfma_common.h"
+
+namespace convfwd {
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kLdA = kBK + 8;     // 80-byte rows: 16-byte reads of 8 consecutive rows are conflict-free
+constexpr int kLdB = kBN + 16;    // 288-byte rows: the 4 rows of a transposing read start 8 banks apart
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+__global__ __launch_bounds__(256)
+void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                    const float *__restrict__ bias, float *__restrict__ y,
+                    int C, int Co, int plane, int64_t P, int npt, int ncb, int remap) {
+    __shared__ __align__(16) uint16_t As[2][kBM][kLdA];
+    __shared__ __align__(16) uint16_t Bs[2][kBK][kLdB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // block -> (pixel tile, channel block); the ncb blocks of a pixel tile are
+    // consecutive logical tiles, and each XCD (block % 8) runs a contiguous range.
+    const int T = npt * ncb;
+    int L = blockIdx.x;
+    if (remap) L = (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
+    const int pt = L / ncb, ob = L - pt * ncb;
+    const int m0 = ob * kBM;
+    const int64_t j0 = (int64_t)pt * kBN;
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(P / plane * C * plane * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)Co * C * 2));
+
+    // loader units: A u -> (row u/4, k-quad u%4); B u -> (k row u/16, 8-pixel group u%16)
+    uint32_t a_off[2], b_off[2];
+    const uint32_t b_step = (uint32_t)kBK * plane * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = tid + 256 * i;
+        const int row = u >> 2, kq = u & 3;
+        a_off[i] = (m0 + row < Co) ? (uint32_t)(((int64_t)(m0 + row) * C + kq * 8) * 2) : kOob;
+        const int kr = u >> 4, pu = u & 15;
+        const int64_t px = j0 + pu * 8;
+        if (px < P) {
+            const int64_t n = px / plane, q = px - n * plane;
+            b_off[i] = (uint32_t)(((n * C + kr) * plane + q) * 2);
+        } else {
+            b_off[i] = kOob;
+        }
+    }
+    uint4 a_reg[2], b_reg[2];
+    auto load = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            a_reg[i] = bload16(wr, a_off[i], (uint32_t)(kt * kBK * 2));
+            b_reg[i] = bload16(xr, b_off[i], (uint32_t)kt * b_step);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = tid + 256 * i;
+            *reinterpret_cast<uint4 *>(&As[buf][u >> 2][(u & 3) * 8]) = a_reg[i];
+            *reinterpret_cast<uint4 *>(&Bs[buf][u >> 4][(u & 15) * 8]) = b_reg[i];
+        }
+    };
+
+    // accumulators start at bias[oc]
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int oc = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+            const float b0 = (bias && oc < Co) ? bias[oc] : 0.f;
+            acc[i][0][r] = b0;
+            acc[i][1][r] = b0;
+        }
+
+    // per-lane LDS coordinates of the operands
+    const int a_row = wm * 64 + (lane & 31), a_k = 8 * (lane >> 5);
+    const int b_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int b_col = wn * 64 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    const int nk = C / kBK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            uint4 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const uint4 *>(&As[buf][a_row + i * 32][kk * 16 + a_k]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint2 lo = read_tr(&Bs[buf][kk * 16 + b_row][b_col + j * 32]);
+                const uint2 hi = read_tr(&Bs[buf][kk * 16 + b_row + 4][b_col + j * 32]);
+                b[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: y[n][oc][q]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t px = j0 + wn * 64 + j * 32 + (lane & 31);
+        if (px >= P) continue;
+        const int64_t n = px / plane, q = px - n * plane;
+        float *yb = y + n * Co * plane + q;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int oc = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+                if (oc < Co) yb[(int64_t)oc * plane] = acc[i][j][r];
+            }
+    }
+}
+
+}  // namespace
+
+bool conv1x1_supported(const Shape &sh, const void *x, const void *w) {
+    const int64_t plane = sh.out_plane();
+    return sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
+           plane < (INT64_C(1) << 31) && sh.x_elems() * 2 < (INT64_C(1) << 31) &&
+           sh.w_elems() * 2 < (INT64_C(1) << 31) &&
+           ((uintptr_t)x % 16) == 0 && ((uintptr_t)w % 16) == 0;
+}
+
+hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
+                               const float *bias, float *y, hipStream_t st) {
+    const int64_t P = sh.pixels();
+    const int plane = (int)sh.out_plane();
+    const int npt = (int)((P + kBN - 1) / kBN);
+    const int ncb = (sh.Co + kBM - 1) / kBM;
+    const int64_t T = (int64_t)npt * ncb;
+    const int remap = (T % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co,
+                       plane, P, npt, ncb, remap);
+    return hipGetLastError();
+}
+
+}  // namespace convfwd

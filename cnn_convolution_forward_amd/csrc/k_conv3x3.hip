@@ -100,14 +100,6 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t a, int ha, uint32_t b, 
     return __builtin_amdgcn_perm(b, a, sel);
 }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-constexpr uint32_t kOob = 0x80000000u;     // buffer offset past any valid byte: loads 0, stores dropped
 
 // Where one thread loads the input of a tile from, and where it puts it in LDS.
 struct LoadCtx {
@@ -487,26 +479,38 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 
 // Repack OIHW 3x3 weights for the PACKED kernel: for every 128-channel block
 // and 16-channel stage, the 36 KB image that stage occupies in LDS
-// ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  One thread
-// writes one 16-byte unit.
+// ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  A workgroup
+// takes 16 output channels of one stage: it reads their 16 x 144 contiguous
+// source values with dword loads into LDS, then writes 288 16-byte units, 32
+// consecutive units (512 bytes) per tap.
+constexpr int kPackOc = 16;
+
 __global__ __launch_bounds__(256)
 void pack_w3x3_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wp, int C, int Co) {
+    __shared__ uint32_t src[kPackOc * kIcStage * 9 / 2];
     const int S = C / kIcStage;
-    const int64_t units = (int64_t)Co * C * 9 / 8;
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (u >= units) return;
-    const int64_t chunk = u / (9 * kOcTile * 2);
-    const int rem = (int)(u - chunk * (9 * kOcTile * 2));
-    const int t = rem / (kOcTile * 2), r2 = rem - t * (kOcTile * 2);
-    const int ocl = r2 >> 1, slot = r2 & 1;
-    const int h = slot ^ wswz(ocl);
-    const int ocb = (int)(chunk / S), st = (int)(chunk - (int64_t)ocb * S);
-    const int64_t oc = (int64_t)ocb * kOcTile + ocl;
-    const int ic0 = st * kIcStage + h * 8;
-    uint16_t v[8];
+    const int oc0 = blockIdx.x * kPackOc, st = blockIdx.y;
+    const int tid = threadIdx.x;
+    constexpr int kRowDw = kIcStage * 9 / 2;                  // 72 dwords per output channel
+    for (int i = tid; i < kPackOc * kRowDw; i += 256) {
+        const int r = i / kRowDw, c = i - r * kRowDw;
+        const uint32_t *row = reinterpret_cast<const uint32_t *>(w + ((int64_t)(oc0 + r) * C + st * kIcStage) * 9);
+        src[i] = row[c];
+    }
+    __syncthreads();
+    const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
+    const int ocb = oc0 / kOcTile;
+    uint16_t *chunk = wp + ((int64_t)ocb * S + st) * (9 * kOcTile * kIcStage);
+    for (int v = tid; v < 9 * kPackOc * 2; v += 256) {
+        const int t = v / (kPackOc * 2), r = v - t * (kPackOc * 2);
+        const int i = r >> 1, slot = r & 1;
+        const int ocl = (oc0 % kOcTile) + i;
+        const int h = slot ^ wswz(ocl);
+        uint16_t e8[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = w[(oc * C + ic0 + e) * 9 + t];
-    *reinterpret_cast<uint4 *>(wp + u * 8) = pack8(v);
+        for (int e = 0; e < 8; ++e) e8[e] = s16[i * (kIcStage * 9) + (h * 8 + e) * 9 + t];
+        *reinterpret_cast<uint4 *>(chunk + ((int64_t)t * kOcTile * 2 + ocl * 2 + slot) * 8) = pack8(e8);
+    }
 }
 
 // MFMA column steps (32 pixels each) that the busier pixel-wave of a tile runs.
@@ -655,9 +659,8 @@ hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint1
     }
     const Plan pl = last;
     if (wpack) {
-        const int64_t units = (int64_t)sh.Co * sh.C * 9 / 8;
-        hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, wpack,
-                           sh.C, sh.Co);
+        hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)(sh.Co / kPackOc), (unsigned)(sh.C / kIcStage)),
+                           dim3(256), 0, st, w, wpack, sh.C, sh.Co);
     }
     dim3 grid((unsigned)grid_size(pl, slots_for(sh, num_cu)), (unsigned)(sh.Co / kOcTile));
 #define CONV3X3_LAUNCH(RP)                                                                          \

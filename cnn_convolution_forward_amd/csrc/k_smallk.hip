@@ -1,0 +1,208 @@
+// k_smallk.hip -- implicit-GEMM convolution for a short reduction
+// (C_in * K^dims <= 128: RGB stems, first 3D layers), any K, stride and pad,
+// 2D or 3D, bf16 in, fp32 accumulate and out, on the gfx950 matrix cores.
+//
+// Y = W_row @ X_col ("Why use matrix multiplication for convolution", 2.3)
+// with the patch matrix X_col (same page, 2.2) never stored.  A workgroup
+// owns TR whole output rows of one (image, output depth): it copies the input
+// patch those rows read -- all C_in channels, K_d planes, (TR-1)*s + K rows and
+// (W_out-1)*s + K columns, zero outside the image ("Hand-writing Conv2D",
+// 1.2: out-of-range taps read 0) -- into LDS once, together with a table
+// koff[k] that gives, for every row k = ((ic*K_d + kd)*K + kh)*K + kw of
+// X_col, that tap's offset from a pixel's patch origin.  The X_col column of
+// output pixel (r, c) of the tile is then patch[origin(r, c) + koff[k]]: a
+// lane gathers its 8 operand values with 8 two-byte LDS reads, and padding
+// rows k >= C_in*K^dims point at a zero element.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16, D[oc][px] = W_row[oc][k] * X_col[k][px]; a
+// workgroup covers 64 output channels (two 32-row A operands, staged in LDS
+// once) and its waves walk the tile's 32-pixel columns.  Each finished column
+// is stored at once -- 32 lanes on 32 consecutive pixels of one channel -- so
+// the output, which dominates the traffic (4 * C_out bytes per pixel against
+// 2 * C_in * s^dims read), leaves as a continuous stream of full lines.
+#include "conv_internal.h"
+#include "mfma_common.h"
+
+namespace convfwd {
+namespace {
+
+constexpr int kOcBlock = 64;            // output channels per workgroup
+constexpr int kMaxK = 128;              // C_in * K^dims, padded to 16
+constexpr int kPatchElems = 16384;      // LDS patch budget (32 KB)
+constexpr int kTargetPx = 512;
+
+struct SmallKPlan {
+    int TR;          // output rows per tile
+    int Rt, Wt;      // patch rows and columns
+    int E;           // patch elements: C_in*K_d*Rt*Wt input values, then Rt*Wt zeros
+    int kg, kpad;    // reduction length and its multiple of 16
+    int tiles_h;     // tiles per (image, output depth)
+};
+
+__global__ __launch_bounds__(256)
+void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                   const float *__restrict__ bias, float *__restrict__ y) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    float *bias_s = reinterpret_cast<float *>(smem);                                 // [64]
+    uint16_t *koff = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4);              // [kpad]
+    uint16_t *ws = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4 + kMaxK * 2);    // [64][kpad]
+    uint16_t *patch = ws + kOcBlock * pl.kpad;                                        // [E]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // tile -> (n, od, oh0)
+    int t = blockIdx.x;
+    const int th = t % pl.tiles_h; t /= pl.tiles_h;
+    const int od = t % sh.Do;
+    const int n = t / sh.Do;
+    const int oh0 = th * pl.TR;
+    const int rows = min(pl.TR, sh.Ho - oh0);
+    const int npx = rows * sh.Wo;
+    const int oc0 = blockIdx.y * kOcBlock;
+
+    // ---- stage the patch: one (channel, depth, row) line per wave iteration
+    const int Dt = sh.Kd;
+    const int64_t HW = (int64_t)sh.H * sh.W;
+    const uint16_t *xn = x + (int64_t)n * sh.C * sh.D * HW;
+    // the lines after the C_in*K_d*Rt input lines form the zero region
+    const int lines = (sh.C * Dt + 1) * pl.Rt;
+    for (int li = wave; li < lines; li += 4) {
+        const int ry = li % pl.Rt, cd = li / pl.Rt;
+        const int dz = cd % Dt, c = cd / Dt;
+        const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
+        const bool row_ok = c < sh.C && id >= 0 && id < sh.D && ih >= 0 && ih < sh.H;
+        const uint16_t *src = xn + ((int64_t)c * sh.D + (row_ok ? id : 0)) * HW + (int64_t)(row_ok ? ih : 0) * sh.W;
+        uint16_t *dst = patch + (int64_t)li * pl.Wt;
+        for (int cx = lane; cx < pl.Wt; cx += 64) {
+            const int iw = cx - sh.p;
+            dst[cx] = (row_ok && iw >= 0 && iw < sh.W) ? src[iw] : (uint16_t)0;
+        }
+    }
+    // ---- tap offsets (padding rows k >= kg point at the zero region, which is
+    // longer than any pixel origin), weights (zero beyond C_out and kg), bias
+    const int KK = sh.K * sh.K, taps = Dt * KK;
+    for (int k = tid; k < pl.kpad; k += 256) {
+        int off = sh.C * Dt * pl.Rt * pl.Wt;
+        if (k < pl.kg) {
+            const int ic = k / taps;
+            int r = k - ic * taps;
+            const int kd = r / KK; r -= kd * KK;
+            const int kh = r / sh.K, kw = r - kh * sh.K;
+            off = ((ic * Dt + kd) * pl.Rt + kh) * pl.Wt + kw;
+        }
+        koff[k] = (uint16_t)off;
+    }
+    for (int i = tid; i < kOcBlock * pl.kpad; i += 256) {
+        const int r = i / pl.kpad, k = i - r * pl.kpad;
+        const int oc = oc0 + r;
+        ws[i] = (oc < sh.Co && k < pl.kg) ? w[(int64_t)oc * pl.kg + k] : (uint16_t)0;
+    }
+    if (tid < kOcBlock) bias_s[tid] = (bias && oc0 + tid < sh.Co) ? bias[oc0 + tid] : 0.f;
+    __syncthreads();
+
+    const int ksteps = pl.kpad / 16;
+    const int khalf = 8 * (lane >> 5);
+    // A operands: rows oc0 + ob*32 + lane%32, k = 16t + khalf .. +7
+    uint4 a[2][kMaxK / 16];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int s = 0; s < kMaxK / 16; ++s)
+            if (s < ksteps)
+                a[ob][s] = *reinterpret_cast<const uint4 *>(ws + (ob * 32 + (lane & 31)) * pl.kpad + 16 * s + khalf);
+
+    const int64_t plane = sh.out_plane();
+    const int64_t q0 = ((int64_t)od * sh.Ho + oh0) * sh.Wo;
+    float *yt = y + ((int64_t)n * sh.Co + oc0) * plane + q0;
+    const int nfrag = (npx + 31) / 32;
+    for (int f = wave; f < nfrag; f += 4) {
+        const int p = f * 32 + (lane & 31);
+        const int pc = p < npx ? p : npx - 1;
+        const int orow = pc / sh.Wo, ocol = pc - orow * sh.Wo;
+        const int base = orow * sh.s * pl.Wt + ocol * sh.s;
+        f32x16_t acc[2];
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(bias_s + ob * 32 + 8 * g + 4 * (lane >> 5));
+                acc[ob][4 * g + 0] = b4.x; acc[ob][4 * g + 1] = b4.y;
+                acc[ob][4 * g + 2] = b4.z; acc[ob][4 * g + 3] = b4.w;
+            }
+#pragma unroll
+        for (int s = 0; s < kMaxK / 16; ++s) {
+            if (s < ksteps) {
+                const uint4 ko = *reinterpret_cast<const uint4 *>(koff + 16 * s + khalf);
+                const uint32_t kv[4] = {ko.x, ko.y, ko.z, ko.w};
+                uint32_t bw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = patch[base + (kv[e] & 0xffffu)];
+                    const uint32_t hi = patch[base + (kv[e] >> 16)];
+                    bw[e] = lo | (hi << 16);
+                }
+                const uint4 b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+                acc[0] = mfma32x32x16(a[0][s], b, acc[0]);
+                acc[1] = mfma32x32x16(a[1][s], b, acc[1]);
+            }
+        }
+        if (p < npx) {
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ocl = ob * 32 + mfma32_row(r, lane);
+                    if (oc0 + ocl < sh.Co) yt[(int64_t)ocl * plane + p] = acc[ob][r];
+                }
+        }
+    }
+}
+
+int64_t patch_elems(const Shape &sh, int TR) {
+    const int64_t Rt = (int64_t)(TR - 1) * sh.s + sh.K;
+    const int64_t Wt = (int64_t)(sh.Wo - 1) * sh.s + sh.K;
+    return ((int64_t)sh.C * sh.Kd + 1) * Rt * Wt;
+}
+
+SmallKPlan make_smallk_plan(const Shape &sh) {
+    SmallKPlan pl{};
+    pl.kg = (int)sh.kgemm();
+    pl.kpad = (pl.kg + 15) / 16 * 16;
+    int TR = kTargetPx / sh.Wo;
+    if (TR < 1) TR = 1;
+    if (TR > sh.Ho) TR = sh.Ho;
+    while (TR > 1 && patch_elems(sh, TR) > kPatchElems) --TR;
+    // even out the row tiles of a plane
+    const int tiles = (sh.Ho + TR - 1) / TR;
+    TR = (sh.Ho + tiles - 1) / tiles;
+    pl.TR = TR;
+    pl.Rt = (TR - 1) * sh.s + sh.K;
+    pl.Wt = (sh.Wo - 1) * sh.s + sh.K;
+    pl.E = (int)patch_elems(sh, TR);
+    pl.tiles_h = tiles;
+    return pl;
+}
+
+size_t smem_bytes(const SmallKPlan &pl) {
+    return (size_t)kOcBlock * 4 + kMaxK * 2 + (size_t)kOcBlock * pl.kpad * 2 + (size_t)pl.E * 2;
+}
+
+}  // namespace
+
+bool smallk_supported(const Shape &sh) {
+    if (sh.kgemm() > kMaxK) return false;
+    if (patch_elems(sh, 1) > kPatchElems) return false;
+    return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);
+}
+
+hipError_t launch_smallk_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                              float *y, hipStream_t st) {
+    const SmallKPlan pl = make_smallk_plan(sh);
+    const int64_t tiles = (int64_t)sh.N * sh.Do * pl.tiles_h;
+    dim3 grid((unsigned)tiles, (unsigned)((sh.Co + kOcBlock - 1) / kOcBlock));
+    hipLaunchKernelGGL(smallk_kernel, grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y);
+    return hipGetLastError();
+}
+
+}  // namespace convfwd

@@ -36,4 +36,18 @@ __device__ __forceinline__ uint4 pack8(const uint16_t (&v)[8]) {
     return r;
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at p (raw buffer, 32-bit offsets).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr uint32_t kOob = 0x80000000u;     // buffer offset past any valid byte: loads 0, stores dropped
+
 }  // namespace convfwd

@@ -259,3 +259,50 @@ def test_headline_workload_with_workspace(integer):
         B.conv(x, w, b, 1, 1, out=y, workspace=work)
         torch.cuda.synchronize()
         compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], exact=integer, label="headline ws int=%s" % integer)
+
+
+# ---- the pointwise (1x1) kernel: ragged pixel and channel tiles ----------------
+
+POINTWISE = [
+    # (ndim, N, C, spatial, Co): K=1, s=1, p=0, C % 32 == 0, plane % 8 == 0
+    (2, 3, 64, (9, 8), 200),       # 216 pixels: tiles straddle images, last tile ragged; 2 ragged channel blocks
+    (2, 2, 32, (4, 4), 128),       # one partial pixel tile
+    (2, 1, 96, (16, 16), 64),      # C_out below one channel block
+    (2, 4, 256, (28, 28), 1024),   # the 1x1 workload's layer at N = 4
+    (3, 2, 32, (2, 3, 4), 96),     # 3D pointwise
+]
+
+
+@pytest.mark.parametrize("shape", POINTWISE, ids=lambda s: "x".join(map(str, s[:3] + s[3] + s[4:])))
+@pytest.mark.parametrize("integer", [True, False])
+def test_pointwise_kernel(shape, integer):
+    ndim, N, C, sp, Co = shape
+    wl = synth.Workload("pointwise", ndim, N, C, sp, Co, 1, 1, 0, "bf16", "normal", 500)
+    t = synth.make_inputs(wl, seed=N * 1000 + C + Co, integer=integer, with_bias=(Co % 3 != 0))
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "mfma"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
+
+
+# ---- the short-reduction kernel (C_in * K^dims <= 128): stems, first 3D layers ---
+
+SMALL_K = [
+    # (ndim, N, C, spatial, Co, K, s, p)
+    (2, 2, 3, (23, 37), 100, 3, 2, 1),     # stem-like, ragged rows/columns, 2 ragged channel blocks
+    (2, 1, 2, (30, 30), 64, 7, 2, 3),      # K = 7 (98 reduction rows)
+    (2, 1, 4, (40, 300), 16, 3, 1, 1),     # a wide row: one output row per tile
+    (2, 3, 3, (224, 224), 64, 3, 2, 1),    # the stem workload's layer at N = 3
+    (2, 2, 33, (7, 6), 64, 1, 1, 0),       # pointwise with C % 32 != 0
+    (3, 1, 3, (6, 10, 12), 20, 3, 1, 1),
+    (3, 2, 4, (5, 7, 9), 64, 3, 2, 1),     # 108 reduction rows, strided 3D
+    (3, 1, 3, (16, 64, 64), 64, 3, 1, 1),  # the 3D workload's layer at N = 1
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_K, ids=lambda s: "x".join(map(str, s[:3] + s[3] + s[4:])))
+@pytest.mark.parametrize("integer", [True, False])
+def test_small_reduction_kernel(shape, integer):
+    ndim, N, C, sp, Co, K, s, p = shape
+    wl = synth.Workload("smallk", ndim, N, C, sp, Co, K, s, p, "bf16", "normal", 600)
+    t = synth.make_inputs(wl, seed=N * 100 + C * 10 + K, integer=integer, with_bias=(Co % 2 == 0))
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "auto"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
