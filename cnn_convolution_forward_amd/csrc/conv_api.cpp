@@ -151,10 +151,16 @@ conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, cons
 
 namespace convfwd {
 
-// MFMA route: a specialised kernel when the shape matches one (3x3 stride 1,
-// pointwise, short reduction), else the general implicit GEMM.
+// MFMA route: a specialised kernel when the shape matches one (3x3 stride 1
+// -- the column-group kernel when a weight workspace is given --, pointwise,
+// short reduction), else the general implicit GEMM.
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                              const float *bias, float *y, hipStream_t st, void *ws, size_t ws_bytes) {
+    if (ws && ws_bytes >= conv3x3s1_workspace_bytes(sh) && conv3x3cg_supported(sh, x, w)) {
+        uint16_t *wp = (uint16_t *)ws;
+        launch_pack_w3x3(sh, w, wp, st);
+        return launch_conv3x3cg_bf16(sh, x, wp, bias, y, st);
+    }
     if (conv3x3s1_supported(sh, x, w)) {
         uint16_t *wp = (ws && ws_bytes >= conv3x3s1_workspace_bytes(sh)) ? (uint16_t *)ws : nullptr;
         return launch_conv3x3s1_bf16(sh, x, w, wp, bias, y, st);
@@ -165,7 +171,7 @@ hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
 }
 
 size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w) {
-    return conv3x3s1_supported(sh, x, w) ? conv3x3s1_workspace_bytes(sh) : 0;
+    return (conv3x3cg_supported(sh, x, w) || conv3x3s1_supported(sh, x, w)) ? conv3x3s1_workspace_bytes(sh) : 0;
 }
 
 // VALU route for bf16 inputs.

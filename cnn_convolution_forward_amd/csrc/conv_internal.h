@@ -49,6 +49,13 @@ size_t conv3x3s1_workspace_bytes(const Shape &sh);
 // conv3x3s1_workspace_bytes() bytes that receives the repacked weights first.
 hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
                                  const float *bias, float *y, hipStream_t st);
+// Repack OIHW 3x3 weights (C % 16 == 0, Co % 128 == 0) into the per-stage LDS
+// images both 3x3 kernels load: Co*C*9*2 bytes at wpack.
+void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st);
+// Column-group 3x3 stride-1 kernel (packed weights only).
+bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w);
+hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack, const float *bias,
+                                 float *y, hipStream_t st);
 // Pointwise (K = 1, stride 1, pad 0) GEMM kernel.
 bool conv1x1_supported(const Shape &sh, const void *x, const void *w);
 hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,

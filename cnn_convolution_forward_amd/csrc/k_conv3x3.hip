@@ -35,7 +35,7 @@
 // == 0, C_in >= 32, C_out % 128 == 0, W % 8 == 0, 8 <= W <= 64, 16-byte aligned x and w.
 // The kernel is instantiated for row pitches ROWPX = 10, 18, 34, 66 pixels.
 #include "conv_internal.h"
-#include "mfma_common.h"
+#include "conv3x3_common.h"
 
 namespace convfwd {
 namespace {
@@ -88,19 +88,6 @@ __host__ __device__ inline Tile decode_tile(const Plan &pl, int H, int b) {
     return tl;
 }
 
-// 16-byte halves of a 32-byte weight row are swapped on bit 2 xor bit 3 of the
-// row, so 16-byte accesses of 8 (32 banks) or 16 (64 banks) consecutive rows
-// reach distinct banks.
-__device__ __forceinline__ int wswz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
-
-// lo 16 bits from half `ha` of a, hi 16 bits from half `hb` of b (one v_perm_b32).
-__device__ __forceinline__ uint32_t pack_halves(uint32_t a, int ha, uint32_t b, int hb) {
-    const uint32_t sel = (uint32_t)(2 * ha) | ((uint32_t)(2 * ha + 1) << 8) |
-                         ((uint32_t)(4 + 2 * hb) << 16) | ((uint32_t)(5 + 2 * hb) << 24);
-    return __builtin_amdgcn_perm(b, a, sel);
-}
-
-
 // Where one thread loads the input of a tile from, and where it puts it in LDS.
 struct LoadCtx {
     __amdgpu_buffer_rsrc_t xr;   // the tile's image
@@ -110,7 +97,6 @@ struct LoadCtx {
 };
 
 // Per-thread state shared by every tile of the workgroup.
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 struct KCtx {
     uint8_t *wbuf0, *ibuf0;
@@ -153,23 +139,9 @@ __device__ __forceinline__ void dma_w_stage(const KCtx &k, int s, int buf) {
 #pragma unroll
     for (int q = 0; q < 9; ++q) {
         const int blk = k.wave * 9 + q;
-        // Issued as inline assembly: the instruction has no register result
-        // (it writes LDS), and the compiler's own waits after the builtin form
-        // would also wait for the unrelated input loads in flight.  Completion
-        // is awaited explicitly (vmcnt) before the barrier that publishes the
-        // buffer; nothing reads the target buffer before that barrier.
-        const uint32_t m0v = (uint32_t)(uintptr_t)(k.wlds0 + buf * kWBufBytes + blk * 1024);
-        const int soff = s * kWBufBytes + blk * 1024;
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :
-                     : "s"(__builtin_amdgcn_readfirstlane(m0v)), "v"(k.lane16), "s"(k.wpr),
-                       "s"(__builtin_amdgcn_readfirstlane(soff))
-                     : "m0", "memory");
+        dma_1k(k.wlds0 + buf * kWBufBytes + blk * 1024, k.wpr, k.lane16, s * kWBufBytes + blk * 1024);
     }
 }
-
-// s_waitcnt with only the vector-memory counter limited to n (n < 64).
-#define CONV3X3_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Transposed LDS writes of a loaded stage, in four parts so they can be spread
 // between MFMAs: parts 0-1 weights (taps 0-4, 5-8), parts 2-3 input (pixels 0-3, 4-7).
@@ -625,6 +597,11 @@ Plan make_plan(const Shape &sh, int slots) {
 
 }  // namespace
 
+void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st) {
+    hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)(sh.Co / kPackOc), (unsigned)(sh.C / kIcStage)),
+                       dim3(256), 0, st, w, wpack, sh.C, sh.Co);
+}
+
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t HW = (int64_t)sh.H * sh.W;
     return sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIcStage == 0 &&
@@ -659,8 +636,7 @@ hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint1
     }
     const Plan pl = last;
     if (wpack) {
-        hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)(sh.Co / kPackOc), (unsigned)(sh.C / kIcStage)),
-                           dim3(256), 0, st, w, wpack, sh.C, sh.Co);
+        launch_pack_w3x3(sh, w, wpack, st);
     }
     dim3 grid((unsigned)grid_size(pl, slots_for(sh, num_cu)), (unsigned)(sh.Co / kOcTile));
 #define CONV3X3_LAUNCH(RP)                                                                          \

@@ -1,0 +1,344 @@
+// k_conv3x3_cg.hip -- 3x3, stride 1, pad 1 convolution with column-group
+// pixel fragments, bf16 in, fp32 accumulate and out, on the gfx950 matrix cores.
+//
+// The product is Y = W_row @ X_col ("Why use matrix multiplication for
+// convolution", 2.3), with X_col never stored: for each chunk of 16 input
+// channels the workgroup holds one halo tile of the input in LDS, and the nine
+// taps of the kernel read it at shifted addresses ("Hand-writing Conv2D", 4.1:
+// unfold a tile, multiply, discard).  Zero padding exists only in LDS.
+//
+// Pixel fragments.  A v_mfma_f32_32x32x16_bf16 operand covers 32 output
+// pixels.  Here the 32 pixels of fragment c are 8 rows x 4 column groups:
+// lane n holds row n % 8, column c + D * (n / 8), with D = W / 4.  Moving one
+// column to the right maps fragment c onto fragment c + 1, so the horizontal
+// taps (kw = 0, 1, 2) of fragments c .. c + J - 1 all read the same J + 2
+// input fragments.  Moving one row down is a move by one lane inside each
+// 8-lane group (DPP), so kernel rows 1 and 2 reuse the row-0 fragments and
+// only the 8 lanes of the new bottom row read LDS.  Per 16-channel stage a
+// wave reads 9 weight fragments and J + 2 full input fragments (+ 2 (J + 2)
+// one-eighth reads) for 9 J MFMAs (20 KB for 63 MFMAs at J = 7, against
+// 126 KB when every tap reads both operands).
+//
+// Tiling: a workgroup computes 64 output channels x 8 output rows x W (one
+// tile per workgroup), four waves in a 2 x 2 grid: 32 channels x J = D/2
+// fragments each (J accumulator tiles, <= 128 accumulator registers).  Two
+// workgroups share a CU (<= 256 registers per lane, ~66 KB of LDS each), so
+// one workgroup's prologue, barriers, epilogue and output drain overlap the
+// other's MFMA work.  The K loop runs over 16-channel stages:
+//   weights  [tap 9][oc 64][ic 16], 18 KB per stage, double-buffered, copied
+//            by direct-to-LDS loads from the packed workspace
+//            (launch_pack_w3x3, 128-channel blocks; a workgroup copies the
+//            64-row half of each tap's block);
+//   input    [row 10][col RP][ic 16] at 48 bytes per pixel and an odd row
+//            pitch RP >= W + 2, so the 8 rows of a fragment column hit 8
+//            distinct 16-byte bank groups; single-buffered: the next stage is
+//            loaded into registers during the MFMAs and written transposed
+//            (NCHW keeps channels strided, the operand needs 8 consecutive)
+//            between two barriers.
+// Accumulator orientation D[px][oc]: lane l owns channel l % 32, and its 16
+// slots are pixels (rows 4*(l/32) .. +3) x (4 column groups); across its J
+// fragments a lane holds J consecutive columns of each (row, group).  The
+// epilogue stages 16 channels at a time in LDS as [channel][row][column] and
+// stores them back in 16-byte chunks as whole 8-row blocks of each channel,
+// contiguous in y (bias is the accumulators' initial value).
+//
+// Requirements (checked by the launcher): K = 3, s = 1, p = 1, C_in % 16 == 0,
+// C_out % 128 == 0, W % 8 == 0, 32 <= W <= 64, packed weights, 16-byte
+// aligned x.
+#include "conv_internal.h"
+#include "conv3x3_common.h"
+
+namespace convfwd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kOc = 64;                  // output channels per workgroup
+constexpr int kPackOcBlock = 128;        // channel block of the packed weight layout
+constexpr int kIc = 16;                  // input channels per stage
+constexpr int kRows = 8;                 // output rows per tile
+constexpr int kInRows = kRows + 2;       // input rows per tile (halo)
+constexpr int kPix = 48;                 // LDS bytes per input pixel: 16 bf16 + 16 pad
+constexpr int kTapBytes = kOc * 32;      // one tap's weights in LDS (2 KB)
+constexpr int kWStage = 9 * kTapBytes;   // 18432 bytes of weights per stage
+constexpr int kPackStage = 9 * kPackOcBlock * 32;   // 36864: one stage of a packed 128-channel block
+constexpr int kEpiOc = 16;               // channels per epilogue pass
+constexpr int kEpiBytes = kEpiOc * (kRows * 64 + 4) * 4;   // largest pass image (W = 64)
+
+template <int D>
+struct Geo {
+    static constexpr int W = 4 * D;
+    static constexpr int J = D / 2;                       // fragments per pixel-wave
+    static constexpr int RP = (W + 2) | 1;                // odd input row pitch (pixels)
+    static constexpr int IN_BYTES = kInRows * RP * kPix;
+    static constexpr int LDS = 2 * kWStage + IN_BYTES > kEpiBytes ? 2 * kWStage + IN_BYTES : kEpiBytes;
+    static constexpr int UNITS = 2 * kInRows * (W / 8);   // input load units per stage
+};
+
+// Rows of a fragment one down: lane 8g + r takes lane 8g + r + 1 (DPP
+// row_shl:1 inside each 16-lane row).  Lanes 8g + 7 receive a wrong or zero
+// value and are overwritten by the caller.
+__device__ __forceinline__ uint4 rows_down(const uint4 &v) {
+    uint4 r;
+    r.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x101, 0xf, 0xf, true);
+    r.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x101, 0xf, 0xf, true);
+    r.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x101, 0xf, 0xf, true);
+    r.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x101, 0xf, 0xf, true);
+    return r;
+}
+
+__device__ __forceinline__ uint4 pick(bool c, const uint4 &a, const uint4 &b) {
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// The MFMAs of input-fragment column q (column c0 - 1 + q of this wave's
+// range) and kernel row rr: the fragment serves output fragment j = q - kw
+// for the three horizontal taps kw.
+template <int D, int RR>
+__device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], const uint4 &b, int q) {
+    constexpr int J = Geo<D>::J;
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw) {
+        const int j = q - kw;
+        if (j >= 0 && j < J) acc[j] = mfma32x32x16(b, A[RR * 3 + kw], acc[j]);
+    }
+}
+
+// Column step q.  The kernel-row-0 fragment of column q comes from LDS; the
+// fragments of kernel rows 1 and 2 are the row-0 (row-1) fragment moved one
+// row down across lanes, plus one new row that only lanes 8g + 7 read from
+// LDS (8 of 64 lanes).  A step first issues the LDS reads of column q + 1,
+// then the 9 (or fewer) MFMAs of column q, so the reads have a column of
+// MFMA work to arrive.
+template <int D, int q>
+__device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], uint4 (&B0)[2],
+                                       uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, bool row7) {
+    constexpr int J = Geo<D>::J, RP = Geo<D>::RP, Q = J + 2;
+    if constexpr (q + 1 < Q) {
+        B0[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (q + 1) * kPix);
+        if (row7) {
+            T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (RP + q + 1) * kPix);
+            T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (2 * RP + q + 1) * kPix);
+        }
+    }
+    const uint4 b0 = B0[q & 1];
+    cg_mfma<D, 0>(acc, A, b0, q);
+    const uint4 b1 = pick(row7, T1[q & 1], rows_down(b0));
+    cg_mfma<D, 1>(acc, A, b1, q);
+    const uint4 b2 = pick(row7, T2[q & 1], rows_down(b1));
+    cg_mfma<D, 2>(acc, A, b2, q);
+    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, row7);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
+void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
+                      const float *__restrict__ bias, float *__restrict__ y,
+                      int C, int H, int Co, int rb_per_img, int remap) {
+    using G = Geo<D>;
+    constexpr int W = G::W, J = G::J, RP = G::RP;
+    __shared__ __align__(16) uint8_t smem[G::LDS];
+    static_assert(G::LDS >= kEpiBytes, "the epilogue image overlays the stage buffers");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    // block -> (tile, channel half); the two halves of a tile are neighbours,
+    // and with remap consecutive tiles (which share halo rows) run on one XCD
+    // (block b runs on XCD b % 8)
+    const int T = gridDim.x;
+    int t = blockIdx.x;
+    if (remap) t = (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
+    const int half = t & 1;
+    t >>= 1;
+    const int n = t / rb_per_img;
+    const int r0 = (t - n * rb_per_img) * kRows;
+    const int ocb = (int)blockIdx.y * kPackOcBlock + half * kOc;
+    const int HW = H * W;
+    const int S = C / kIc;
+
+    uint8_t *const wbuf = smem;
+    uint8_t *const ibuf = smem + 2 * kWStage;
+    lds_u8 *const wlds = (lds_u8 *)smem;
+
+    // ---- input loader: unit u -> (row rho, 8-pixel group pg, channel half g8);
+    // rows fastest so neighbouring lanes write LDS rows RP pixels apart
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)n * C * HW, (uint32_t)C * HW * 2);
+    const bool in_active = tid < G::UNITS;
+    const int rho = tid % kInRows, rest = tid / kInRows;
+    const int pg = rest % (W / 8), g8 = in_active ? rest / (W / 8) : 0;
+    const int ih = r0 - 1 + rho;
+    const uint32_t ivoff = (in_active && ih >= 0 && ih < H)
+                               ? (uint32_t)((g8 * 8 * HW + ih * W + pg * 8) * 2) : kOob;
+    const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + 1) * kPix + g8 * 16);
+    const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = chan_bytes * kIc;
+    uint4 xin[8];
+    auto load_x = [&](int s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xin[e] = bload16(xr, ivoff, (uint32_t)s * stage_bytes + e * chan_bytes);
+    };
+    auto store_x = [&]() {
+        if (!in_active) return;
+        const uint32_t *v = reinterpret_cast<const uint32_t *>(xin);   // v[e*4 + j/2]: channel e, pixels j, j+1
+        uint8_t *dst = ibuf + idst;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int dj = j >> 1, hj = j & 1;
+            uint4 o;
+            o.x = pack_halves(v[0 * 4 + dj], hj, v[1 * 4 + dj], hj);
+            o.y = pack_halves(v[2 * 4 + dj], hj, v[3 * 4 + dj], hj);
+            o.z = pack_halves(v[4 * 4 + dj], hj, v[5 * 4 + dj], hj);
+            o.w = pack_halves(v[6 * 4 + dj], hj, v[7 * 4 + dj], hj);
+            *reinterpret_cast<uint4 *>(dst + j * kPix) = o;
+        }
+    };
+    // ---- weights: 18 x 1 KB blocks per stage (tap t, sub-block u: rows
+    // 32u .. 32u+31 of this workgroup's 64-row half of the packed block);
+    // wave w copies blocks w, w + 4, ...
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp + (int64_t)blockIdx.y * kPackOcBlock * C * 9,
+                                                (uint32_t)kPackOcBlock * C * 9 * 2);
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    auto dma_w = [&](int s, int buf) {
+        for (int blk = wave; blk < 18; blk += 4) {
+            const int tap = blk >> 1, u = blk & 1;
+            dma_1k(wlds + buf * kWStage + tap * kTapBytes + u * 1024, wr, lane16,
+                   s * kPackStage + tap * (kPackOcBlock * 32) + half * kTapBytes + u * 1024);
+        }
+    };
+
+    // operand addresses: A (weights) row wm*32 + l32 of the tap, k half h
+    // (swizzled on the row's bits 2-3, which the 64-row offset leaves alone);
+    // B (input fragment) for fragment column c' = c0 - 1 + q at kernel row rr
+    // is b_base + (rr*RP + q) * 48
+    const uint32_t a_off = (uint32_t)((wm * 32 + l32) * 32 + ((h ^ wswz(l32)) * 16));
+    const int c0 = wn * J;
+    const uint32_t b_base = (uint32_t)((((l32 & 7) * RP) + D * (l32 >> 3) + c0) * kPix + h * 16);
+    const bool row7 = (l32 & 7) == 7;        // lanes that read the new row of kernel rows 1 and 2
+
+    // zero the input buffer: halo columns are never written again
+    for (int i = tid; i < G::IN_BYTES / 16; i += kThreads)
+        reinterpret_cast<uint4 *>(ibuf)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    // ---- prologue: stage 0
+    dma_w(0, 0);
+    load_x(0);
+    const float bv = bias ? bias[ocb + wm * 32 + l32] : 0.f;
+    CONV3X3_WAIT_VMCNT(0);
+    store_x();
+    __syncthreads();
+
+    // accumulators start at this lane's channel bias
+    f32x16_t acc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = bv;
+
+    for (int s = 0; s < S; ++s) {
+        const int b = s & 1;
+        const bool more = s + 1 < S;
+        if (more) {
+            dma_w(s + 1, b ^ 1);
+            load_x(s + 1);
+        }
+        const uint8_t *wb = wbuf + b * kWStage + a_off;
+        const uint8_t *ib = ibuf + b_base;
+        uint4 A[9], B0[2], T1[2], T2[2];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) A[t] = *reinterpret_cast<const uint4 *>(wb + t * kTapBytes);
+        B0[0] = *reinterpret_cast<const uint4 *>(ib);
+        if (row7) {
+            T1[0] = *reinterpret_cast<const uint4 *>(ib + RP * kPix);
+            T2[0] = *reinterpret_cast<const uint4 *>(ib + 2 * RP * kPix);
+        }
+        cg_col<D, 0>(acc, A, B0, T1, T2, ib, row7);
+        CONV3X3_WAIT_VMCNT(0);      // weights of the next stage in LDS, its input in registers
+        __syncthreads();            // every wave is done with the input buffer
+        if (more) {
+            store_x();
+            __syncthreads();        // next stage's input and weights visible
+        }
+    }
+
+    // ---- epilogue: 4 passes of 16 channels through LDS, then whole rows out.
+    // Pass p: channels 16p .. 16p+15 = wave row wm = p/2, lanes with
+    // l32 / 16 == p % 2.  The pass image is [channel 16][row 8][column W]
+    // fp32 with a channel pitch of 8W + 4 dwords; a writer lane puts slot r
+    // (row 4h + r%4, group r/4) of fragment j at column c0 + j + D*(r/4).
+    // Readback: 16-byte chunks, consecutive threads on consecutive chunks of
+    // one channel's 8 rows -- a contiguous 32*W-byte block of y -- so every
+    // store instruction writes 1 KB of consecutive output.
+    float *const epi = reinterpret_cast<float *>(smem);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + ((int64_t)n * Co + ocb) * HW, (uint32_t)kOc * HW * 4);
+    constexpr int kChPitch = kRows * W + 4;
+    constexpr int kChunks = kEpiOc * kRows * W / 4;      // 16-byte chunks per pass
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (wm == (p >> 1) && (l32 >> 4) == (p & 1)) {
+            float *dst = epi + (l32 & 15) * kChPitch + c0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 4 * h + (r & 3), grp = r >> 2;
+#pragma unroll
+                for (int j = 0; j < J; ++j) dst[row * W + grp * D + j] = acc[j][r];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
+            const int cid = k * kThreads + tid;
+            if (kChunks % kThreads == 0 || cid < kChunks) {
+                const int ocl = cid / (kRows * W / 4), e = cid - ocl * (kRows * W / 4);   // e: chunk within the 8 rows
+                const int row = (4 * e) / W;
+                const float4 a4 = *reinterpret_cast<const float4 *>(epi + ocl * kChPitch + 4 * e);
+                const bool ok = r0 + row < H;
+                const uint32_t vo = ok ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + 4 * e) * 4) : kOob;
+                const u32x4_t va = {__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
+                                    __float_as_uint(a4.w)};
+                __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
+            }
+        }
+        if (p < 3) __syncthreads();
+    }
+}
+
+}  // namespace
+
+bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
+    (void)w;
+    const int64_t HW = (int64_t)sh.H * sh.W;
+    return sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
+           sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
+           (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
+           (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range
+           (int64_t)kPackOcBlock * sh.C * 9 * 2 < (INT64_C(1) << 31) &&
+           (int64_t)sh.N * ((sh.H + kRows - 1) / kRows) * 2 < (INT64_C(1) << 31) &&
+           ((uintptr_t)x % 16) == 0;
+}
+
+hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack, const float *bias,
+                                 float *y, hipStream_t st) {
+    const int rb = (sh.H + kRows - 1) / kRows;
+    const int64_t blocks = (int64_t)sh.N * rb * 2;       // tiles x two 64-channel halves
+    const int remap = (blocks % 8 == 0) ? 1 : 0;
+    dim3 grid((unsigned)blocks, (unsigned)(sh.Co / kPackOcBlock));
+#define CONV3X3CG_LAUNCH(DV)                                                                          \
+    hipLaunchKernelGGL((conv3x3cg_kernel<DV>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
+                       sh.Co, rb, remap)
+    switch (sh.W / 4) {
+        case 8: CONV3X3CG_LAUNCH(8); break;
+        case 10: CONV3X3CG_LAUNCH(10); break;
+        case 12: CONV3X3CG_LAUNCH(12); break;
+        case 14: CONV3X3CG_LAUNCH(14); break;
+        case 16: CONV3X3CG_LAUNCH(16); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef CONV3X3CG_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace convfwd

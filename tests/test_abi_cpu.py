@@ -123,7 +123,8 @@ def test_workspace_entry_point_validation():
     assert need == 128 * 128 * 9 * 2
     assert B.conv2d_fwd_workspace_bytes(64, 128, 56, 56, 128, 3, 1, 1, 2) == 0     # VALU route
     assert B.conv2d_fwd_workspace_bytes(2, 3, 9, 11, 4, 3, 2, 1, 0) == 0          # no route needs one
-    assert B.conv2d_fwd_workspace_bytes(2, 16, 56, 56, 128, 3, 1, 1, 0) == 0      # one stage: general kernel
+    assert B.conv2d_fwd_workspace_bytes(2, 16, 56, 56, 128, 3, 1, 1, 0) == 128 * 16 * 9 * 2   # one stage
+    assert B.conv2d_fwd_workspace_bytes(2, 16, 9, 12, 128, 3, 1, 1, 0) == 0       # W = 12: general kernel
     args = (64, 128, 56, 56, 128, 3, 1, 1, 0, None)
     assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, None, 0, *args) == 6
     assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS, need - 2, *args) == 6

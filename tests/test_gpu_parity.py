@@ -222,7 +222,9 @@ FAST3x3 = [
     (1, 32, 5, 24, 128),
     (5, 64, 9, 48, 128),
     (16, 32, 56, 56, 128),     # enough tiles for the chunk-pair plan and the XCD remap
-    (2, 16, 56, 56, 128),      # C = 16: one stage, served by the general kernel
+    (2, 16, 56, 56, 128),      # C = 16: one stage (general kernel without a workspace)
+    (3, 32, 17, 32, 256),      # W = 32, two channel blocks, ragged last row block
+    (1, 16, 8, 56, 128),       # one row block, one stage
 ]
 
 
@@ -238,7 +240,7 @@ def test_conv3x3_fast_kernel(shape, integer, ws):
     y_ref, S = reference(wl, t)
     x, w, b = dev(t.x, None), dev(t.w, None), dev(t.b, np.float32)
     work = B.workspace_for(x, w, 1, 1, "mfma") if ws else None
-    if ws and C >= 32:
+    if ws and (C >= 32 or 32 <= W <= 56):
         assert work is not None and work.numel() == Co * C * 9 * 2
     y = poisoned(wl.y_shape)
     B.conv(x, w, b, 1, 1, algo="mfma", out=y, workspace=work)
