@@ -5,19 +5,23 @@
                     [--no-cpu-baseline] [--report]
 
 A step is one full forward pass of the convolution (every kernel of the chosen
-route) over one batch of seeded synthetic input that is already resident in
-device memory.  W untimed steps, then exactly K timed steps bracketed by
-torch.cuda.synchronize().  The default workload is the 3x3 layer (N=64,
-C_in=C_out=128, 56x56, stride 1, pad 1, bf16 in, fp32 out).
+route, the weight repack included) over one batch of seeded synthetic input
+that is already resident in device memory.  W untimed steps, then exactly K
+timed steps bracketed by torch.cuda.synchronize().  The default workload is
+the 3x3 layer (N=64, C_in=C_out=128, 56x56, stride 1, pad 1, bf16 in, fp32
+out).
 
 One JSON line on stdout:
   value        FLOP/s of the whole job (2*N*C_out*H_out*W_out*C_in*K^2, padded
                taps included) / measured time, in TFLOP/s
-  roofline     the dominant kernel: algorithmic FLOP (or bytes) per launch over
-               its average launch time from HIP events recorded on the stream
-               the library launches on, against the MI355X peak
-  cpu_baseline the CPU oracle (plain fp64 loops, OpenMP) timed on a bounded
-               sample of the same workload on this host
+  roofline     the dominant kernel (the convolution): algorithmic FLOP (or
+               bytes) per launch over its average launch time from HIP events
+               recorded on the stream the library launches on, against the
+               MI355X peak; traffic = HBM bytes per launch from rocprofv3
+               counters (profiles/counters_*.json) while they match the
+               current kernel sources, else null
+  cpu_baseline the CPU oracle (plain fp64 loops, OpenMP) timed on the same
+               inputs on this host (the whole batch unless told otherwise)
 --report prints one more line per workload to stderr (all five, every route).
 """
 from __future__ import annotations
@@ -49,7 +53,7 @@ def parse():
     ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
-                    help="images in the oracle's timed sample (0 = pick ~10 s of work)")
+                    help="images in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--report", action="store_true", help="also time every workload/route (stderr)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times): the "
@@ -75,7 +79,12 @@ def bound_of(wl, route):
 
 
 class Runner:
-    """Device-resident inputs and one callable step for a workload/route."""
+    """Device-resident inputs and one callable step for a workload/route.
+
+    A step is everything one forward pass needs: for the 2D bf16 MFMA route
+    with packed weights, the weight repack (conv2d_pack_weights_bf16) and the
+    convolution (conv2d_fwd_bf16_prepacked); otherwise the one library call.
+    `main()` is the launch whose duration the roofline uses (the convolution)."""
 
     def __init__(self, wl, route, seed=None):
         import torch
@@ -93,29 +102,40 @@ class Runner:
         self.b = None if t.b is None else torch.from_numpy(t.b).cuda()
         self.y = torch.empty(wl.y_shape, dtype=torch.float32, device="cuda")
         self.ws = None
-        self.work = None
+        self.packed = None
         if route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16":
-            # device workspace for repacked weights (allocated once; the repack
-            # itself runs inside every step)
-            self.work = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
+            self.packed = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
         if route == "explicit":
             nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
                                          wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.B = B
 
-    def step(self):
+    def pre(self):
+        """Work of the step that precedes the measured launch (weight repack)."""
+        if self.packed is not None:
+            self.B.pack_weights(self.w, tuple(self.x.shape), self.wl.stride, self.wl.pad, self.route,
+                                workspace=self.packed)
+
+    def main(self):
         if self.route == "explicit":
             self.B.conv_explicit(self.x, self.w, self.b, self.wl.stride, self.wl.pad,
                                  workspace=self.ws, out=self.y)
+        elif self.packed is not None:
+            self.B.conv_prepacked(self.x, self.packed, tuple(self.w.shape), self.b, self.wl.stride,
+                                  self.wl.pad, self.route, out=self.y)
         else:
-            self.B.conv(self.x, self.w, self.b, self.wl.stride, self.wl.pad, algo=self.route, out=self.y,
-                        workspace=self.work)
+            self.B.conv(self.x, self.w, self.b, self.wl.stride, self.wl.pad, algo=self.route, out=self.y)
+
+    def step(self):
+        self.pre()
+        self.main()
 
 
 def time_steps(runner, steps, warmup):
-    """Wall time of `steps` steps (synchronised on both sides) and per-step HIP
-    event durations recorded on the stream the library launches on."""
+    """Wall time of `steps` steps (synchronised on both sides) and, per step,
+    the duration of the main launch from HIP events recorded on the stream
+    the library launches on (torch's current stream, passed to every call)."""
     import torch
     for _ in range(warmup):
         runner.step()
@@ -125,8 +145,9 @@ def time_steps(runner, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        runner.pre()
         ev[i][0].record(stream)
-        runner.step()
+        runner.main()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -134,9 +155,36 @@ def time_steps(runner, steps, warmup):
     return wall, per
 
 
+# HBM traffic of the main kernel from rocprofv3 counters (profiles/counters_*.json):
+# FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what they read for a plain
+# copy of known size.  Used only while the kernel sources still hash to the
+# value recorded with the counters.
+def kernel_sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(workload, route):
+    import glob
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.json"))):
+        with open(f) as fh:
+            c = json.load(fh)
+        if c.get("workload") != workload or c.get("route") != route:
+            continue
+        if kernel_sources_sha(c["sources"]) != c["sources_sha256"]:
+            return None, "counters in %s predate the current kernel sources" % os.path.basename(f)
+        return c["hbm_bytes_per_dispatch"], os.path.basename(f)
+    return None, "no counter summary for this workload"
+
+
 def cpu_baseline(wl, runner, sample_images):
-    """Time the oracle on the first `sample_images` images of the same inputs;
-    also report the parity of the GPU output on that sample."""
+    """Time the oracle on the first `sample_images` images of the same inputs
+    (the whole batch by default); also report the parity of the GPU output on
+    that sample."""
     import oracle
     t = runner.t
     n = sample_images
@@ -154,7 +202,8 @@ def cpu_baseline(wl, runner, sample_images):
         rel = float(np.max(np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "%d of %d images of the same seeded inputs, one full pass, fp64" % (n, wl.N),
+            "sample": "%d of %d images of the same seeded inputs (one full forward pass over them), "
+                      "fp64" % (n, wl.N),
             "parity_on_sample": {"max_abs_delta_over_S": rel, "tau": tau, "pass": ok}}
 
 
@@ -178,6 +227,7 @@ def report_all(steps, warmup):
             _, wall, per = measure(wl, route, steps, warmup)
             t = float(np.mean(per))
             line = {"workload": name, "route": route, "us_per_call": round(t * 1e6, 2),
+                    "us_per_step": round(wall / steps * 1e6, 2),
                     "TFLOP/s": round(wl.flops() / t / 1e12, 2),
                     "pct_bf16_mfma_peak": round(100 * wl.flops() / t / 1e12 / PEAK_BF16_TFLOPS, 2),
                     "algorithmic_GB/s": round(algorithmic_bytes(wl) / t / 1e9, 1),
@@ -213,6 +263,7 @@ def main():
     flops = wl.flops()
     value = flops * args.steps / wall / 1e12
     kern = float(np.mean(per))
+    traffic, traffic_src = traffic_from_profiles(wl.name, args.route)
     bound = bound_of(wl, args.route)
     if bound == "mfma":
         ach, peak, unit = flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -228,12 +279,14 @@ def main():
         "config": describe(wl) | {"route": args.route},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                     "frac": round(ach / peak, 4), "traffic": None,
+                     "frac": round(ach / peak, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "kernel_avg_us": round(kern * 1e6, 3), "kernel_median_us": round(float(np.median(per)) * 1e6, 3),
-                     "timing": "HIP events around each launch on the library's stream"},
+                     "timing": "HIP events on the library's stream around the convolution launch of each "
+                               "timed step (the weight repack before it is in the step, not in this figure)"},
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_images or max(1, min(wl.N, 16))
+        n = args.cpu_sample_images or wl.N
         out["cpu_baseline"] = cpu_baseline(wl, runner, n)
     print(json.dumps(out), flush=True)
     if args.report:

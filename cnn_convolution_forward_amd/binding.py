@@ -26,6 +26,7 @@ ALGO = {"auto": 0, "mfma": 1, "valu": 2}
 EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv2d_fwd_bf16", "conv2d_fwd_f32", "conv3d_fwd_bf16", "conv3d_fwd_f32",
            "conv2d_fwd_workspace_bytes", "conv2d_fwd_bf16_ws",
+           "conv2d_pack_weights_bf16", "conv2d_fwd_bf16_prepacked",
            "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
            "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit")
 
@@ -64,6 +65,10 @@ def lib():
         L.conv2d_fwd_workspace_bytes.argtypes = [_i] * 9
         L.conv2d_fwd_bf16_ws.restype = _i
         L.conv2d_fwd_bf16_ws.argtypes = [_vp] * 5 + [_sz] + [_i] * 9 + [_vp]
+        L.conv2d_pack_weights_bf16.restype = _i
+        L.conv2d_pack_weights_bf16.argtypes = [_vp, _vp, _sz] + [_i] * 9 + [_vp]
+        L.conv2d_fwd_bf16_prepacked.restype = _i
+        L.conv2d_fwd_bf16_prepacked.argtypes = [_vp, _vp, _sz, _vp, _vp] + [_i] * 9 + [_vp]
         L.conv_im2col_bytes.restype = _sz
         L.conv_im2col_bytes.argtypes = [_i] * 9
         L.conv2d_im2col_bf16.restype = _i
@@ -114,6 +119,16 @@ def conv3d_fwd_f32(x, w, bias, y, N, C_in, D, H, W, C_out, K, stride, pad, algo=
 
 def conv2d_fwd_workspace_bytes(N, C_in, H, W, C_out, K, stride, pad, algo=0):
     return int(lib().conv2d_fwd_workspace_bytes(N, C_in, H, W, C_out, K, stride, pad, algo))
+
+
+def conv2d_pack_weights_bf16(w, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv2d_pack_weights_bf16(w, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad, algo, stream)
+
+
+def conv2d_fwd_bf16_prepacked(x, ws, ws_bytes, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo=0,
+                              stream=None):
+    return lib().conv2d_fwd_bf16_prepacked(x, ws, ws_bytes, bias, y, N, C_in, H, W, C_out, K, stride, pad,
+                                           algo, stream)
 
 
 def conv2d_fwd_bf16_ws(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad, algo=0,
@@ -235,6 +250,49 @@ def conv(x, w, bias=None, stride=1, pad=0, algo="auto", out=None, workspace=None
         st = (conv3d_fwd_f32 if f32 else conv3d_fwd_bf16)(*args)
     if st != CONV_OK:
         raise ConvError(st, "conv%dd_fwd" % ndim)
+    return y
+
+
+def pack_weights(w, x_shape, stride=1, pad=0, algo="auto", workspace=None):
+    """Pack 2D bf16 weights for conv_prepacked (conv2d_pack_weights_bf16);
+    returns the workspace tensor.  x_shape: (N, C_in, H, W) of the inputs the
+    packed weights will be used with."""
+    torch = _torch()
+    _check_tensor(w, "w", (torch.bfloat16, torch.int16, torch.uint16))
+    N, C, H, W = x_shape
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    need = conv2d_fwd_workspace_bytes(N, C, H, W, w.shape[0], w.shape[2], stride, pad, a)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = conv2d_pack_weights_bf16(_ptr(w), _ptr(workspace), wsb, N, C, H, W, w.shape[0], w.shape[2], stride,
+                                  pad, a, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv2d_pack_weights_bf16")
+    return workspace
+
+
+def conv_prepacked(x, workspace, w_shape, bias=None, stride=1, pad=0, algo="auto", out=None):
+    """conv(x, w) + bias with w taken from pack_weights' workspace (w_shape:
+    the (C_out, C_in, K, K) shape of the packed weights)."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    _check_tensor(bias, "bias", (torch.float32,))
+    C_out, C_in, K = w_shape[0], w_shape[1], w_shape[2]
+    if x.dim() != 4 or x.shape[1] != C_in:
+        raise ValueError("x must be N x C_in x H x W with C_in = %d" % C_in)
+    outs = [conv_out_dim(d, K, stride, pad) for d in x.shape[2:]]
+    if min(outs) < 1:
+        raise ConvError(3, "conv_prepacked")
+    y = out if out is not None else torch.empty((x.shape[0], C_out, *outs), dtype=torch.float32,
+                                                device=x.device)
+    _check_tensor(y, "out", (torch.float32,))
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    wsb = workspace.numel() * workspace.element_size()
+    st = conv2d_fwd_bf16_prepacked(_ptr(x), _ptr(workspace), wsb, _ptr(bias), _ptr(y), x.shape[0], C_in,
+                                   x.shape[2], x.shape[3], C_out, K, stride, pad, a, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv2d_fwd_bf16_prepacked")
     return y
 
 

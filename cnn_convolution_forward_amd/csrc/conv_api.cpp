@@ -170,6 +170,14 @@ hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     return launch_igemm_generic_bf16(sh, x, w, bias, y, st);
 }
 
+hipError_t launch_igemm_prepacked_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack,
+                                       const float *bias, float *y, hipStream_t st) {
+    if (conv3x3cg_supported(sh, x, wpack)) return launch_conv3x3cg_bf16(sh, x, wpack, bias, y, st);
+    if (conv3x3s1_supported(sh, x, wpack))
+        return launch_conv3x3s1_bf16(sh, x, wpack, const_cast<uint16_t *>(wpack), bias, y, st, true);
+    return hipErrorInvalidValue;
+}
+
 size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w) {
     return (conv3x3cg_supported(sh, x, w) || conv3x3s1_supported(sh, x, w)) ? conv3x3s1_workspace_bytes(sh) : 0;
 }
@@ -245,6 +253,43 @@ conv_status_t conv2d_fwd_bf16_ws(const uint16_t *x, const uint16_t *w, const flo
                                  int W, int C_out, int K, int stride, int pad, int algo, void *stream) {
     return fwd_bf16(2, x, w, bias, y, N, C_in, 1, H, W, C_out, K, stride, pad, algo, stream, true,
                     workspace, workspace_bytes);
+}
+
+conv_status_t conv2d_pack_weights_bf16(const uint16_t *w, void *workspace, size_t workspace_bytes, int N,
+                                       int C_in, int H, int W, int C_out, int K, int stride, int pad,
+                                       int algo, void *stream) {
+    if (!w || !workspace) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(2, N, C_in, 1, H, W, C_out, K, stride, pad, sh);
+    if (st != CONV_OK) return st;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    if (pick_route(sh, algo) != CONV_ALGO_MFMA || (uintptr_t)w % 16) return CONV_ERR_ALGO;
+    const size_t need = convfwd::igemm_workspace_bytes(sh, (const void *)256, w);
+    if (!need) return CONV_ERR_ALGO;
+    if (workspace_bytes < need || (uintptr_t)workspace % 16) return CONV_ERR_WORKSPACE;
+    if (overlaps(workspace, (int64_t)workspace_bytes, w, sh.w_elems() * 2)) return CONV_ERR_ALIAS;
+    convfwd::launch_pack_w3x3(sh, w, (uint16_t *)workspace, (hipStream_t)stream);
+    return to_status(hipGetLastError());
+}
+
+conv_status_t conv2d_fwd_bf16_prepacked(const uint16_t *x, const void *workspace, size_t workspace_bytes,
+                                        const float *bias, float *y, int N, int C_in, int H, int W,
+                                        int C_out, int K, int stride, int pad, int algo, void *stream) {
+    if (!x || !workspace || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(2, N, C_in, 1, H, W, C_out, K, stride, pad, sh);
+    if (st != CONV_OK) return st;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    if (pick_route(sh, algo) != CONV_ALGO_MFMA) return CONV_ERR_ALGO;
+    const size_t need = convfwd::igemm_workspace_bytes(sh, x, workspace);
+    if (!need) return CONV_ERR_ALGO;
+    if (workspace_bytes < need || (uintptr_t)workspace % 16) return CONV_ERR_WORKSPACE;
+    const int64_t yb = sh.y_elems() * 4;
+    if (overlaps(y, yb, x, sh.x_elems() * 2) || overlaps(y, yb, workspace, (int64_t)workspace_bytes) ||
+        overlaps(y, yb, bias, (int64_t)sh.Co * 4))
+        return CONV_ERR_ALIAS;
+    return to_status(convfwd::launch_igemm_prepacked_bf16(sh, x, (const uint16_t *)workspace, bias, y,
+                                                          (hipStream_t)stream));
 }
 
 size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W, int K, int stride,

@@ -37,6 +37,10 @@ hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
                              size_t ws_bytes = 0);
 // Workspace bytes the MFMA route can use for this shape (0: none).
 size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w);
+// The MFMA route with weights already packed into ws by launch_pack_w3x3
+// (only for shapes where igemm_workspace_bytes() > 0).
+hipError_t launch_igemm_prepacked_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack,
+                                       const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                             const float *bias, float *y, hipStream_t st);
 // Route-specific launchers behind the two dispatchers above.
@@ -46,9 +50,10 @@ bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);
 // Workspace for the repacked weights of the 3x3 kernel (bytes).
 size_t conv3x3s1_workspace_bytes(const Shape &sh);
 // wpack: NULL (weights transposed in the kernel) or a 16-byte aligned buffer of
-// conv3x3s1_workspace_bytes() bytes that receives the repacked weights first.
+// conv3x3s1_workspace_bytes() bytes that receives the repacked weights first
+// (prepacked: it already holds them; w is then not read).
 hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
-                                 const float *bias, float *y, hipStream_t st);
+                                 const float *bias, float *y, hipStream_t st, bool prepacked = false);
 // Repack OIHW 3x3 weights (C % 16 == 0, Co % 128 == 0) into the per-stage LDS
 // images both 3x3 kernels load: Co*C*9*2 bytes at wpack.
 void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st);

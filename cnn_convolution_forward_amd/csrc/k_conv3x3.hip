@@ -618,26 +618,26 @@ size_t conv3x3s1_workspace_bytes(const Shape &sh) {
 }
 
 hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,
-                                 const float *bias, float *y, hipStream_t st) {
-    static int num_cu = 0;
-    if (num_cu == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            num_cu <= 0)
-            num_cu = 256;
+                                 const float *bias, float *y, hipStream_t st, bool prepacked) {
+    // CU count of the current device and the last plan, per host thread (the
+    // plan depends only on (N, H, W) and the CU count).
+    thread_local int cached_dev = -1, num_cu = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
+    if (dev != cached_dev) {
+        int n = 0;
+        num_cu = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                     ? n : 256;
+        cached_dev = dev;
     }
-    // The plan depends only on (N, H, W); remember the last one.
-    static int last_n = -1, last_h = -1, last_w = -1;
-    static Plan last{};
-    if (sh.N != last_n || sh.H != last_h || sh.W != last_w) {
+    thread_local int last_n = -1, last_h = -1, last_w = -1, last_cu = -1;
+    thread_local Plan last{};
+    if (sh.N != last_n || sh.H != last_h || sh.W != last_w || num_cu != last_cu) {
         last = make_plan(sh, slots_for(sh, num_cu));
-        last_n = sh.N; last_h = sh.H; last_w = sh.W;
+        last_n = sh.N; last_h = sh.H; last_w = sh.W; last_cu = num_cu;
     }
     const Plan pl = last;
-    if (wpack) {
-        launch_pack_w3x3(sh, w, wpack, st);
-    }
+    if (wpack && !prepacked) launch_pack_w3x3(sh, w, wpack, st);
     dim3 grid((unsigned)grid_size(pl, slots_for(sh, num_cu)), (unsigned)(sh.Co / kOcTile));
 #define CONV3X3_LAUNCH(RP)                                                                          \
     do {                                                                                            \

@@ -115,11 +115,12 @@ CONV_API conv_status_t conv3d_fwd_f32(const float *x, const float *w, const floa
 /* ---- with a workspace --------------------------------------------------- */
 
 /* Bytes of device workspace conv2d_fwd_bf16_ws can use for these arguments:
- * the 3x3 stride-1 pad-1 MFMA kernel (C_in % 16 == 0, C_in >= 32,
- * C_out % 128 == 0, W % 8 == 0, 8 <= W <= 64) repacks the weights once per
- * call into C_out*C_in*9*2 bytes laid out as the per-stage LDS images, so
- * that it streams them with coalesced direct-to-LDS loads instead of
- * transposing OIHW in every workgroup.  0 when no route uses a workspace. */
+ * the 3x3 stride-1 pad-1 MFMA kernels (C_in % 16 == 0, C_out % 128 == 0,
+ * W % 8 == 0, and 32 <= W <= 64, or C_in >= 32 and 8 <= W <= 64) repack the
+ * weights once per call into C_out*C_in*9*2 bytes laid out as per-stage LDS
+ * images, so that they stream them with coalesced direct-to-LDS loads
+ * instead of transposing OIHW in every workgroup.  0 when no route uses a
+ * workspace. */
 CONV_API size_t conv2d_fwd_workspace_bytes(int N, int C_in, int H, int W, int C_out,
                                            int K, int stride, int pad, int algo);
 
@@ -133,6 +134,31 @@ CONV_API conv_status_t conv2d_fwd_bf16_ws(const uint16_t *x, const uint16_t *w, 
                                           float *y, void *workspace, size_t workspace_bytes,
                                           int N, int C_in, int H, int W, int C_out,
                                           int K, int stride, int pad, int algo, void *stream);
+
+/* The two halves of conv2d_fwd_bf16_ws, for callers whose weights do not
+ * change between calls (the weight view W_row of "Why use matrix
+ * multiplication for convolution", 2.2, prepared once): */
+
+/* Writes the packed weights for these arguments into the workspace (16-byte
+ * aligned, >= conv2d_fwd_workspace_bytes() bytes) on `stream`.  w: OIHW bf16,
+ * 16-byte aligned.  Returns CONV_ERR_ALGO when no route of these arguments
+ * uses packed weights (conv2d_fwd_workspace_bytes() == 0) or w is not 16-byte
+ * aligned, CONV_ERR_WORKSPACE if the workspace is too small or misaligned,
+ * CONV_ERR_ALIAS if it overlaps w. */
+CONV_API conv_status_t conv2d_pack_weights_bf16(const uint16_t *w, void *workspace, size_t workspace_bytes,
+                                                int N, int C_in, int H, int W, int C_out,
+                                                int K, int stride, int pad, int algo, void *stream);
+
+/* conv2d_fwd_bf16 with the weights taken from a workspace that
+ * conv2d_pack_weights_bf16 filled for the same sizes and algo (the weight
+ * tensor itself is not read).  Same result as conv2d_fwd_bf16_ws.  The
+ * workspace is only read, so concurrent calls may share it.  Errors as
+ * conv2d_fwd_bf16_ws, plus CONV_ERR_ALGO when these arguments have no
+ * packed-weight route. */
+CONV_API conv_status_t conv2d_fwd_bf16_prepacked(const uint16_t *x, const void *workspace,
+                                                 size_t workspace_bytes, const float *bias, float *y,
+                                                 int N, int C_in, int H, int W, int C_out,
+                                                 int K, int stride, int pad, int algo, void *stream);
 
 /* ---- explicit im2col path ("Why use matrix multiplication for convolution",
  *      2.2 and 3.1): X_col is materialised in caller-owned device memory. ---- */

@@ -131,3 +131,26 @@ def test_workspace_entry_point_validation():
     assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS + 8, need, *args) == 6          # misaligned
     assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, Y + 64, need, *args) == 5          # overlaps y
     assert B.conv2d_fwd_bf16_ws(X, Wp, BIAS, Y, WS, need, 64, 128, 56, 56, 128, 3, 1, 1, 5, None) == 7
+
+
+def test_pack_and_prepacked_validation():
+    """Host-side checks of the pack / prepacked pair (no GPU call is reached)."""
+    need = B.conv2d_fwd_workspace_bytes(64, 128, 56, 56, 128, 3, 1, 1, 0)
+    dims = (64, 128, 56, 56, 128, 3, 1, 1)
+    assert B.conv2d_pack_weights_bf16(None, WS, need, *dims, 0, None) == 1          # NULL w
+    assert B.conv2d_pack_weights_bf16(Wp, None, need, *dims, 0, None) == 1          # NULL workspace
+    assert B.conv2d_pack_weights_bf16(Wp, WS, need, 64, 128, 56, 56, 128, 0, 1, 1, 0, None) == 2
+    assert B.conv2d_pack_weights_bf16(Wp, WS, need, *dims, 2, None) == 7            # VALU: nothing packed
+    assert B.conv2d_pack_weights_bf16(Wp, WS, need, 2, 3, 9, 11, 4, 3, 2, 1, 0, None) == 7   # no packed route
+    assert B.conv2d_pack_weights_bf16(Wp, WS, need - 2, *dims, 0, None) == 6
+    assert B.conv2d_pack_weights_bf16(Wp, WS + 8, need, *dims, 0, None) == 6        # misaligned workspace
+    assert B.conv2d_pack_weights_bf16(Wp, Wp, need, *dims, 0, None) == 5            # workspace over w
+    assert B.conv2d_pack_weights_bf16(Wp + 2, WS, need, *dims, 0, None) == 7        # misaligned w
+    assert B.conv2d_fwd_bf16_prepacked(None, WS, need, BIAS, Y, *dims, 0, None) == 1
+    assert B.conv2d_fwd_bf16_prepacked(X, None, need, BIAS, Y, *dims, 0, None) == 1
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, None, *dims, 0, None) == 1
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, Y, *dims, 7, None) == 7
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, Y, 2, 3, 9, 11, 4, 3, 2, 1, 0, None) == 7
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need - 16, BIAS, Y, *dims, 0, None) == 6
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, WS + 64, *dims, 0, None) == 5   # y over workspace
+    assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, X + 64, *dims, 0, None) == 5    # y over x

@@ -308,3 +308,29 @@ def test_small_reduction_kernel(shape, integer):
     t = synth.make_inputs(wl, seed=N * 100 + C * 10 + K, integer=integer, with_bias=(Co % 2 == 0))
     y_ref, S = reference(wl, t)
     compare(_go(wl, t, "auto"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
+
+
+# ---- packed weights reused across calls (conv2d_pack_weights_bf16 + _prepacked) ----
+
+@pytest.mark.parametrize("shape", [(2, 32, 56, 56, 128), (3, 32, 7, 64, 128), (2, 48, 12, 16, 128),
+                                   (1, 16, 9, 40, 256)], ids=lambda s: "x".join(map(str, s)))
+def test_pack_once_run_twice(shape):
+    """Weights packed once serve two different batches; each result equals the
+    oracle and, bit for bit, the one-call workspace path."""
+    N, C, H, W, Co = shape
+    wl = synth.Workload("prepacked", 2, N, C, (H, W), Co, 3, 1, 1, "bf16", "normal", 700)
+    t1 = synth.make_inputs(wl, seed=sum(shape))
+    t2 = synth.make_inputs(wl, seed=sum(shape) + 1)
+    w, b = dev(t1.w, None), dev(t1.b, np.float32)
+    ws = B.pack_weights(w, (N, C, H, W), 1, 1)
+    for t in (t1, t2):
+        x = dev(t.x, None)
+        y = poisoned(wl.y_shape)
+        B.conv_prepacked(x, ws, tuple(w.shape), b, 1, 1, out=y)
+        y_ws = poisoned(wl.y_shape)
+        B.conv(x, w, b, 1, 1, out=y_ws, workspace=B.workspace_for(x, w, 1, 1))
+        torch.cuda.synchronize()
+        tt = synth.Tensors(x=t.x, w=t1.w, b=t1.b, seed=t.seed)
+        y_ref, S = reference(wl, tt)
+        compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], label="prepacked %s" % (shape,))
+        assert torch.equal(y, y_ws)
