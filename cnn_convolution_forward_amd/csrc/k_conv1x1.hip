@@ -17,17 +17,18 @@
 //   B  [ic 32][px 128] (+16 pad) -- pixels contiguous as in NCHW; the
 //      transposing LDS read ds_read_b64_tr_b16 turns four rows of 4-pixel
 //      chunks into 4 consecutive k per pixel, two reads per fragment.
-// Epilogue: bias is the accumulators' initial value; fp32 stores go to
-// y[n][oc][q], 32 lanes on 32 consecutive pixels of one channel.
+// Epilogue: + bias[oc]; fp32 stores go to y[n][oc][q], 32 lanes on 32
+// consecutive pixels of one channel.
 //
 // The layer is bound by its output bytes (4 * C_out per pixel against 2 * C_in
-// read), so the goal is a steady store stream: small LDS footprint (38 KB) and
-// ~128 VGPRs let several workgroups share a CU, and block indices are mapped
+// read), so the goal is a steady store stream: a small LDS footprint (38 KB)
+// and at most 128 registers per lane let four workgroups share a CU (their
+// loads and stores overlap each other's K loops), and block indices are mapped
 // so that the C_out / 128 tiles of one pixel range run on the same XCD and
 // read that pixel range from its L2 once.
 //
 // Requirements (checked by the launcher): K = 1, stride 1, pad 0, C_in % 32
-// == 0, plane % 8 == 0, 16-byte aligned x and w, x and w below 2 GiB.
+// == 0, plane % 8 == 0, 16-byte aligned x and w, x, w and y below 2 GiB.
 #include "conv_internal.h"
 #include "mfma_common.h"
 
@@ -46,7 +47,7 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const float *__restrict__ bias, float *__restrict__ y,
                     int C, int Co, int plane, int64_t P, int npt, int ncb, int remap) {
@@ -103,16 +104,13 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
         }
     };
 
-    // accumulators start at bias[oc]
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int oc = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-            const float b0 = (bias && oc < Co) ? bias[oc] : 0.f;
-            acc[i][0][r] = b0;
-            acc[i][1][r] = b0;
+            acc[i][0][r] = 0.f;
+            acc[i][1][r] = 0.f;
         }
 
     // per-lane LDS coordinates of the operands
@@ -148,21 +146,30 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
         __syncthreads();
     }
 
-    // epilogue: y[n][oc][q]
+    // epilogue: y[n][oc][q] = acc + bias[oc], through buffer resources (32-bit
+    // offsets; a bias resource with no records reads 0 when there is no bias)
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)(P * Co * 4));
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bias ? (const void *)bias : (const void *)y,
+                                                bias ? (uint32_t)Co * 4 : 0u);
+    uint32_t base[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t px = j0 + wn * 64 + j * 32 + (lane & 31);
-        if (px >= P) continue;
         const int64_t n = px / plane, q = px - n * plane;
-        float *yb = y + n * Co * plane + q;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int oc = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                if (oc < Co) yb[(int64_t)oc * plane] = acc[i][j][r];
-            }
+        base[j] = (px < P) ? (uint32_t)((n * Co * plane + q) * 4) : kOob;
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int oc = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+            const float bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, oc * 4, 0, 0));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t vo = (oc < Co) ? base[j] + (uint32_t)oc * plane * 4 : kOob;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] + bv), yr, (int)vo, 0, 0);
+            }
+        }
 }
 
 }  // namespace
@@ -171,6 +178,7 @@ bool conv1x1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t plane = sh.out_plane();
     return sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
            plane < (INT64_C(1) << 31) && sh.x_elems() * 2 < (INT64_C(1) << 31) &&
+           sh.y_elems() * 4 < (INT64_C(1) << 31) &&
            sh.w_elems() * 2 < (INT64_C(1) << 31) &&
            ((uintptr_t)x % 16) == 0 && ((uintptr_t)w % 16) == 0;
 }

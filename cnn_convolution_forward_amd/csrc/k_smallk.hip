@@ -39,7 +39,10 @@ struct SmallKPlan {
     int tiles_h;     // tiles per (image, output depth)
 };
 
-__global__ __launch_bounds__(256)
+// KS: reduction steps of 16 (kpad / 16), a template parameter so the weight
+// operands take exactly 8 * KS registers.
+template <int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KS <= 4 ? 4 : KS <= 6 ? 3 : 2, 8)))
 void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                    const float *__restrict__ bias, float *__restrict__ y) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -101,20 +104,20 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     if (tid < kOcBlock) bias_s[tid] = (bias && oc0 + tid < sh.Co) ? bias[oc0 + tid] : 0.f;
     __syncthreads();
 
-    const int ksteps = pl.kpad / 16;
     const int khalf = 8 * (lane >> 5);
     // A operands: rows oc0 + ob*32 + lane%32, k = 16t + khalf .. +7
-    uint4 a[2][kMaxK / 16];
+    uint4 a[2][KS];
 #pragma unroll
     for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-        for (int s = 0; s < kMaxK / 16; ++s)
-            if (s < ksteps)
-                a[ob][s] = *reinterpret_cast<const uint4 *>(ws + (ob * 32 + (lane & 31)) * pl.kpad + 16 * s + khalf);
+        for (int s = 0; s < KS; ++s)
+            a[ob][s] = *reinterpret_cast<const uint4 *>(ws + (ob * 32 + (lane & 31)) * pl.kpad + 16 * s + khalf);
 
     const int64_t plane = sh.out_plane();
-    const int64_t q0 = ((int64_t)od * sh.Ho + oh0) * sh.Wo;
-    float *yt = y + ((int64_t)n * sh.Co + oc0) * plane + q0;
+    const uint32_t q0 = (uint32_t)(((int64_t)od * sh.Ho + oh0) * sh.Wo);
+    // this workgroup's 64 output channels of image n, 32-bit offsets
+    const int nch = min(kOcBlock, sh.Co - oc0);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + ((int64_t)n * sh.Co + oc0) * plane, (uint32_t)(nch * plane * 4));
     const int nfrag = (npx + 31) / 32;
     for (int f = wave; f < nfrag; f += 4) {
         const int p = f * 32 + (lane & 31);
@@ -125,37 +128,44 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 b4 = *reinterpret_cast<const float4 *>(bias_s + ob * 32 + 8 * g + 4 * (lane >> 5));
-                acc[ob][4 * g + 0] = b4.x; acc[ob][4 * g + 1] = b4.y;
-                acc[ob][4 * g + 2] = b4.z; acc[ob][4 * g + 3] = b4.w;
-            }
+            for (int r = 0; r < 16; ++r) acc[ob][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < kMaxK / 16; ++s) {
-            if (s < ksteps) {
-                const uint4 ko = *reinterpret_cast<const uint4 *>(koff + 16 * s + khalf);
-                const uint32_t kv[4] = {ko.x, ko.y, ko.z, ko.w};
-                uint32_t bw[4];
+        for (int s = 0; s < KS; ++s) {
+            const uint4 ko = *reinterpret_cast<const uint4 *>(koff + 16 * s + khalf);
+            const uint32_t kv[4] = {ko.x, ko.y, ko.z, ko.w};
+            uint32_t bw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = patch[base + (kv[e] & 0xffffu)];
+                const uint32_t hi = patch[base + (kv[e] >> 16)];
+                bw[e] = lo | (hi << 16);
+            }
+            const uint4 b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+            acc[0] = mfma32x32x16(a[0][s], b, acc[0]);
+            acc[1] = mfma32x32x16(a[1][s], b, acc[1]);
+        }
+        // y = acc + bias: 32 lanes on 32 consecutive pixels of one channel;
+        // pixels past the tile and channels past C_out are not stored.  The
+        // channel row offset is wave-uniform except for the lane half (4
+        // rows), so it splits into soffset + voffset; bias comes from LDS in
+        // the loop (volatile: not held in registers across fragments).
+        const int hrow = 4 * (lane >> 5);
+        const uint32_t pvo = p < npx ? (q0 + (uint32_t)p + (uint32_t)hrow * (uint32_t)plane) * 4 : kOob;
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+                const f32x4v_t b4 = *reinterpret_cast<const volatile f32x4v_t *>(bias_s + ob * 32 + 8 * g + hrow);
+                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = patch[base + (kv[e] & 0xffffu)];
-                    const uint32_t hi = patch[base + (kv[e] >> 16)];
-                    bw[e] = lo | (hi << 16);
+                    const int c = ob * 32 + 8 * g + e;             // channel without the lane-half rows
+                    const uint32_t vo = c + hrow < nch ? pvo : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ob][4 * g + e] + bb[e]), yr, (int)vo,
+                                                          (int)((uint32_t)c * (uint32_t)plane * 4), 0);
                 }
-                const uint4 b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-                acc[0] = mfma32x32x16(a[0][s], b, acc[0]);
-                acc[1] = mfma32x32x16(a[1][s], b, acc[1]);
             }
-        }
-        if (p < npx) {
-#pragma unroll
-            for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ocl = ob * 32 + mfma32_row(r, lane);
-                    if (oc0 + ocl < sh.Co) yt[(int64_t)ocl * plane + p] = acc[ob][r];
-                }
-        }
     }
 }
 
@@ -193,6 +203,7 @@ size_t smem_bytes(const SmallKPlan &pl) {
 bool smallk_supported(const Shape &sh) {
     if (sh.kgemm() > kMaxK) return false;
     if (patch_elems(sh, 1) > kPatchElems) return false;
+    if ((int64_t)kOcBlock * sh.out_plane() * 4 >= (INT64_C(1) << 31)) return false;   // one output block per buffer range
     return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);
 }
 
@@ -201,7 +212,20 @@ hipError_t launch_smallk_bf16(const Shape &sh, const uint16_t *x, const uint16_t
     const SmallKPlan pl = make_smallk_plan(sh);
     const int64_t tiles = (int64_t)sh.N * sh.Do * pl.tiles_h;
     dim3 grid((unsigned)tiles, (unsigned)((sh.Co + kOcBlock - 1) / kOcBlock));
-    hipLaunchKernelGGL(smallk_kernel, grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y);
+#define SMALLK_LAUNCH(KSV) \
+    hipLaunchKernelGGL((smallk_kernel<KSV>), grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y)
+    switch (pl.kpad / 16) {
+        case 1: SMALLK_LAUNCH(1); break;
+        case 2: SMALLK_LAUNCH(2); break;
+        case 3: SMALLK_LAUNCH(3); break;
+        case 4: SMALLK_LAUNCH(4); break;
+        case 5: SMALLK_LAUNCH(5); break;
+        case 6: SMALLK_LAUNCH(6); break;
+        case 7: SMALLK_LAUNCH(7); break;
+        case 8: SMALLK_LAUNCH(8); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef SMALLK_LAUNCH
     return hipGetLastError();
 }
 
