@@ -6,8 +6,10 @@
 // with the patch matrix X_col (same page, 2.2) never stored.  A workgroup
 // owns TR whole output rows of one (image, output depth): it copies the input
 // patch those rows read -- all C_in channels, K_d planes, (TR-1)*s + K rows and
-// (W_out-1)*s + K columns, zero outside the image ("Hand-writing Conv2D",
-// 1.2: out-of-range taps read 0) -- into LDS once, together with a table
+// the columns the taps reach, zero outside the image ("Hand-writing Conv2D",
+// 1.2: out-of-range taps read 0) -- into LDS once (for W % 8 == 0: zero fill,
+// then in-range input rows copied in 16-byte pieces to a 16-byte aligned
+// column origin), together with a table
 // koff[k] that gives, for every row k = ((ic*K_d + kd)*K + kh)*K + kw of
 // X_col, that tap's offset from a pixel's patch origin.  The X_col column of
 // output pixel (r, c) of the tile is then patch[origin(r, c) + koff[k]]: a
@@ -33,7 +35,9 @@ constexpr int kTargetPx = 512;
 
 struct SmallKPlan {
     int TR;          // output rows per tile
-    int Rt, Wt;      // patch rows and columns
+    int Rt, Wt;      // patch rows and columns (row pitch)
+    int X0;          // patch column of input column 0 (>= pad)
+    int vec;         // 1: rows are copied in 16-byte pieces (W % 8 == 0, aligned x, X0 and Wt multiples of 8)
     int E;           // patch elements: C_in*K_d*Rt*Wt input values, then Rt*Wt zeros
     int kg, kpad;    // reduction length and its multiple of 16
     int tiles_h;     // tiles per (image, output depth)
@@ -48,7 +52,7 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     extern __shared__ __align__(16) uint8_t smem[];
     float *bias_s = reinterpret_cast<float *>(smem);                                 // [64]
     uint16_t *koff = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4);              // [kpad]
-    uint16_t *ws = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4 + kMaxK * 2);    // [64][kpad]
+    uint16_t *ws = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4 + kMaxK * 2);    // [64][kg] (room for [64][kpad])
     uint16_t *patch = ws + kOcBlock * pl.kpad;                                        // [E]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -64,22 +68,41 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     const int npx = rows * sh.Wo;
     const int oc0 = blockIdx.y * kOcBlock;
 
-    // ---- stage the patch: one (channel, depth, row) line per wave iteration
+    // ---- stage the patch: line li = (channel, depth, row) holds input row
+    // (id, ih) at columns X0 + iw; everything else, and the lines after the
+    // C_in*K_d*Rt input lines (the zero region), is zero
     const int Dt = sh.Kd;
     const int64_t HW = (int64_t)sh.H * sh.W;
     const uint16_t *xn = x + (int64_t)n * sh.C * sh.D * HW;
-    // the lines after the C_in*K_d*Rt input lines form the zero region
-    const int lines = (sh.C * Dt + 1) * pl.Rt;
-    for (int li = wave; li < lines; li += 4) {
-        const int ry = li % pl.Rt, cd = li / pl.Rt;
-        const int dz = cd % Dt, c = cd / Dt;
-        const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
-        const bool row_ok = c < sh.C && id >= 0 && id < sh.D && ih >= 0 && ih < sh.H;
-        const uint16_t *src = xn + ((int64_t)c * sh.D + (row_ok ? id : 0)) * HW + (int64_t)(row_ok ? ih : 0) * sh.W;
-        uint16_t *dst = patch + (int64_t)li * pl.Wt;
-        for (int cx = lane; cx < pl.Wt; cx += 64) {
-            const int iw = cx - sh.p;
-            dst[cx] = (row_ok && iw >= 0 && iw < sh.W) ? src[iw] : (uint16_t)0;
+    if (pl.vec) {
+        for (int i = tid; i < pl.E / 8; i += 256) reinterpret_cast<uint4 *>(patch)[i] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+        const int cpr = sh.W / 8;                                   // 16-byte pieces per input row
+        const int pieces = sh.C * Dt * pl.Rt * cpr;
+        for (int i = tid; i < pieces; i += 256) {
+            const int li = i / cpr, pc = i - li * cpr;
+            const int ry = li % pl.Rt, cd = li / pl.Rt;
+            const int dz = cd % Dt, c = cd / Dt;
+            const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
+            if (id >= 0 && id < sh.D && ih >= 0 && ih < sh.H) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xn + ((int64_t)c * sh.D + id) * HW +
+                                                                   (int64_t)ih * sh.W + pc * 8);
+                *reinterpret_cast<uint4 *>(patch + li * pl.Wt + pl.X0 + pc * 8) = v;
+            }
+        }
+    } else {
+        const int lines = (sh.C * Dt + 1) * pl.Rt;
+        for (int li = wave; li < lines; li += 4) {
+            const int ry = li % pl.Rt, cd = li / pl.Rt;
+            const int dz = cd % Dt, c = cd / Dt;
+            const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
+            const bool row_ok = c < sh.C && id >= 0 && id < sh.D && ih >= 0 && ih < sh.H;
+            const uint16_t *src = xn + ((int64_t)c * sh.D + (row_ok ? id : 0)) * HW + (int64_t)(row_ok ? ih : 0) * sh.W;
+            uint16_t *dst = patch + (int64_t)li * pl.Wt;
+            for (int cx = lane; cx < pl.Wt; cx += 64) {
+                const int iw = cx - pl.X0;
+                dst[cx] = (row_ok && iw >= 0 && iw < sh.W) ? src[iw] : (uint16_t)0;
+            }
         }
     }
     // ---- tap offsets (padding rows k >= kg point at the zero region, which is
@@ -96,22 +119,43 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
         }
         koff[k] = (uint16_t)off;
     }
-    for (int i = tid; i < kOcBlock * pl.kpad; i += 256) {
-        const int r = i / pl.kpad, k = i - r * pl.kpad;
-        const int oc = oc0 + r;
-        ws[i] = (oc < sh.Co && k < pl.kg) ? w[(int64_t)oc * pl.kg + k] : (uint16_t)0;
+    // this workgroup's weight rows are one contiguous run of W_row: copy it
+    // flat (16-byte pieces when the run is 16-byte aligned, as it is for an
+    // aligned w), the fragments below index it as [oc][kg]
+    {
+        const int nch_w = min(kOcBlock, sh.Co - oc0);
+        const int nel = nch_w * pl.kg;
+        const uint16_t *wsrc = w + (int64_t)oc0 * pl.kg;
+        int done = 0;
+        if (((uintptr_t)wsrc % 16) == 0) {
+            for (int i = tid; i < nel / 8; i += 256)
+                reinterpret_cast<uint4 *>(ws)[i] = reinterpret_cast<const uint4 *>(wsrc)[i];
+            done = nel / 8 * 8;
+        }
+        for (int i = done + tid; i < nel; i += 256) ws[i] = wsrc[i];
     }
     if (tid < kOcBlock) bias_s[tid] = (bias && oc0 + tid < sh.Co) ? bias[oc0 + tid] : 0.f;
     __syncthreads();
 
     const int khalf = 8 * (lane >> 5);
-    // A operands: rows oc0 + ob*32 + lane%32, k = 16t + khalf .. +7
+    // A operands: rows oc0 + ob*32 + lane%32, k = 16t + khalf .. +7, zero
+    // past C_out and past kg
+    const int nch_a = min(kOcBlock, sh.Co - oc0);
     uint4 a[2][KS];
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob)
+    for (int ob = 0; ob < 2; ++ob) {
+        const int ocl = ob * 32 + (lane & 31);
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            a[ob][s] = *reinterpret_cast<const uint4 *>(ws + (ob * 32 + (lane & 31)) * pl.kpad + 16 * s + khalf);
+        for (int s = 0; s < KS; ++s) {
+            uint16_t e8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = 16 * s + khalf + e;
+                e8[e] = (ocl < nch_a && k < pl.kg) ? ws[ocl * pl.kg + k] : (uint16_t)0;
+            }
+            a[ob][s] = pack8(e8);
+        }
+    }
 
     const int64_t plane = sh.out_plane();
     const uint32_t q0 = (uint32_t)(((int64_t)od * sh.Ho + oh0) * sh.Wo);
@@ -123,7 +167,7 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
         const int p = f * 32 + (lane & 31);
         const int pc = p < npx ? p : npx - 1;
         const int orow = pc / sh.Wo, ocol = pc - orow * sh.Wo;
-        const int base = orow * sh.s * pl.Wt + ocol * sh.s;
+        const int base = orow * sh.s * pl.Wt + ocol * sh.s - sh.p + pl.X0;
         f32x16_t acc[2];
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
@@ -169,27 +213,46 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     }
 }
 
-int64_t patch_elems(const Shape &sh, int TR) {
+// Patch geometry for TR output rows: row pitch Wt and origin X0 (vec: both
+// multiples of 8 and the whole input row fits, so rows copy in 16-byte pieces).
+void patch_geom(const Shape &sh, bool vec, int &X0, int &Wt) {
+    const int need = (sh.Wo - 1) * sh.s - sh.p + sh.K;          // columns iw < need are read
+    if (vec) {
+        X0 = (sh.p + 7) / 8 * 8;
+        Wt = (X0 + (need > sh.W ? need : sh.W) + 7) / 8 * 8;
+    } else {
+        X0 = sh.p;
+        Wt = X0 + need;
+    }
+}
+
+int64_t patch_elems(const Shape &sh, int TR, bool vec) {
+    int X0, Wt;
+    patch_geom(sh, vec, X0, Wt);
     const int64_t Rt = (int64_t)(TR - 1) * sh.s + sh.K;
-    const int64_t Wt = (int64_t)(sh.Wo - 1) * sh.s + sh.K;
     return ((int64_t)sh.C * sh.Kd + 1) * Rt * Wt;
 }
 
-SmallKPlan make_smallk_plan(const Shape &sh) {
+bool vec_ok(const Shape &sh, const void *x) {
+    return sh.W % 8 == 0 && ((uintptr_t)x % 16) == 0 && sh.p <= 8;
+}
+
+SmallKPlan make_smallk_plan(const Shape &sh, bool vec) {
     SmallKPlan pl{};
     pl.kg = (int)sh.kgemm();
     pl.kpad = (pl.kg + 15) / 16 * 16;
+    pl.vec = vec ? 1 : 0;
     int TR = kTargetPx / sh.Wo;
     if (TR < 1) TR = 1;
     if (TR > sh.Ho) TR = sh.Ho;
-    while (TR > 1 && patch_elems(sh, TR) > kPatchElems) --TR;
+    while (TR > 1 && patch_elems(sh, TR, vec) > kPatchElems) --TR;
     // even out the row tiles of a plane
     const int tiles = (sh.Ho + TR - 1) / TR;
     TR = (sh.Ho + tiles - 1) / tiles;
     pl.TR = TR;
     pl.Rt = (TR - 1) * sh.s + sh.K;
-    pl.Wt = (sh.Wo - 1) * sh.s + sh.K;
-    pl.E = (int)patch_elems(sh, TR);
+    patch_geom(sh, vec, pl.X0, pl.Wt);
+    pl.E = (int)patch_elems(sh, TR, vec);
     pl.tiles_h = tiles;
     return pl;
 }
@@ -202,14 +265,15 @@ size_t smem_bytes(const SmallKPlan &pl) {
 
 bool smallk_supported(const Shape &sh) {
     if (sh.kgemm() > kMaxK) return false;
-    if (patch_elems(sh, 1) > kPatchElems) return false;
+    if (patch_elems(sh, 1, false) > kPatchElems) return false;
     if ((int64_t)kOcBlock * sh.out_plane() * 4 >= (INT64_C(1) << 31)) return false;   // one output block per buffer range
     return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);
 }
 
 hipError_t launch_smallk_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
                               float *y, hipStream_t st) {
-    const SmallKPlan pl = make_smallk_plan(sh);
+    const bool vec = vec_ok(sh, x) && patch_elems(sh, 1, true) <= kPatchElems;
+    const SmallKPlan pl = make_smallk_plan(sh, vec);
     const int64_t tiles = (int64_t)sh.N * sh.Do * pl.tiles_h;
     dim3 grid((unsigned)tiles, (unsigned)((sh.Co + kOcBlock - 1) / kOcBlock));
 #define SMALLK_LAUNCH(KSV) \

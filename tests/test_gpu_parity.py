@@ -297,6 +297,9 @@ SMALL_K = [
     (3, 1, 3, (6, 10, 12), 20, 3, 1, 1),
     (3, 2, 4, (5, 7, 9), 64, 3, 2, 1),     # 108 reduction rows, strided 3D
     (3, 1, 3, (16, 64, 64), 64, 3, 1, 1),  # the 3D workload's layer at N = 1
+    (2, 1, 2, (30, 32), 64, 7, 2, 3),      # W % 8 == 0: rows staged in 16-byte pieces, pad 3, K = 7
+    (2, 2, 3, (17, 40), 96, 5, 1, 2),      # 16-byte staging, pad 2, ragged rows and channel block
+    (3, 2, 4, (5, 8, 16), 64, 3, 2, 1),    # 3D, 16-byte staging, stride 2
 ]
 
 
