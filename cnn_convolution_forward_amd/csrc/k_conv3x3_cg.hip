@@ -22,19 +22,20 @@
 // Tiling: a workgroup computes 64 output channels x 8 output rows x W (one
 // tile per workgroup), four waves in a 2 x 2 grid: 32 channels x J = D/2
 // fragments each (J accumulator tiles, <= 128 accumulator registers).  Two
-// workgroups share a CU (<= 256 registers per lane, ~66 KB of LDS each), so
+// workgroups share a CU (<= 256 registers per lane, <= 80 KB of LDS each), so
 // one workgroup's prologue, barriers, epilogue and output drain overlap the
 // other's MFMA work.  The K loop runs over 16-channel stages:
 //   weights  [tap 9][oc 64][ic 16], 18 KB per stage, double-buffered, copied
 //            by direct-to-LDS loads from the packed workspace
 //            (launch_pack_w3x3, 128-channel blocks; a workgroup copies the
 //            64-row half of each tap's block);
-//   input    [row 10][col RP][ic 16] at 48 bytes per pixel and an odd row
-//            pitch RP >= W + 2, so the 8 rows of a fragment column hit 8
-//            distinct 16-byte bank groups; single-buffered: the next stage is
-//            loaded into registers during the MFMAs and written transposed
-//            (NCHW keeps channels strided, the operand needs 8 consecutive)
-//            between two barriers.
+//   input    [row 10][col RP][ic 16] at 32 bytes per pixel, an odd row pitch
+//            RP >= W + 2 and the two 16-byte halves swapped on bit 2 of the
+//            row, so the 8 rows of a fragment column hit 8 distinct 16-byte
+//            bank groups; double-buffered: the next stage is loaded into
+//            registers at the start of a stage and written transposed (NCHW
+//            keeps channels strided, the operand needs 8 consecutive) into
+//            the other buffer halfway through its MFMAs; one barrier a stage.
 // Accumulator orientation D[px][oc]: lane l owns channel l % 32, and its 16
 // slots are pixels (rows 4*(l/32) .. +3) x (4 column groups); across its J
 // fragments a lane holds J consecutive columns of each (row, group).  The
@@ -57,12 +58,18 @@ constexpr int kPackOcBlock = 128;        // channel block of the packed weight l
 constexpr int kIc = 16;                  // input channels per stage
 constexpr int kRows = 8;                 // output rows per tile
 constexpr int kInRows = kRows + 2;       // input rows per tile (halo)
-constexpr int kPix = 48;                 // LDS bytes per input pixel: 16 bf16 + 16 pad
+constexpr int kPix = 32;                 // LDS bytes per input pixel: 16 bf16, halves swizzled by row
 constexpr int kTapBytes = kOc * 32;      // one tap's weights in LDS (2 KB)
 constexpr int kWStage = 9 * kTapBytes;   // 18432 bytes of weights per stage
 constexpr int kPackStage = 9 * kPackOcBlock * 32;   // 36864: one stage of a packed 128-channel block
 constexpr int kEpiOc = 16;               // channels per epilogue pass
 constexpr int kEpiBytes = kEpiOc * (kRows * 64 + 4) * 4;   // largest pass image (W = 64)
+
+// 16-byte half of an input pixel that holds channels 8h .. 8h+7 in LDS
+// input row rho: the halves swap on bit 2 of the row, so the 8 rows of a
+// fragment column (32-byte pixels, odd row pitch) hit 8 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int in_half(int h, int rho) { return h ^ ((rho >> 2) & 1); }
 
 template <int D>
 struct Geo {
@@ -70,7 +77,7 @@ struct Geo {
     static constexpr int J = D / 2;                       // fragments per pixel-wave
     static constexpr int RP = (W + 2) | 1;                // odd input row pitch (pixels)
     static constexpr int IN_BYTES = kInRows * RP * kPix;
-    static constexpr int LDS = 2 * kWStage + IN_BYTES > kEpiBytes ? 2 * kWStage + IN_BYTES : kEpiBytes;
+    static constexpr int LDS = 2 * kWStage + 2 * IN_BYTES;
     static constexpr int UNITS = 2 * kInRows * (W / 8);   // input load units per stage
 };
 
@@ -109,15 +116,16 @@ __device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[Geo<D>::J], const uint4 
 // LDS (8 of 64 lanes).  A step first issues the LDS reads of column q + 1,
 // then the 9 (or fewer) MFMAs of column q, so the reads have a column of
 // MFMA work to arrive.
-template <int D, int q>
+template <int D, int q, class Mid>
 __device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], uint4 (&B0)[2],
-                                       uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, bool row7) {
+                                       uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, const uint8_t *tb,
+                                       bool row7, Mid &&mid) {
     constexpr int J = Geo<D>::J, RP = Geo<D>::RP, Q = J + 2;
     if constexpr (q + 1 < Q) {
         B0[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (q + 1) * kPix);
         if (row7) {
-            T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (RP + q + 1) * kPix);
-            T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (2 * RP + q + 1) * kPix);
+            T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (RP + q + 1) * kPix);
+            T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (2 * RP + q + 1) * kPix);
         }
     }
     const uint4 b0 = B0[q & 1];
@@ -126,7 +134,8 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (
     cg_mfma<D, 1>(acc, A, b1, q);
     const uint4 b2 = pick(row7, T2[q & 1], rows_down(b1));
     cg_mfma<D, 2>(acc, A, b2, q);
-    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, row7);
+    if constexpr (q == Q / 2) mid();
+    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, tb, row7, mid);
 }
 
 template <int D>
@@ -138,6 +147,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     constexpr int W = G::W, J = G::J, RP = G::RP;
     __shared__ __align__(16) uint8_t smem[G::LDS];
     static_assert(G::LDS >= kEpiBytes, "the epilogue image overlays the stage buffers");
+    static_assert(G::LDS <= 80 * 1024, "two workgroups per CU");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,17 +181,17 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     const int ih = r0 - 1 + rho;
     const uint32_t ivoff = (in_active && ih >= 0 && ih < H)
                                ? (uint32_t)((g8 * 8 * HW + ih * W + pg * 8) * 2) : kOob;
-    const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + 1) * kPix + g8 * 16);
+    const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + 1) * kPix + in_half(g8, rho) * 16);
     const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = chan_bytes * kIc;
     uint4 xin[8];
     auto load_x = [&](int s) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xin[e] = bload16(xr, ivoff, (uint32_t)s * stage_bytes + e * chan_bytes);
     };
-    auto store_x = [&]() {
+    auto store_x = [&](int buf) {
         if (!in_active) return;
         const uint32_t *v = reinterpret_cast<const uint32_t *>(xin);   // v[e*4 + j/2]: channel e, pixels j, j+1
-        uint8_t *dst = ibuf + idst;
+        uint8_t *dst = ibuf + buf * G::IN_BYTES + idst;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int dj = j >> 1, hj = j & 1;
@@ -213,11 +223,14 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     // is b_base + (rr*RP + q) * 48
     const uint32_t a_off = (uint32_t)((wm * 32 + l32) * 32 + ((h ^ wswz(l32)) * 16));
     const int c0 = wn * J;
-    const uint32_t b_base = (uint32_t)((((l32 & 7) * RP) + D * (l32 >> 3) + c0) * kPix + h * 16);
+    const uint32_t b_base = (uint32_t)((((l32 & 7) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                       in_half(h, l32 & 7) * 16);
     const bool row7 = (l32 & 7) == 7;        // lanes that read the new row of kernel rows 1 and 2
+    // their rows 8 and 9 keep the unswapped halves
+    const uint32_t t_base = (uint32_t)(((7 * RP) + D * (l32 >> 3) + c0) * kPix + in_half(h, 8) * 16);
 
-    // zero the input buffer: halo columns are never written again
-    for (int i = tid; i < G::IN_BYTES / 16; i += kThreads)
+    // zero both input buffers: halo columns are never written again
+    for (int i = tid; i < 2 * G::IN_BYTES / 16; i += kThreads)
         reinterpret_cast<uint4 *>(ibuf)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
@@ -226,7 +239,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     load_x(0);
     const float bv = bias ? bias[ocb + wm * 32 + l32] : 0.f;
     CONV3X3_WAIT_VMCNT(0);
-    store_x();
+    store_x(0);
     __syncthreads();
 
     // accumulators start at this lane's channel bias
@@ -244,22 +257,27 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
             load_x(s + 1);
         }
         const uint8_t *wb = wbuf + b * kWStage + a_off;
-        const uint8_t *ib = ibuf + b_base;
+        const uint8_t *ib = ibuf + b * G::IN_BYTES + b_base;
+        const uint8_t *tb = ibuf + b * G::IN_BYTES + t_base;
         uint4 A[9], B0[2], T1[2], T2[2];
 #pragma unroll
         for (int t = 0; t < 9; ++t) A[t] = *reinterpret_cast<const uint4 *>(wb + t * kTapBytes);
         B0[0] = *reinterpret_cast<const uint4 *>(ib);
         if (row7) {
-            T1[0] = *reinterpret_cast<const uint4 *>(ib + RP * kPix);
-            T2[0] = *reinterpret_cast<const uint4 *>(ib + 2 * RP * kPix);
+            T1[0] = *reinterpret_cast<const uint4 *>(tb + RP * kPix);
+            T2[0] = *reinterpret_cast<const uint4 *>(tb + 2 * RP * kPix);
         }
-        cg_col<D, 0>(acc, A, B0, T1, T2, ib, row7);
-        CONV3X3_WAIT_VMCNT(0);      // weights of the next stage in LDS, its input in registers
-        __syncthreads();            // every wave is done with the input buffer
-        if (more) {
-            store_x();
-            __syncthreads();        // next stage's input and weights visible
-        }
+        // halfway through the stage the next stage's input (loaded at its
+        // start) goes into the other buffer, which nobody reads this stage
+        auto mid = [&]() {
+            if (more) {
+                CONV3X3_WAIT_VMCNT(0);
+                store_x(b ^ 1);
+            }
+        };
+        cg_col<D, 0>(acc, A, B0, T1, T2, ib, tb, row7, mid);
+        CONV3X3_WAIT_VMCNT(0);      // next stage's weights in LDS
+        __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
     // ---- epilogue: 4 passes of 16 channels through LDS, then whole rows out.
