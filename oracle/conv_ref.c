@@ -27,7 +27,9 @@
  * Besides y, each convolution returns S = sum over the same taps of |x * w|
  * (bias excluded), the scale against which a low-precision result is judged.
  *
- * Parity pins live in tests/test_oracle_pins.py; every function here is pinned.
+ * Parity pins live in tests/test_oracle_pins.py (plain convolution) and
+ * tests/test_oracle_pins_general.py (dilation and groups); every function here
+ * is pinned.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -250,6 +252,176 @@ void oracle_matmul(const double *A, const double *B, double *Cm,
             for (int64_t k = 0; k < Kk; ++k) acc += A[i * Kk + k] * B[k * Nn + j];
             Cm[i * Nn + j] = acc;
         }
+}
+
+/* ---- dilation and groups ----------------------------------------------------
+ *
+ *   [PyTorch tensor products and conv2d/conv3d dimension semantics, 4.2]
+ *        with dilation d the taps of one window sit d apart, so a window spans
+ *        d(K-1)+1 input positions and out = floor((in + 2p - d(K-1) - 1)/s) + 1
+ *        (also [Conv2d from the official docs, 3.2 and 3.3]).
+ *   [PyTorch tensor products and conv2d/conv3d dimension semantics, 4.3]
+ *        groups g: C_in and C_out are each cut into g equal consecutive blocks;
+ *        output block i reads input block i only; the weight's second extent is
+ *        C_in/g; g = C_in is the depthwise case ([Conv2d from the official
+ *        docs, 3.4] gives the same rule).
+ *   The depth dimension of a 3D problem takes the same K, s, p and d
+ *   ([PyTorch tensor products and conv2d/conv3d dimension semantics, 5.2]).
+ */
+
+/* Output length with dilation d; -1 when a parameter is out of range or the
+ * dilated window never fits. */
+int64_t oracle_out_dim_dilated(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+{
+    if (in < 1 || k < 1 || s < 1 || p < 0 || d < 1) return -1;
+    int64_t span = d * (k - 1) + 1;
+    int64_t room = in + 2 * p - span;
+    if (room < 0) return -1;
+    return room / s + 1;
+}
+
+/* Geometry of one general problem; 2D is carried with Dd = 1 and a depth
+ * kernel of one tap. */
+typedef struct {
+    int64_t N, C, Dd, H, W, Co, G;
+    int64_t Kz, K;          /* depth taps (1 in 2D), in-plane taps */
+    int64_t s, p, d;        /* in-plane stride, pad, dilation      */
+    int64_t sz, pz, dz;     /* depth stride, pad, dilation         */
+    int64_t Do, Ho, Wo;
+} gen_geom;
+
+static int gen_geom_make(gen_geom *g, int ndim, int64_t N, int64_t C, int64_t D, int64_t H,
+                         int64_t W, int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d,
+                         int64_t G)
+{
+    if (ndim != 2 && ndim != 3) return -1;
+    if (N < 1 || C < 1 || Co < 1 || G < 1 || C % G != 0 || Co % G != 0) return -1;
+    g->N = N; g->C = C; g->H = H; g->W = W; g->Co = Co; g->G = G;
+    g->K = K; g->s = s; g->p = p; g->d = d;
+    if (ndim == 3) {
+        g->Dd = D; g->Kz = K; g->sz = s; g->pz = p; g->dz = d;
+        g->Do = oracle_out_dim_dilated(D, K, s, p, d);
+    } else {
+        g->Dd = 1; g->Kz = 1; g->sz = 1; g->pz = 0; g->dz = 1;
+        g->Do = 1;
+    }
+    g->Ho = oracle_out_dim_dilated(H, K, s, p, d);
+    g->Wo = oracle_out_dim_dilated(W, K, s, p, d);
+    if (g->Do < 0 || g->Ho < 0 || g->Wo < 0) return -1;
+    return 0;
+}
+
+/* One output element: output channel oc belongs to group oc / (Co/G) and sums
+ * over the C/G input channels of that group, the weight holding C/G input
+ * channels per filter.  Tap (kz, kh, kw) reads input (od*sz + kz*dz - pz,
+ * oh*s + kh*d - p, ow*s + kw*d - p); outside the input it adds nothing. */
+static void gen_one(const gen_geom *g, const double *x, const double *w, int64_t n, int64_t oc,
+                    int64_t od, int64_t oh, int64_t ow, double *acc_out, double *S_out)
+{
+    const int64_t Cg = g->C / g->G, Cog = g->Co / g->G;
+    const int64_t grp = oc / Cog;
+    double acc = 0.0, S = 0.0;
+    for (int64_t j = 0; j < Cg; ++j) {
+        const int64_t ic = grp * Cg + j;
+        for (int64_t kz = 0; kz < g->Kz; ++kz) {
+            const int64_t iz = od * g->sz + kz * g->dz - g->pz;
+            if (iz < 0 || iz >= g->Dd) continue;
+            for (int64_t kh = 0; kh < g->K; ++kh) {
+                const int64_t iy = oh * g->s + kh * g->d - g->p;
+                if (iy < 0 || iy >= g->H) continue;
+                for (int64_t kw = 0; kw < g->K; ++kw) {
+                    const int64_t ix = ow * g->s + kw * g->d - g->p;
+                    if (ix < 0 || ix >= g->W) continue;
+                    const double xv = x[(((n * g->C + ic) * g->Dd + iz) * g->H + iy) * g->W + ix];
+                    const double wv = w[(((oc * Cg + j) * g->Kz + kz) * g->K + kh) * g->K + kw];
+                    const double prod = xv * wv;
+                    acc += prod;
+                    S += fabs(prod);
+                }
+            }
+        }
+    }
+    *acc_out = acc;
+    *S_out = S;
+}
+
+/* Full 2D or 3D convolution with dilation d and groups G.  x: (N, C, [D,] H, W),
+ * w: (Co, C/G, K, K[, K]), y and S: (N, Co, [Do,] Ho, Wo).  bias and S may be
+ * NULL.  Returns 0, or -1 on a bad shape. */
+int oracle_conv_general(int ndim, const double *x, const double *w, const double *bias,
+                        double *y, double *S,
+                        int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                        int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, Co, K, s, p, d, G) != 0) return -1;
+    const int64_t plane = g.Do * g.Ho * g.Wo;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t oc = 0; oc < Co; ++oc)
+            for (int64_t q = 0; q < plane; ++q) {
+                const int64_t ow = q % g.Wo, oh = (q / g.Wo) % g.Ho, od = q / (g.Wo * g.Ho);
+                double acc, sa;
+                gen_one(&g, x, w, n, oc, od, oh, ow, &acc, &sa);
+                const int64_t o = (n * Co + oc) * plane + q;
+                y[o] = acc + (bias ? bias[oc] : 0.0);
+                if (S) S[o] = sa;
+            }
+    return 0;
+}
+
+/* The same at the flat output indices idx[0..npts) only. */
+int oracle_conv_general_points(int ndim, const double *x, const double *w, const double *bias,
+                               const int64_t *idx, int64_t npts, double *y, double *S,
+                               int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                               int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, Co, K, s, p, d, G) != 0) return -1;
+    const int64_t plane = g.Do * g.Ho * g.Wo, total = N * Co * plane;
+    for (int64_t i = 0; i < npts; ++i)
+        if (idx[i] < 0 || idx[i] >= total) return -1;
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t q = idx[i] % plane, oc = (idx[i] / plane) % Co, n = idx[i] / (plane * Co);
+        const int64_t ow = q % g.Wo, oh = (q / g.Wo) % g.Ho, od = q / (g.Wo * g.Ho);
+        double acc, sa;
+        gen_one(&g, x, w, n, oc, od, oh, ow, &acc, &sa);
+        y[i] = acc + (bias ? bias[oc] : 0.0);
+        if (S) S[i] = sa;
+    }
+    return 0;
+}
+
+/* Explicit im2col with dilation, 2D or 3D [Why use matrix multiplication for
+ * convolution, 2.2 and 3.1, with the dilated tap offsets above].  col has
+ * C*K^ndim rows, row ((ic*Kz + kz)*K + kh)*K + kw, and N*Do*Ho*Wo columns in
+ * output order; an out-of-range tap is 0.  Groups do not change X_col: group i
+ * multiplies its own block of C/G * K^ndim consecutive rows. */
+int oracle_im2col_dilated(int ndim, const double *x, double *col,
+                          int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                          int64_t K, int64_t s, int64_t p, int64_t d)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, 1, K, s, p, d, 1) != 0) return -1;
+    const int64_t plane = g.Do * g.Ho * g.Wo, cols = N * plane;
+    for (int64_t ic = 0; ic < C; ++ic)
+      for (int64_t kz = 0; kz < g.Kz; ++kz)
+        for (int64_t kh = 0; kh < K; ++kh)
+          for (int64_t kw = 0; kw < K; ++kw) {
+            const int64_t r = ((ic * g.Kz + kz) * K + kh) * K + kw;
+            for (int64_t n = 0; n < N; ++n)
+              for (int64_t q = 0; q < plane; ++q) {
+                const int64_t ow = q % g.Wo, oh = (q / g.Wo) % g.Ho, od = q / (g.Wo * g.Ho);
+                const int64_t iz = od * g.sz + kz * g.dz - g.pz;
+                const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw * d - p;
+                double v = 0.0;
+                if (0 <= iz && iz < g.Dd && 0 <= iy && iy < H && 0 <= ix && ix < W)
+                    v = x[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix];
+                col[r * cols + n * plane + q] = v;
+              }
+          }
+    return 0;
 }
 
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */

@@ -67,6 +67,15 @@ def lib():
         L.oracle_im2col3d.restype = ctypes.c_int
         L.oracle_im2col3d.argtypes = [_dp, _dp] + [_i64] * 8
         L.oracle_matmul.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64]
+        L.oracle_out_dim_dilated.restype = _i64
+        L.oracle_out_dim_dilated.argtypes = [_i64] * 5
+        L.oracle_conv_general.restype = ctypes.c_int
+        L.oracle_conv_general.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp] + [_i64] * 11
+        L.oracle_conv_general_points.restype = ctypes.c_int
+        L.oracle_conv_general_points.argtypes = [ctypes.c_int, _dp, _dp, _dp, ctypes.c_void_p, _i64,
+                                                 _dp, _dp] + [_i64] * 11
+        L.oracle_im2col_dilated.restype = ctypes.c_int
+        L.oracle_im2col_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -201,6 +210,88 @@ def matmul(A, B):
     Cm = np.empty((M, Nn), np.float64)
     lib().oracle_matmul(_p(A), _p(B), _p(Cm), M, Kk, Nn)
     return Cm
+
+
+def out_dim_dilated(n: int, k: int, s: int, p: int, d: int) -> int:
+    """floor((n + 2p - d(k-1) - 1)/s) + 1, or -1 if the dilated window never fits
+    [PyTorch tensor products and conv2d/conv3d dimension semantics, 4.2]."""
+    return int(lib().oracle_out_dim_dilated(n, k, s, p, d))
+
+
+def _general_dims(x, w, groups):
+    ndim = x.ndim - 2
+    if ndim == 2:
+        N, C, H, W = x.shape
+        D = 1
+        ks = w.shape[2:]
+    elif ndim == 3:
+        N, C, D, H, W = x.shape
+        ks = w.shape[2:]
+    else:
+        raise ValueError("x must be NCHW or NCDHW")
+    Co, Cg = w.shape[0], w.shape[1]
+    if len(ks) != ndim or len(set(ks)) != 1:
+        raise ValueError("weight shape %s is not a square/cubic kernel" % (w.shape,))
+    if groups < 1 or C % groups or Co % groups or Cg * groups != C:
+        raise ValueError("groups=%d does not fit C_in=%d, C_out=%d, weight %s" % (groups, C, Co, w.shape))
+    return ndim, N, C, D, H, W, Co, ks[0]
+
+
+def conv_general(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, with_S=True):
+    """y (and S) of a 2D or 3D convolution with dilation and groups, fp64.
+    w: (C_out, C_in/groups, K, K[, K])
+    [PyTorch tensor products and conv2d/conv3d dimension semantics, 4.2-4.3, 5.2]."""
+    x, w = decode(x), decode(w)
+    b = None if bias is None else decode(bias)
+    ndim, N, C, D, H, W, Co, K = _general_dims(x, w, groups)
+    if b is not None and b.shape != (Co,):
+        raise ValueError("bias must have shape (C_out,)")
+    sizes = [out_dim_dilated(n, K, stride, pad, dilation) for n in ((D, H, W) if ndim == 3 else (H, W))]
+    if min(sizes) < 0:
+        raise ValueError("dilated kernel larger than padded input")
+    y = np.empty((N, Co) + tuple(sizes), np.float64)
+    S = np.empty_like(y) if with_S else None
+    rc = lib().oracle_conv_general(ndim, _p(x), _p(w), _p(b), _p(y), _p(S),
+                                   N, C, D, H, W, Co, K, stride, pad, dilation, groups)
+    if rc != 0:
+        raise ValueError("oracle_conv_general rejected the shape")
+    return (y, S) if with_S else y
+
+
+def conv_general_points(x, w, bias, stride, pad, dilation, groups, idx):
+    """y and S of conv_general at the flat output indices ``idx`` only."""
+    x, w = decode(x), decode(w)
+    b = None if bias is None else decode(bias)
+    ndim, N, C, D, H, W, Co, K = _general_dims(x, w, groups)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    y = np.empty(idx.shape, np.float64)
+    S = np.empty(idx.shape, np.float64)
+    rc = lib().oracle_conv_general_points(ndim, _p(x), _p(w), _p(b), idx.ctypes.data, idx.size,
+                                          _p(y), _p(S), N, C, D, H, W, Co, K, stride, pad,
+                                          dilation, groups)
+    if rc != 0:
+        raise ValueError("oracle_conv_general_points rejected the request")
+    return y, S
+
+
+def im2col_dilated(x, K, stride, pad, dilation):
+    """X_col (C*K^ndim, N*out_plane) with dilated taps, 2D or 3D by x.ndim."""
+    x = decode(x)
+    ndim = x.ndim - 2
+    if ndim == 2:
+        N, C, H, W = x.shape
+        D = 1
+        dims = (H, W)
+    else:
+        N, C, D, H, W = x.shape
+        dims = (D, H, W)
+    sizes = [out_dim_dilated(n, K, stride, pad, dilation) for n in dims]
+    if min(sizes) < 0:
+        raise ValueError("bad im2col shape")
+    col = np.empty((C * K ** ndim, N * int(np.prod(sizes))), np.float64)
+    if lib().oracle_im2col_dilated(ndim, _p(x), _p(col), N, C, D, H, W, K, stride, pad, dilation) != 0:
+        raise ValueError("bad im2col shape")
+    return col
 
 
 def num_threads() -> int:

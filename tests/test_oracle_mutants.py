@@ -3,8 +3,11 @@
 Each case edits one line of a temporary copy of oracle/conv_ref.c (a plausible
 slip: sign of the padding offset, kh/kw swapped, bias dropped, X_col columns
 transposed, a depth offset lost, |x*w| replaced by x*w, ceil for floor, an
-off-by-one bounds check), builds it with gcc, and runs tests/test_oracle_pins.py
-against that build in a subprocess.  The run must fail.  Runs on the CPU only.
+off-by-one bounds check; in the dilation/groups functions: dilation dropped
+from an axis, groups interleaved, the group's channel offset lost, the dilated
+span mis-sized), builds it with gcc, and runs the matching pin file
+(tests/test_oracle_pins.py or tests/test_oracle_pins_general.py) against that
+build in a subprocess.  The run must fail.  Runs on the CPU only.
 """
 import os
 import subprocess
@@ -32,10 +35,27 @@ MUTANTS = {
                          "int64_t iw = ow + kw - p;\n                    if (!(0 <= iw"),
 }
 
+# Mistakes in the dilation / groups functions, caught by test_oracle_pins_general.py.
+MUTANTS_GENERAL = {
+    "dilation_dropped_h": ("const int64_t iy = oh * g->s + kh * g->d - g->p;",
+                           "const int64_t iy = oh * g->s + kh - g->p;"),
+    "depth_dilation_dropped": ("const int64_t iz = od * g->sz + kz * g->dz - g->pz;",
+                               "const int64_t iz = od * g->sz + kz - g->pz;"),
+    "groups_interleaved": ("const int64_t grp = oc / Cog;", "const int64_t grp = oc % g->G;"),
+    "group_offset_dropped": ("const int64_t ic = grp * Cg + j;", "const int64_t ic = j + 0 * grp;"),
+    "dilated_span_wrong": ("int64_t span = d * (k - 1) + 1;", "int64_t span = d * k - d + 1 + (d > 1);"),
+    "im2col_dilation_dropped_w": ("const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw * d - p;",
+                                  "const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw - p;"),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_planted_mistake_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
+
+CASES = [(n, "test_oracle_pins.py") for n in sorted(MUTANTS)] + \
+        [(n, "test_oracle_pins_general.py") for n in sorted(MUTANTS_GENERAL)]
+
+
+@pytest.mark.parametrize("name,pins", CASES)
+def test_planted_mistake_is_caught(name, pins, tmp_path):
+    old, new = {**MUTANTS, **MUTANTS_GENERAL}[name]
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not found once: %s" % name
     mutant_c = tmp_path / "conv_ref_mutant.c"
@@ -45,6 +65,6 @@ def test_planted_mistake_is_caught(name, tmp_path):
                            "-o", str(so), str(mutant_c), "-lm"])
     env = dict(os.environ, CONV_ORACLE_LIB_OVERRIDE=str(so), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "planted mistake %r passed every pin:\n%s" % (name, r.stdout[-2000:])
