@@ -22,11 +22,12 @@ One JSON line on stdout:
                current kernel sources, else null
   cpu_baseline the CPU oracle (plain fp64 loops, OpenMP) timed on the same
                inputs on this host (the whole batch unless told otherwise)
---report prints one more line per workload to stderr (all five, every route).
+--report prints one more line per workload to stderr (every workload, every route).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -103,11 +104,17 @@ class Runner:
         self.y = torch.empty(wl.y_shape, dtype=torch.float32, device="cuda")
         self.ws = None
         self.packed = None
-        if route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16":
+        # dilation / groups go through the general entry points (conv_params_t)
+        self.params = None if wl.plain else B.make_params(wl.x_shape, wl.w_shape, wl.stride, wl.pad,
+                                                          wl.dilation, wl.groups)
+        if route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16" and wl.plain:
             self.packed = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
         if route == "explicit":
-            nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
-                                         wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
+            if self.params is not None:
+                nbytes = B.conv_xcol_bytes(self.params)
+            else:
+                nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
+                                             wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.B = B
         self._bind()
@@ -126,7 +133,14 @@ class Runner:
         algo = B.ALGO.get(self.route, 0)
         x, w, b, y = ptr(self.x), ptr(self.w), ptr(self.b), ptr(self.y)
         self._pre = None
-        if self.route == "explicit":
+        if self.params is not None:
+            prm = ctypes.byref(self.params)
+            if self.route == "explicit":
+                self._main = (L.conv_fwd_explicit_bf16, (prm, x, w, b, y, ptr(self.ws), self.ws.numel(), st))
+            else:
+                fn = L.conv_fwd_f32 if wl.dtype == "f32" else L.conv_fwd_bf16
+                self._main = (fn, (prm, x, w, b, y, algo, st))
+        elif self.route == "explicit":
             nb = self.ws.numel()
             if wl.ndim == 2:
                 self._main = (L.conv2d_fwd_bf16_explicit,
@@ -237,9 +251,12 @@ def cpu_baseline(wl, runner, sample_images):
     t = runner.t
     n = sample_images
     xs = t.x[:n]
-    f = oracle.conv2d if wl.ndim == 2 else oracle.conv3d
     t0 = time.perf_counter()
-    y_ref, S = f(xs, t.w, t.b, wl.stride, wl.pad)
+    if wl.plain:
+        f = oracle.conv2d if wl.ndim == 2 else oracle.conv3d
+        y_ref, S = f(xs, t.w, t.b, wl.stride, wl.pad)
+    else:
+        y_ref, S = oracle.conv_general(xs, t.w, t.b, wl.stride, wl.pad, wl.dilation, wl.groups)
     dt = time.perf_counter() - t0
     flops = wl.flops() * n / wl.N
     y_gpu = runner.y[:n].cpu().numpy().astype(np.float64)
@@ -256,8 +273,9 @@ def cpu_baseline(wl, runner, sample_images):
 
 
 def describe(wl):
+    extra = {} if wl.plain else {"dilation": wl.dilation, "groups": wl.groups}
     return {"workload": wl.name, "x": list(wl.x_shape), "w": list(wl.w_shape), "y": list(wl.y_shape),
-            "stride": wl.stride, "pad": wl.pad, "in_dtype": wl.dtype, "out_dtype": "f32",
+            "stride": wl.stride, "pad": wl.pad, **extra, "in_dtype": wl.dtype, "out_dtype": "f32",
             "seed": wl.seed, "flop_per_step": wl.flops(), "algorithmic_bytes_per_step": algorithmic_bytes(wl)}
 
 
@@ -269,7 +287,7 @@ def measure(wl, route, steps, warmup):
 
 def report_all(steps, warmup):
     from cnn_convolution_forward_amd import synth
-    for name, wl in synth.WORKLOADS.items():
+    for name, wl in synth.ALL_WORKLOADS.items():
         routes = ["valu"] if wl.dtype == "f32" else ["auto", "mfma", "valu", "explicit"]
         for route in routes:
             _, wall, gpu, per = measure(wl, route, steps, warmup)
@@ -304,7 +322,7 @@ def main():
         return
     from cnn_convolution_forward_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.ALL_WORKLOADS[args.workload]
     print("bench: %s route=%s steps=%d warmup=%d" % (wl.name, args.route, args.steps, args.warmup),
           file=sys.stderr, flush=True)
     runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup)
@@ -324,7 +342,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
         "gpu_ms_per_step": round(gpu / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded PCG64; x N(0,1), w N(0,1/sqrt(fan_in)), b U[-1,1]; bf16 by RNE)",
+        "data": "synthetic (seeded PCG64; x %s, w %s, b U[-1,1]%s)" % (
+            "N(0,1)" if wl.x_dist == "normal" else "U[-1,1]",
+            "U[-1,1]" if wl.dtype == "f32" else "N(0,1/sqrt(fan_in))",
+            "; bf16 by RNE" if wl.dtype == "bf16" else ""),
         "config": describe(wl) | {"route": args.route},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,

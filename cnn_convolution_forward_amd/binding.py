@@ -28,7 +28,15 @@ EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv2d_fwd_workspace_bytes", "conv2d_fwd_bf16_ws",
            "conv2d_pack_weights_bf16", "conv2d_fwd_bf16_prepacked",
            "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
-           "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit")
+           "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit",
+           "conv_out_dim_dilated", "conv_fwd_bf16", "conv_fwd_f32", "conv_xcol_bytes",
+           "conv_im2col_bf16", "conv_fwd_explicit_bf16")
+
+
+class ConvParams(ctypes.Structure):
+    """conv_params_t: a general problem (dilation and groups)."""
+    _fields_ = [(n, ctypes.c_int) for n in ("ndim", "N", "C_in", "D", "H", "W", "C_out", "K", "stride",
+                                             "pad", "dilation", "groups")]
 
 
 class ConvError(RuntimeError):
@@ -79,6 +87,18 @@ def lib():
         L.conv2d_fwd_bf16_explicit.argtypes = [_vp] * 5 + [_sz] + [_i] * 8 + [_vp]
         L.conv3d_fwd_bf16_explicit.restype = _i
         L.conv3d_fwd_bf16_explicit.argtypes = [_vp] * 5 + [_sz] + [_i] * 9 + [_vp]
+        _pp = ctypes.POINTER(ConvParams)
+        L.conv_out_dim_dilated.restype = _i64
+        L.conv_out_dim_dilated.argtypes = [_i64] * 5
+        for name in ("conv_fwd_bf16", "conv_fwd_f32"):
+            getattr(L, name).restype = _i
+            getattr(L, name).argtypes = [_pp, _vp, _vp, _vp, _vp, _i, _vp]
+        L.conv_xcol_bytes.restype = _sz
+        L.conv_xcol_bytes.argtypes = [_pp]
+        L.conv_im2col_bf16.restype = _i
+        L.conv_im2col_bf16.argtypes = [_pp, _vp, _vp, _vp]
+        L.conv_fwd_explicit_bf16.restype = _i
+        L.conv_fwd_explicit_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -159,6 +179,44 @@ def conv3d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, D, H, W, C_ou
                              stream=None):
     return lib().conv3d_fwd_bf16_explicit(x, w, bias, y, ws, ws_bytes, N, C_in, D, H, W, C_out, K,
                                           stride, pad, stream)
+
+
+def _pref(params):
+    return None if params is None else ctypes.byref(params)
+
+
+def conv_out_dim_dilated(n, k, stride, pad, dilation):
+    return int(lib().conv_out_dim_dilated(n, k, stride, pad, dilation))
+
+
+def conv_fwd_bf16(params, x, w, bias, y, algo=0, stream=None):
+    return lib().conv_fwd_bf16(_pref(params), x, w, bias, y, algo, stream)
+
+
+def conv_fwd_f32(params, x, w, bias, y, algo=0, stream=None):
+    return lib().conv_fwd_f32(_pref(params), x, w, bias, y, algo, stream)
+
+
+def conv_xcol_bytes(params):
+    return int(lib().conv_xcol_bytes(_pref(params)))
+
+
+def conv_im2col_bf16(params, x, xcol, stream=None):
+    return lib().conv_im2col_bf16(_pref(params), x, xcol, stream)
+
+
+def conv_fwd_explicit_bf16(params, x, w, bias, y, ws, ws_bytes, stream=None):
+    return lib().conv_fwd_explicit_bf16(_pref(params), x, w, bias, y, ws, ws_bytes, stream)
+
+
+def make_params(x_shape, w_shape, stride=1, pad=0, dilation=1, groups=1):
+    """ConvParams from NC(D)HW input and OI(D)HW weight shapes."""
+    ndim = len(x_shape) - 2
+    if ndim not in (2, 3) or len(w_shape) != ndim + 2:
+        raise ValueError("expected 4-D or 5-D x and a weight of the same rank")
+    sp = list(x_shape[2:])
+    return ConvParams(ndim, x_shape[0], x_shape[1], sp[0] if ndim == 3 else 1, sp[-2], sp[-1], w_shape[0],
+                      w_shape[2], stride, pad, dilation, groups)
 
 
 # ---- torch-tensor helpers (device memory + stream plumbing only) --------------
@@ -349,4 +407,88 @@ def conv_explicit(x, w, bias=None, stride=1, pad=0, workspace=None, out=None):
                                       D, sp[1], sp[2], w.shape[0], K, stride, pad, _stream())
     if st != CONV_OK:
         raise ConvError(st, "conv%dd_fwd_bf16_explicit" % ndim)
+    return y
+
+
+def _general_out_shape(x, w, stride, pad, dilation):
+    K = w.shape[2]
+    outs = [conv_out_dim_dilated(d, K, stride, pad, dilation) for d in x.shape[2:]]
+    return (x.shape[0], w.shape[0], *outs)
+
+
+def _general_check(x, w, groups, half_ok=True):
+    torch = _torch()
+    ndim = x.dim() - 2
+    if ndim not in (2, 3) or w.dim() != x.dim():
+        raise ValueError("x must be 4-D or 5-D and w of the same rank")
+    if any(k != w.shape[2] for k in w.shape[2:]):
+        raise ValueError("only square/cubic kernels are supported")
+    if groups < 1 or x.shape[1] % groups or w.shape[0] % groups or w.shape[1] * groups != x.shape[1]:
+        raise ValueError("w.shape[1]=%d * groups=%d must equal C_in=%d and groups must divide C_out=%d"
+                         % (w.shape[1], groups, x.shape[1], w.shape[0]))
+    _ = torch
+    return ndim
+
+
+def conv_general(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, algo="auto", out=None):
+    """y = conv(x, w) + bias with dilation and groups (conv_fwd_bf16 /
+    conv_fwd_f32).  w: (C_out, C_in/groups, K, K[, K]).  Returns float32 y."""
+    torch = _torch()
+    _general_check(x, w, groups)
+    f32 = x.dtype == torch.float32
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_tensor(x, "x", (torch.float32,) if f32 else half)
+    _check_tensor(w, "w", (torch.float32,) if f32 else half)
+    _check_tensor(bias, "bias", (torch.float32,))
+    shape = _general_out_shape(x, w, stride, pad, dilation)
+    if min(shape[2:]) < 1:
+        raise ConvError(3, "conv_general")
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check_tensor(y, "out", (torch.float32,))
+    prm = make_params(tuple(x.shape), tuple(w.shape), stride, pad, dilation, groups)
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    fn = conv_fwd_f32 if f32 else conv_fwd_bf16
+    st = fn(prm, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), a, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_fwd_f32" if f32 else "conv_fwd_bf16")
+    return y
+
+
+def im2col_general(x, K, stride=1, pad=0, dilation=1, out=None):
+    """X_col with dilated taps (conv_im2col_bf16) as int16 bf16 bit patterns."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    ndim = x.dim() - 2
+    prm = make_params(tuple(x.shape), (1, x.shape[1]) + (K,) * ndim, stride, pad, dilation, 1)
+    nbytes = conv_xcol_bytes(prm)
+    if nbytes == 0:
+        raise ConvError(2, "conv_xcol_bytes")
+    rows = x.shape[1] * K ** ndim
+    col = out if out is not None else torch.empty((rows, nbytes // 2 // rows), dtype=torch.int16,
+                                                  device=x.device)
+    st = conv_im2col_bf16(prm, _ptr(x), _ptr(col), _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_im2col_bf16")
+    return col
+
+
+def conv_explicit_general(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, workspace=None, out=None):
+    """conv_fwd_explicit_bf16: dilated im2col into a workspace, then one GEMM per group."""
+    torch = _torch()
+    _general_check(x, w, groups)
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_tensor(x, "x", half)
+    _check_tensor(w, "w", half)
+    _check_tensor(bias, "bias", (torch.float32,))
+    prm = make_params(tuple(x.shape), tuple(w.shape), stride, pad, dilation, groups)
+    nbytes = conv_xcol_bytes(prm)
+    if nbytes == 0:
+        raise ConvError(2, "conv_xcol_bytes")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    shape = _general_out_shape(x, w, stride, pad, dilation)
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    st = conv_fwd_explicit_bf16(prm, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_fwd_explicit_bf16")
     return y

@@ -24,6 +24,14 @@ int64_t out_dim(int64_t in, int64_t K, int64_t s, int64_t p) {
     return num / s + 1;
 }
 
+// With dilation d the window spans d(K-1)+1 inputs:
+// floor((in + 2p - d(K-1) - 1)/s) + 1 ("PyTorch tensor products and
+// conv2d/conv3d dimension semantics", 4.2).  K, d < 2^31, so the span fits.
+int64_t out_dim_dil(int64_t in, int64_t K, int64_t s, int64_t p, int64_t d) {
+    if (in < 1 || K < 1 || s < 1 || p < 0 || d < 1 || K > INT32_MAX || d > INT32_MAX) return -1;
+    return out_dim(in, d * (K - 1) + 1, s, p);
+}
+
 bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
     uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -32,11 +40,12 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
 
 // Fill `sh` from the arguments.  Returns CONV_OK or the first violated rule.
 conv_status_t make_shape(int ndim, int N, int C, int D, int H, int W, int Co,
-                         int K, int s, int p, Shape &sh) {
-    if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1 || Co < 1 || K < 1 || s < 1 || p < 0)
+                         int K, int s, int p, Shape &sh, int dil = 1, int G = 1) {
+    if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1 || Co < 1 || K < 1 || s < 1 || p < 0 ||
+        dil < 1 || G < 1 || C % G != 0 || Co % G != 0)
         return CONV_ERR_PARAM;
-    int64_t Ho = out_dim(H, K, s, p), Wo = out_dim(W, K, s, p);
-    int64_t Do = ndim == 3 ? out_dim(D, K, s, p) : 1;
+    int64_t Ho = out_dim_dil(H, K, s, p, dil), Wo = out_dim_dil(W, K, s, p, dil);
+    int64_t Do = ndim == 3 ? out_dim_dil(D, K, s, p, dil) : 1;
     if (Ho < 1 || Wo < 1 || Do < 1) return CONV_ERR_SHAPE;
     sh.ndim = ndim;
     sh.N = N; sh.C = C; sh.D = D; sh.H = H; sh.W = W; sh.Co = Co;
@@ -44,6 +53,9 @@ conv_status_t make_shape(int ndim, int N, int C, int D, int H, int W, int Co,
     sh.Kd = ndim == 3 ? K : 1;
     sh.sd = ndim == 3 ? s : 1;
     sh.pd = ndim == 3 ? p : 0;
+    sh.dil = dil;
+    sh.dild = ndim == 3 ? dil : 1;
+    sh.G = G;
     sh.Do = (int)Do; sh.Ho = (int)Ho; sh.Wo = (int)Wo;
     // Element counts in int64: each factor is < 2^31, so each pairwise product
     // fits; stop as soon as a running product passes the limit.
@@ -51,7 +63,7 @@ conv_status_t make_shape(int ndim, int N, int C, int D, int H, int W, int Co,
     if (taps > kMaxElems / K) return CONV_ERR_OVERFLOW;
     taps *= K;
     const int64_t fx[] = {N, C, D, H, W};
-    const int64_t fw[] = {Co, C, taps};
+    const int64_t fw[] = {Co, C / G, taps};
     const int64_t fy[] = {N, Co, Do, Ho, Wo};
     int64_t acc = 1;
     for (int64_t f : fx) { if (acc > kMaxElems / f) return CONV_ERR_OVERFLOW; acc *= f; }
@@ -81,19 +93,24 @@ conv_status_t to_status(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_
 // that goes to the direct VALU kernel.
 constexpr int64_t kValuMaxK = 32;
 
+// One input channel per group (the depthwise layer) has no channel reduction
+// for the matrix cores: VALU as well.
 int pick_route(const Shape &sh, int algo) {
     if (algo != CONV_ALGO_AUTO) return algo;
     if (convfwd::smallk_supported(sh)) return CONV_ALGO_MFMA;
+    if (convfwd::depthwise_supported(sh)) return CONV_ALGO_VALU;
     return sh.kgemm() <= kValuMaxK ? CONV_ALGO_VALU : CONV_ALGO_MFMA;
 }
 
-conv_status_t fwd_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
-                       int N, int C, int D, int H, int W, int Co, int K, int s, int p,
-                       int algo, void *stream, bool with_ws, void *ws, size_t ws_bytes) {
-    if (!x || !w || !y) return CONV_ERR_NULL;
-    Shape sh;
-    conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
-    if (st != CONV_OK) return st;
+conv_status_t shape_from_params(const conv_params_t *prm, Shape &sh) {
+    if (prm->ndim != 2 && prm->ndim != 3) return CONV_ERR_PARAM;
+    return make_shape(prm->ndim, prm->N, prm->C_in, prm->ndim == 3 ? prm->D : 1, prm->H, prm->W,
+                      prm->C_out, prm->K, prm->stride, prm->pad, sh, prm->dilation, prm->groups);
+}
+
+conv_status_t fwd_bf16_sh(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                          float *y, int algo, void *stream, bool with_ws, void *ws, size_t ws_bytes) {
+    conv_status_t st;
     if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
     const int route = pick_route(sh, algo);
     if (with_ws) {
@@ -107,6 +124,26 @@ conv_status_t fwd_bf16(int ndim, const uint16_t *x, const uint16_t *w, const flo
     return to_status(convfwd::launch_igemm_bf16(sh, x, w, bias, y, hs, ws, ws_bytes));
 }
 
+conv_status_t fwd_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                       int N, int C, int D, int H, int W, int Co, int K, int s, int p,
+                       int algo, void *stream, bool with_ws, void *ws, size_t ws_bytes) {
+    if (!x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
+    if (st != CONV_OK) return st;
+    return fwd_bf16_sh(sh, x, w, bias, y, algo, stream, with_ws, ws, ws_bytes);
+}
+
+conv_status_t fwd_f32_sh(const Shape &sh, const float *x, const float *w, const float *bias, float *y,
+                         int algo, void *stream) {
+    conv_status_t st;
+    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    if ((st = check_alias(sh, 4, x, w, bias, y, nullptr, 0)) != CONV_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (convfwd::depthwise_supported(sh)) return to_status(convfwd::launch_depthwise_f32(sh, x, w, bias, y, hs));
+    return to_status(convfwd::launch_valu_f32(sh, x, w, bias, y, hs));
+}
+
 conv_status_t fwd_f32(int ndim, const float *x, const float *w, const float *bias, float *y,
                       int N, int C, int D, int H, int W, int Co, int K, int s, int p,
                       int algo, void *stream) {
@@ -114,9 +151,13 @@ conv_status_t fwd_f32(int ndim, const float *x, const float *w, const float *bia
     Shape sh;
     conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
     if (st != CONV_OK) return st;
-    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_VALU) return CONV_ERR_ALGO;
-    if ((st = check_alias(sh, 4, x, w, bias, y, nullptr, 0)) != CONV_OK) return st;
-    return to_status(convfwd::launch_valu_f32(sh, x, w, bias, y, (hipStream_t)stream));
+    return fwd_f32_sh(sh, x, w, bias, y, algo, stream);
+}
+
+conv_status_t im2col_bf16_sh(const Shape &sh, const uint16_t *x, uint16_t *xcol, void *stream) {
+    if (sh.xcol_rows() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
+    if (overlaps(xcol, sh.xcol_elems() * 2, x, sh.x_elems() * 2)) return CONV_ERR_ALIAS;
+    return to_status(convfwd::launch_im2col_bf16(sh, x, xcol, (hipStream_t)stream));
 }
 
 conv_status_t im2col_bf16(int ndim, const uint16_t *x, uint16_t *xcol, int N, int C, int D, int H,
@@ -125,9 +166,20 @@ conv_status_t im2col_bf16(int ndim, const uint16_t *x, uint16_t *xcol, int N, in
     Shape sh;
     conv_status_t st = make_shape(ndim, N, C, D, H, W, 1, K, s, p, sh);
     if (st != CONV_OK) return st;
-    if (sh.kgemm() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
-    if (overlaps(xcol, sh.xcol_elems() * 2, x, sh.x_elems() * 2)) return CONV_ERR_ALIAS;
-    return to_status(convfwd::launch_im2col_bf16(sh, x, xcol, (hipStream_t)stream));
+    return im2col_bf16_sh(sh, x, xcol, stream);
+}
+
+conv_status_t explicit_bf16_sh(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                               float *y, void *ws, size_t ws_bytes, void *stream) {
+    conv_status_t st;
+    if (sh.xcol_rows() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
+    if ((uint64_t)ws_bytes < (uint64_t)sh.xcol_elems() * 2) return CONV_ERR_WORKSPACE;
+    if ((st = check_alias(sh, 2, x, w, bias, y, ws, ws_bytes)) != CONV_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    uint16_t *xcol = (uint16_t *)ws;
+    hipError_t e = convfwd::launch_im2col_bf16(sh, x, xcol, hs);
+    if (e != hipSuccess) return CONV_ERR_HIP;
+    return to_status(convfwd::launch_gemm_xcol_bf16(sh, w, xcol, bias, y, hs));
 }
 
 conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, const float *bias,
@@ -137,14 +189,7 @@ conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, cons
     Shape sh;
     conv_status_t st = make_shape(ndim, N, C, D, H, W, Co, K, s, p, sh);
     if (st != CONV_OK) return st;
-    if (sh.kgemm() > kMaxElems / sh.pixels()) return CONV_ERR_OVERFLOW;
-    if ((uint64_t)ws_bytes < (uint64_t)sh.xcol_elems() * 2) return CONV_ERR_WORKSPACE;
-    if ((st = check_alias(sh, 2, x, w, bias, y, ws, ws_bytes)) != CONV_OK) return st;
-    hipStream_t hs = (hipStream_t)stream;
-    uint16_t *xcol = (uint16_t *)ws;
-    hipError_t e = convfwd::launch_im2col_bf16(sh, x, xcol, hs);
-    if (e != hipSuccess) return CONV_ERR_HIP;
-    return to_status(convfwd::launch_gemm_xcol_bf16(sh, w, xcol, bias, y, hs));
+    return explicit_bf16_sh(sh, x, w, bias, y, ws, ws_bytes, stream);
 }
 
 }  // namespace
@@ -182,9 +227,11 @@ size_t igemm_workspace_bytes(const Shape &sh, const void *x, const void *w) {
     return (conv3x3cg_supported(sh, x, w) || conv3x3s1_supported(sh, x, w)) ? conv3x3s1_workspace_bytes(sh) : 0;
 }
 
-// VALU route for bf16 inputs.
+// VALU route for bf16 inputs: the depthwise kernel for one input channel per
+// group, else the general direct kernel.
 hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                             const float *bias, float *y, hipStream_t st) {
+    if (depthwise_supported(sh)) return launch_depthwise_bf16(sh, x, w, bias, y, st);
     return launch_valu_generic_bf16(sh, x, w, bias, y, st);
 }
 
@@ -200,7 +247,7 @@ const char *conv_status_str(int status) {
     switch (status) {
         case CONV_OK: return "ok";
         case CONV_ERR_NULL: return "a required pointer is NULL";
-        case CONV_ERR_PARAM: return "a size, kernel or stride < 1, or pad < 0";
+        case CONV_ERR_PARAM: return "a size, kernel, stride or dilation < 1, pad < 0, or groups not dividing the channels";
         case CONV_ERR_SHAPE: return "kernel larger than the padded input (no output position)";
         case CONV_ERR_OVERFLOW: return "a tensor would hold 2^31 or more elements";
         case CONV_ERR_ALIAS: return "output overlaps an input or the workspace";
@@ -298,7 +345,7 @@ size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W, int K, 
     Shape sh;
     if (make_shape(ndim, N, C_in, ndim == 3 ? D : 1, H, W, 1, K, stride, pad, sh) != CONV_OK)
         return 0;
-    if (sh.kgemm() > kMaxElems / sh.pixels()) return 0;
+    if (sh.xcol_rows() > kMaxElems / sh.pixels()) return 0;
     return (size_t)sh.xcol_elems() * 2;
 }
 
@@ -326,6 +373,56 @@ conv_status_t conv3d_fwd_bf16_explicit(const uint16_t *x, const uint16_t *w, con
                                        int stride, int pad, void *stream) {
     return explicit_bf16(3, x, w, bias, y, workspace, workspace_bytes, N, C_in, D, H, W, C_out,
                          K, stride, pad, stream);
+}
+
+// ---- general problems: dilation and groups ----
+
+int64_t conv_out_dim_dilated(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t dilation) {
+    return out_dim_dil(in, K, stride, pad, dilation);
+}
+
+conv_status_t conv_fwd_bf16(const conv_params_t *prm, const uint16_t *x, const uint16_t *w,
+                            const float *bias, float *y, int algo, void *stream) {
+    if (!prm || !x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    return fwd_bf16_sh(sh, x, w, bias, y, algo, stream, false, nullptr, 0);
+}
+
+conv_status_t conv_fwd_f32(const conv_params_t *prm, const float *x, const float *w, const float *bias,
+                           float *y, int algo, void *stream) {
+    if (!prm || !x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    return fwd_f32_sh(sh, x, w, bias, y, algo, stream);
+}
+
+size_t conv_xcol_bytes(const conv_params_t *prm) {
+    if (!prm) return 0;
+    Shape sh;
+    if (shape_from_params(prm, sh) != CONV_OK) return 0;
+    if (sh.xcol_rows() > kMaxElems / sh.pixels()) return 0;
+    return (size_t)sh.xcol_elems() * 2;
+}
+
+conv_status_t conv_im2col_bf16(const conv_params_t *prm, const uint16_t *x, uint16_t *xcol, void *stream) {
+    if (!prm || !x || !xcol) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    return im2col_bf16_sh(sh, x, xcol, stream);
+}
+
+conv_status_t conv_fwd_explicit_bf16(const conv_params_t *prm, const uint16_t *x, const uint16_t *w,
+                                     const float *bias, float *y, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    if (!prm || !x || !w || !y || !workspace) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    return explicit_bf16_sh(sh, x, w, bias, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -8,7 +8,10 @@
 namespace convfwd {
 
 // One convolution problem.  2D problems are carried as 3D with D = Do = 1,
-// Kd = 1, pad_d = 0, stride_d = 1, so every kernel indexes (d, h, w).
+// Kd = 1, pad_d = 0, stride_d = 1, dil_d = 1, so every kernel indexes (d, h, w).
+// Tap (kd, kh, kw) of output (od, oh, ow) reads input
+// (od*sd + kd*dild - pd, oh*s + kh*dil - p, ow*s + kw*dil - p); output channel
+// oc belongs to group oc / (Co/G) and reads the C/G input channels of that group.
 struct Shape {
     int ndim;               // 2 or 3
     int N, C, D, H, W;      // input  N x C x D x H x W
@@ -16,16 +19,22 @@ struct Shape {
     int K, s, p;            // square/cubic kernel, one stride, one symmetric pad
     int Kd, sd, pd;         // depth kernel/stride/pad: (K, s, p) in 3D, (1, 1, 0) in 2D
     int Do, Ho, Wo;         // output spatial extents (Do = 1 in 2D)
+    int dil = 1, dild = 1;  // dilation in H/W and in depth (dild = 1 in 2D)
+    int G = 1;              // groups: divides C and Co
 
+    __host__ __device__ int Cg() const { return C / G; }                                // input channels per group
+    __host__ __device__ int Cog() const { return Co / G; }                              // output channels per group
+    __host__ __device__ bool plain() const { return dil == 1 && G == 1; }
     __host__ __device__ int64_t taps() const { return (int64_t)Kd * K * K; }            // K^ndim
-    __host__ __device__ int64_t kgemm() const { return (int64_t)C * taps(); }          // C_in * K^ndim
+    __host__ __device__ int64_t kgemm() const { return (int64_t)Cg() * taps(); }       // reduction per group
+    __host__ __device__ int64_t xcol_rows() const { return (int64_t)C * taps(); }      // rows of X_col
     __host__ __device__ int64_t in_plane() const { return (int64_t)D * H * W; }
     __host__ __device__ int64_t out_plane() const { return (int64_t)Do * Ho * Wo; }
     __host__ __device__ int64_t pixels() const { return (int64_t)N * out_plane(); }    // GEMM N dimension
     __host__ __device__ int64_t x_elems() const { return (int64_t)N * C * in_plane(); }
     __host__ __device__ int64_t w_elems() const { return (int64_t)Co * kgemm(); }
     __host__ __device__ int64_t y_elems() const { return (int64_t)Co * pixels(); }
-    __host__ __device__ int64_t xcol_elems() const { return kgemm() * pixels(); }
+    __host__ __device__ int64_t xcol_elems() const { return xcol_rows() * pixels(); }
 };
 
 // Kernel launchers.  Each enqueues on `st` and returns hipGetLastError().
@@ -73,5 +82,11 @@ hipError_t launch_valu_generic_bf16(const Shape &sh, const uint16_t *x, const ui
                                     const float *bias, float *y, hipStream_t st);
 hipError_t launch_valu_f32(const Shape &sh, const float *x, const float *w,
                            const float *bias, float *y, hipStream_t st);
+// Depthwise-style kernel for one input channel per group (C/G == 1), 2D.
+bool depthwise_supported(const Shape &sh);
+hipError_t launch_depthwise_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                                 float *y, hipStream_t st);
+hipError_t launch_depthwise_f32(const Shape &sh, const float *x, const float *w, const float *bias,
+                                float *y, hipStream_t st);
 
 }  // namespace convfwd

@@ -176,7 +176,7 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
 
 bool conv1x1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t plane = sh.out_plane();
-    return sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
+    return sh.plain() && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
            plane < (INT64_C(1) << 31) && sh.x_elems() * 2 < (INT64_C(1) << 31) &&
            sh.y_elems() * 4 < (INT64_C(1) << 31) &&
            sh.w_elems() * 2 < (INT64_C(1) << 31) &&

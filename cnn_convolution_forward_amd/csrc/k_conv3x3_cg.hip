@@ -329,7 +329,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
     (void)w;
     const int64_t HW = (int64_t)sh.H * sh.W;
-    return sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
+    return sh.plain() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
            sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
            (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range

@@ -11,7 +11,10 @@
 //
 // GEMM view: M = C_out (rows of W_row), N = N*Do*Ho*Wo output pixels, K =
 // C_in*K^dims in the natural OIHW order r = ((ic*Kd + kd)*K + kh)*K + kw, so a
-// row of W_row is contiguous in memory.  Block tile BM x 128 pixels x 32 k,
+// row of W_row is contiguous in memory.  With groups G the problem is G
+// independent GEMMs of C_out/G x (C_in/G * K^dims) each, one per blockIdx.z
+// ("PyTorch tensor products and conv2d/conv3d dimension semantics", 4.3); with
+// dilation d the taps of the gather sit d inputs apart (same page, 4.2).  Block tile BM x 128 pixels x 32 k,
 // four waves in a 2 x 2 grid, v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 // The epilogue adds bias[oc] and stores fp32 straight into N C_out (D) H W
 // order: the reshape + axis swap of "Why use matrix multiplication for
@@ -32,15 +35,19 @@ template <int BM, bool kExplicit>
 __global__ __launch_bounds__(256)
 void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint16_t *__restrict__ w,
                           const float *__restrict__ bias, float *__restrict__ y,
-                          int64_t P, int Kg, int w_vec) {
+                          int64_t P, int Kg, int w_vec, int g0) {
     constexpr int MI = BM / 64;               // 32-row MFMA tiles per wave (wave covers BM/2 rows)
     __shared__ __align__(16) uint16_t As[2][BM][kLdk];
     __shared__ __align__(16) uint16_t Bs[2][kBN][kLdk];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM;
+    const int m0 = blockIdx.y * BM;               // first row of the tile inside its group
     const int64_t j0 = (int64_t)blockIdx.x * kBN;
+    const int grp = g0 + (int)blockIdx.z;
+    const int Cog = sh.Co / sh.G, Cg = sh.C / sh.G;
+    const int oc_base = grp * Cog;                  // first output channel of the group
+    const uint16_t *wg = w + (int64_t)oc_base * Kg;
 
     // ---- B loader: this thread owns pixel bpx of the tile and k-quads bkq, bkq+2.
     const int bpx = tid & (kBN - 1);
@@ -54,7 +61,7 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
         int ow = (int)(t % sh.Wo); t /= sh.Wo;
         int oh = (int)(t % sh.Ho); t /= sh.Ho;
         int od = (int)(t % sh.Do); t /= sh.Do;
-        xn = src + t * sh.C * sh.in_plane();
+        xn = src + (t * sh.C + (int64_t)grp * Cg) * sh.in_plane();
         id0 = od * sh.sd - sh.pd;
         ih0 = oh * sh.s - sh.p;
         iw0 = ow * sh.s - sh.p;
@@ -73,13 +80,13 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
             int u = tid + 256 * i;
             int row = u >> 2, kq = u & 3;
             int oc = m0 + row, k = k0 + kq * 8;
-            if (w_vec && oc < sh.Co && k < Kg) {
-                a_reg[i] = *reinterpret_cast<const uint4 *>(w + (int64_t)oc * Kg + k);
+            if (w_vec && oc < Cog && k < Kg) {
+                a_reg[i] = *reinterpret_cast<const uint4 *>(wg + (int64_t)oc * Kg + k);
             } else {
                 uint16_t v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    v[e] = (oc < sh.Co && k + e < Kg) ? w[(int64_t)oc * Kg + k + e] : (uint16_t)0;
+                    v[e] = (oc < Cog && k + e < Kg) ? wg[(int64_t)oc * Kg + k + e] : (uint16_t)0;
                 a_reg[i] = pack8(v);
             }
         }
@@ -92,7 +99,7 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
             if (kExplicit) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    v[e] = (pvalid && k + e < Kg) ? src[(int64_t)(k + e) * P + jp] : (uint16_t)0;
+                    v[e] = (pvalid && k + e < Kg) ? src[((int64_t)grp * Kg + k + e) * P + jp] : (uint16_t)0;
             } else {
                 int ic = k / taps, rem = k - ic * taps;
                 int kd = rem / KK; rem -= kd * KK;
@@ -100,8 +107,8 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     uint16_t val = 0;
-                    if (pvalid && ic < sh.C) {
-                        int id = id0 + kd, ih = ih0 + kh, iw = iw0 + kw;
+                    if (pvalid && ic < Cg) {
+                        int id = id0 + kd * sh.dild, ih = ih0 + kh * sh.dil, iw = iw0 + kw * sh.dil;
                         if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W)
                             val = xn[((int64_t)ic * sh.D + id) * HW + (int64_t)ih * sh.W + iw];
                     }
@@ -169,8 +176,9 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int oc = m0 + wm * (BM / 2) + i * 32 + mfma32_row(r, lane);
-                if (oc < sh.Co) yb[(int64_t)oc * plane] = acc[i][j][r] + (bias ? bias[oc] : 0.f);
+                const int ocl = m0 + wm * (BM / 2) + i * 32 + mfma32_row(r, lane);
+                const int oc = oc_base + ocl;
+                if (ocl < Cog) yb[(int64_t)oc * plane] = acc[i][j][r] + (bias ? bias[oc] : 0.f);
             }
     }
 }
@@ -182,16 +190,24 @@ hipError_t launch_generic(const Shape &sh, const uint16_t *src, const uint16_t *
     const int Kg = (int)sh.kgemm();
     const int w_vec = (Kg % 8 == 0) && ((uintptr_t)w % 16 == 0);
     const unsigned gx = (unsigned)((P + kBN - 1) / kBN);
-    if (sh.Co > 64) {
-        dim3 grid(gx, (unsigned)((sh.Co + 127) / 128));
-        hipLaunchKernelGGL((igemm_generic_kernel<128, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
-                           bias, y, P, Kg, w_vec);
-    } else {
-        dim3 grid(gx, (unsigned)((sh.Co + 63) / 64));
-        hipLaunchKernelGGL((igemm_generic_kernel<64, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
-                           bias, y, P, Kg, w_vec);
+    const int Cog = sh.Co / sh.G;
+    constexpr int kMaxGridZ = 65535;
+    // groups beyond the grid's z limit go in further launches (g0 = first group)
+    for (int g0 = 0; g0 < sh.G; g0 += kMaxGridZ) {
+        const unsigned gz = (unsigned)(sh.G - g0 < kMaxGridZ ? sh.G - g0 : kMaxGridZ);
+        if (Cog > 64) {
+            dim3 grid(gx, (unsigned)((Cog + 127) / 128), gz);
+            hipLaunchKernelGGL((igemm_generic_kernel<128, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
+                               bias, y, P, Kg, w_vec, g0);
+        } else {
+            dim3 grid(gx, (unsigned)((Cog + 63) / 64), gz);
+            hipLaunchKernelGGL((igemm_generic_kernel<64, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
+                               bias, y, P, Kg, w_vec, g0);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace

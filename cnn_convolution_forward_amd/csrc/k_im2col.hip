@@ -2,10 +2,13 @@
 //
 // X_col has C_in*K^dims rows and N*Do*Ho*Wo columns, row-major, bf16.  Row
 // r = ((ic*Kd + kd)*K + kh)*K + kw; column j = ((n*Do + od)*Ho + oh)*Wo + ow;
-// the entry is x at (od*sd+kd-pd, oh*s+kh-p, ow*s+kw-p), or 0 when that
+// the entry is x at (od*sd+kd*dd-pd, oh*s+kh*d-p, ow*s+kw*d-p), or 0 when that
 // coordinate is outside the input ("Why use matrix multiplication for
 // convolution", 2.2 and 3.1; zero padding by bounds checks, "Hand-writing
-// Conv2D", 1.2).  It is a pure copy, so the result is exact.
+// Conv2D", 1.2; taps d apart under dilation, "PyTorch tensor products and
+// conv2d/conv3d dimension semantics", 4.2).  Groups do not change X_col: group
+// g multiplies its own block of C_in/G * K^dims consecutive rows.  It is a
+// pure copy, so the result is exact.
 //
 // Mapping: a thread owns one row r and 8 consecutive columns, so a wave writes
 // 64 x 16 B = 1 KB contiguous along j (the pixel axis) and, for stride 1, reads
@@ -43,9 +46,9 @@ void im2col_bf16_kernel(Shape sh, const uint16_t *__restrict__ x, uint16_t *__re
         for (int e = 0; e < kColsPerThread; ++e) {
             uint16_t val = 0;
             if (n < sh.N) {
-                int id = od * sh.sd + kd - sh.pd;
-                int ih = oh * sh.s + kh - sh.p;
-                int iw = ow * sh.s + kw - sh.p;
+                int id = od * sh.sd + kd * sh.dild - sh.pd;
+                int ih = oh * sh.s + kh * sh.dil - sh.p;
+                int iw = ow * sh.s + kw * sh.dil - sh.p;
                 if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W)
                     val = x[(((int64_t)n * sh.C + ic) * sh.D + id) * ((int64_t)sh.H * sh.W) +
                             (int64_t)ih * sh.W + iw];
@@ -73,7 +76,7 @@ void im2col_bf16_kernel(Shape sh, const uint16_t *__restrict__ x, uint16_t *__re
 
 hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol, hipStream_t st) {
     const int64_t J = sh.pixels();
-    const int rows = (int)sh.kgemm();
+    const int rows = (int)sh.xcol_rows();
     const int64_t groups = (J + kColsPerThread - 1) / kColsPerThread;
     dim3 grid((unsigned)((groups + kThreads - 1) / kThreads), (unsigned)(rows < 65535 ? rows : 65535));
     hipLaunchKernelGGL(im2col_bf16_kernel, grid, dim3(kThreads), 0, st, sh, x, xcol, J, rows);

@@ -264,7 +264,7 @@ size_t smem_bytes(const SmallKPlan &pl) {
 }  // namespace
 
 bool smallk_supported(const Shape &sh) {
-    if (sh.kgemm() > kMaxK) return false;
+    if (!sh.plain() || sh.kgemm() > kMaxK) return false;
     if (patch_elems(sh, 1, false) > kPatchElems) return false;
     if ((int64_t)kOcBlock * sh.out_plane() * 4 >= (INT64_C(1) << 31)) return false;   // one output block per buffer range
     return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);

@@ -50,7 +50,13 @@ class Workload:
     x_dist: str                    # "uniform" (U[-1,1]) or "normal" (N(0,1))
     seed: int
     has_bias: bool = True
+    dilation: int = 1
+    groups: int = 1                # divides C_in and C_out; C_in is depthwise
     note: str = field(default="", compare=False)
+
+    @property
+    def plain(self):
+        return self.dilation == 1 and self.groups == 1
 
     @property
     def x_shape(self):
@@ -58,21 +64,22 @@ class Workload:
 
     @property
     def w_shape(self):
-        return (self.C_out, self.C_in) + (self.K,) * self.ndim
+        return (self.C_out, self.C_in // self.groups) + (self.K,) * self.ndim
 
     @property
     def fan_in(self):
-        return self.C_in * self.K ** self.ndim
+        return self.C_in // self.groups * self.K ** self.ndim
 
     def out_spatial(self):
-        return tuple((d + 2 * self.pad - self.K) // self.stride + 1 for d in self.spatial)
+        span = self.dilation * (self.K - 1) + 1
+        return tuple((d + 2 * self.pad - span) // self.stride + 1 for d in self.spatial)
 
     @property
     def y_shape(self):
         return (self.N, self.C_out) + self.out_spatial()
 
     def flops(self) -> int:
-        """2 * N * C_out * prod(out) * C_in * K^ndim, padded taps included."""
+        """2 * N * C_out * prod(out) * (C_in/groups) * K^ndim, padded taps included."""
         return 2 * int(np.prod(self.y_shape, dtype=np.int64)) * self.fan_in
 
 
@@ -90,6 +97,19 @@ WORKLOADS = {
                             note="x (8,3,16,64,64), w (64,3,3,3,3), s1 p1 -> (8,64,16,64,64)"),
 }
 HEADLINE = "conv3x3_bf16"
+
+# Dilation and groups at the 3x3 layer's size (64 x 128 x 56 x 56, N(0,1) inputs,
+# N(0, 1/sqrt(fan_in)) weights): depthwise (groups = C_in, weight (128,1,3,3)),
+# dilation 2 with pad 2 (size kept), and groups = 4 (weight (128,32,3,3)).
+WORKLOADS_GENERAL = {
+    "depthwise3x3_bf16": Workload("depthwise3x3_bf16", 2, 64, 128, (56, 56), 128, 3, 1, 1, "bf16", "normal", 6,
+                                  groups=128, note="x (64,128,56,56), w (128,1,3,3), groups 128 -> (64,128,56,56)"),
+    "dilated3x3_bf16": Workload("dilated3x3_bf16", 2, 64, 128, (56, 56), 128, 3, 1, 2, "bf16", "normal", 7,
+                                dilation=2, note="x (64,128,56,56), w (128,128,3,3), d2 p2 -> (64,128,56,56)"),
+    "grouped3x3_bf16": Workload("grouped3x3_bf16", 2, 64, 128, (56, 56), 128, 3, 1, 1, "bf16", "normal", 8,
+                                groups=4, note="x (64,128,56,56), w (128,32,3,3), groups 4 -> (64,128,56,56)"),
+}
+ALL_WORKLOADS = {**WORKLOADS, **WORKLOADS_GENERAL}
 
 
 @dataclass
@@ -133,5 +153,5 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, integer: bool = False,
 
 
 def workload(name: str, **override) -> Workload:
-    wl = WORKLOADS[name]
+    wl = ALL_WORKLOADS[name]
     return Workload(**{**wl.__dict__, **override}) if override else wl

@@ -58,7 +58,8 @@ extern "C" {
 typedef enum {
     CONV_OK = 0,
     CONV_ERR_NULL = 1,       /* a required pointer (x, w, y, workspace) is NULL            */
-    CONV_ERR_PARAM = 2,      /* a size < 1, K < 1, stride < 1 or pad < 0                    */
+    CONV_ERR_PARAM = 2,      /* a size < 1, K < 1, stride < 1, pad < 0 (or, for the general
+                                entry points, dilation < 1 or groups not dividing C_in, C_out) */
     CONV_ERR_SHAPE = 3,      /* in + 2*pad < K in some spatial dimension (no output)        */
     CONV_ERR_OVERFLOW = 4,   /* a tensor would hold 2^31 or more elements                   */
     CONV_ERR_ALIAS = 5,      /* y overlaps x, w, bias or the workspace                      */
@@ -198,6 +199,73 @@ CONV_API conv_status_t conv3d_fwd_bf16_explicit(const uint16_t *x, const uint16_
                                        float *y, void *workspace, size_t workspace_bytes,
                                        int N, int C_in, int D, int H, int W, int C_out,
                                        int K, int stride, int pad, void *stream);
+
+/* ---- general problems: dilation and groups -------------------------------
+ *
+ * Dilation d places the K taps of a window d inputs apart, so a window spans
+ * d(K-1)+1 inputs and  out = floor((in + 2*pad - d(K-1) - 1)/stride) + 1
+ * ("PyTorch tensor products and conv2d/conv3d dimension semantics", 4.2;
+ * "Conv2d from the official docs", 3.2-3.3).  Groups G cut C_in and C_out into
+ * G equal consecutive blocks; output block g reads input block g only, and the
+ * weight holds C_in/G input channels per filter (same pages, 4.3 and 3.4).
+ * G == C_in is the depthwise layer.  With g = oc / (C_out/G):
+ *
+ *     y[n][oc][oh][ow] = bias[oc] + sum_{j < C_in/G, kh, kw}
+ *         x[n][g*C_in/G + j][oh*s + kh*d - p][ow*s + kw*d - p] * w[oc][j][kh][kw]
+ *
+ * (3D adds od*s + kd*d - p on the depth axis).  Taps outside the input add 0.
+ * Layouts as above, except w is (C_out, C_in/G, K, K[, K]).  With d = 1 and
+ * G = 1 every entry point below computes exactly what its conv2d_/conv3d_
+ * counterpart computes.  Extra errors: CONV_ERR_PARAM when dilation < 1,
+ * groups < 1, groups does not divide C_in and C_out, or ndim is not 2 or 3;
+ * CONV_ERR_NULL when the parameter block is NULL. */
+typedef struct {
+    int ndim;        /* 2 or 3                                                  */
+    int N, C_in;
+    int D;           /* input depth; ignored (taken as 1) when ndim == 2         */
+    int H, W;
+    int C_out;
+    int K;           /* kernel extent, the same in every spatial dimension       */
+    int stride, pad; /* the same in every spatial dimension                      */
+    int dilation;    /* >= 1                                                     */
+    int groups;      /* >= 1, divides C_in and C_out                             */
+} conv_params_t;
+
+/* floor((in + 2*pad - dilation*(K-1) - 1)/stride) + 1, or -1 on a bad
+ * parameter or when the dilated window does not fit in the padded input. */
+CONV_API int64_t conv_out_dim_dilated(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t dilation);
+
+/* y = conv(x, w) + bias for a general problem, bf16 x and w, fp32 bias (NULL =
+ * none) and y.  AUTO: one input channel per group (C_in/G == 1, 2D) -> the
+ * depthwise VALU kernel, which reads each input once and writes each output
+ * once; a per-group reduction (C_in/G * K^ndim) <= 32 -> the direct VALU
+ * kernel; otherwise the MFMA implicit GEMM, one GEMM of C_out/G x
+ * (C_in/G * K^ndim) per group. */
+CONV_API conv_status_t conv_fwd_bf16(const conv_params_t *params, const uint16_t *x, const uint16_t *w,
+                                     const float *bias, float *y, int algo, void *stream);
+
+/* fp32 twin (VALU route only). */
+CONV_API conv_status_t conv_fwd_f32(const conv_params_t *params, const float *x, const float *w,
+                                    const float *bias, float *y, int algo, void *stream);
+
+/* Bytes of the bf16 X_col of a general problem: C_in*K^ndim rows (groups do
+ * not change X_col; group g uses rows [g, g+1) * C_in/G * K^ndim) by
+ * N * (output positions) columns; 0 on invalid parameters or when X_col would
+ * hold 2^31 or more elements. */
+CONV_API size_t conv_xcol_bytes(const conv_params_t *params);
+
+/* X_col of a general problem: row ((ic*K + kd)*K + kh)*K + kw (kd absent in
+ * 2D), column in output order, entry x at the dilated tap coordinate, 0
+ * outside.  xcol must hold conv_xcol_bytes() bytes.  Exact copy. */
+CONV_API conv_status_t conv_im2col_bf16(const conv_params_t *params, const uint16_t *x, uint16_t *xcol,
+                                        void *stream);
+
+/* conv_im2col_bf16 into the workspace (>= conv_xcol_bytes() bytes), then per
+ * group g the GEMM W_row[g] (C_out/G x C_in/G*K^ndim) @ X_col[rows of g] with
+ * bias, stored into y in N C_out (D) H W order. */
+CONV_API conv_status_t conv_fwd_explicit_bf16(const conv_params_t *params, const uint16_t *x,
+                                              const uint16_t *w, const float *bias, float *y,
+                                              void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -71,3 +71,20 @@ def compare(y_gpu, y_ref, S, tau, exact=False, label=""):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)
     return float(r.max())
+
+
+def run_general(wl, t, algo="auto", explicit=False):
+    """conv_fwd_bf16 / conv_fwd_f32 / conv_fwd_explicit_bf16 on a workload
+    with dilation and groups."""
+    x, w, b = dev(t.x, np.float32), dev(t.w, np.float32), dev(t.b, np.float32)
+    y = poisoned(wl.y_shape)
+    if explicit:
+        B.conv_explicit_general(x, w, b, wl.stride, wl.pad, wl.dilation, wl.groups, out=y)
+    else:
+        B.conv_general(x, w, b, wl.stride, wl.pad, wl.dilation, wl.groups, algo=algo, out=y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def reference_general(wl, t):
+    return oracle.conv_general(t.x, t.w, t.b, wl.stride, wl.pad, wl.dilation, wl.groups)

@@ -154,3 +154,63 @@ def test_pack_and_prepacked_validation():
     assert B.conv2d_fwd_bf16_prepacked(X, WS, need - 16, BIAS, Y, *dims, 0, None) == 6
     assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, WS + 64, *dims, 0, None) == 5   # y over workspace
     assert B.conv2d_fwd_bf16_prepacked(X, WS, need, BIAS, X + 64, *dims, 0, None) == 5    # y over x
+
+
+# ---- general entry points (dilation and groups) ------------------------------
+
+def _gp(**kw):
+    base = dict(ndim=2, N=2, C_in=8, D=1, H=9, W=11, C_out=16, K=3, stride=1, pad=1, dilation=2, groups=4)
+    base.update(kw)
+    return B.ConvParams(**base)
+
+
+def test_out_dim_dilated_matches_pages(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "dilated_sizes.json")))
+    for c in g["cases"]:
+        assert B.conv_out_dim_dilated(c["in"], c["k"], c["s"], c["p"], c["d"]) == c["out"], c
+    g = json.load(open(os.path.join(golden_dir, "output_sizes.json")))
+    for c in g["cases"]:
+        assert B.conv_out_dim_dilated(c["in"], c["k"], c["s"], c["p"], 1) == c["out"], c
+    assert B.conv_out_dim_dilated(9, 3, 1, 1, 0) == -1
+    assert B.conv_out_dim_dilated(9, 3, 1, 1, 1 << 40) == -1
+
+
+def test_general_validation():
+    f = lambda prm, x=X, w=Wp, b=BIAS, y=Y, algo=0: B.conv_fwd_bf16(prm, x, w, b, y, algo, None)
+    assert f(None) == 1
+    assert f(_gp(), x=None) == 1
+    assert f(_gp(), y=None) == 1
+    assert f(_gp(dilation=0)) == 2
+    assert f(_gp(groups=0)) == 2
+    assert f(_gp(groups=3)) == 2                      # does not divide C_in = 8
+    assert f(_gp(groups=8, C_out=12)) == 2            # does not divide C_out
+    assert f(_gp(ndim=4)) == 2
+    assert f(_gp(ndim=1)) == 2
+    assert f(_gp(H=6, W=6, pad=0, dilation=3, K=3)) == 3      # span 7 > 6
+    assert f(_gp(), algo=9) == 7
+    assert f(_gp(), y=X + 64) == 5
+    assert B.conv_fwd_f32(_gp(), X, Wp, BIAS, Y, 1, None) == 7        # MFMA is bf16-only
+    assert B.conv_fwd_f32(None, X, Wp, BIAS, Y, 0, None) == 1
+    assert f(_gp(ndim=3, D=0)) == 2                  # D is read in 3D
+    # the weight holds C_out * C_in/groups * K*K elements: y 4 bytes before its end overlaps it
+    assert f(_gp(), y=Wp + 16 * 2 * 9 * 2 - 4) == 5
+
+
+def test_general_xcol_bytes_and_explicit_validation():
+    prm = _gp()
+    Ho, Wo = B.conv_out_dim_dilated(9, 3, 1, 1, 2), B.conv_out_dim_dilated(11, 3, 1, 1, 2)
+    need = 8 * 9 * 2 * Ho * Wo * 2
+    assert B.conv_xcol_bytes(prm) == need
+    assert B.conv_xcol_bytes(None) == 0
+    assert B.conv_xcol_bytes(_gp(groups=3)) == 0
+    assert B.conv_xcol_bytes(_gp(ndim=3, D=5)) == 8 * 27 * 2 * B.conv_out_dim_dilated(5, 3, 1, 1, 2) * Ho * Wo * 2
+    e = lambda prm, ws=WS, nb=need, y=Y: B.conv_fwd_explicit_bf16(prm, X, Wp, BIAS, y, ws, nb, None)
+    assert e(None) == 1
+    assert e(prm, ws=None) == 1
+    assert e(prm, nb=need - 2) == 6
+    assert e(prm, ws=Y + 8) == 5
+    assert e(_gp(groups=5)) == 2
+    assert B.conv_im2col_bf16(None, X, Y, None) == 1
+    assert B.conv_im2col_bf16(prm, None, Y, None) == 1
+    assert B.conv_im2col_bf16(prm, X, X + 2, None) == 5
+    assert B.conv_im2col_bf16(_gp(dilation=-1), X, Y, None) == 2
