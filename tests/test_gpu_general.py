@@ -90,6 +90,8 @@ DEPTHWISE = [
     (2, 16, 7, 7, 1, 7, 1, 3, 1),              # K 7 (runtime K)
     (1, 2, 1, 1, 4, 3, 1, 1, 1),               # 1x1 input: only the centre tap
     (1, 1, 9, 9, 8, 3, 1, 1, 1),               # C_in = 1, groups = 1: one channel, 8 filters
+    (1, 4097, 32, 32, 1, 3, 1, 1, 1),          # 4097 tiles: two tiles per workgroup, odd tail
+    (1, 16387, 8, 16, 1, 3, 2, 1, 1),          # 16387 tiles: eight per workgroup, ragged tail
 ]
 
 
