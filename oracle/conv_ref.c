@@ -27,9 +27,9 @@
  * Besides y, each convolution returns S = sum over the same taps of |x * w|
  * (bias excluded), the scale against which a low-precision result is judged.
  *
- * Parity pins live in tests/test_oracle_pins.py (plain convolution) and
- * tests/test_oracle_pins_general.py (dilation and groups); every function here
- * is pinned.
+ * Parity pins live in tests/test_oracle_pins.py (plain convolution),
+ * tests/test_oracle_pins_general.py (dilation and groups) and
+ * tests/test_oracle_pins_backward.py (gradients); every function here is pinned.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -419,6 +419,105 @@ int oracle_im2col_dilated(int ndim, const double *x, double *col,
                 if (0 <= iz && iz < g.Dd && 0 <= iy && iy < H && 0 <= ix && ix < W)
                     v = x[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix];
                 col[r * cols + n * plane + q] = v;
+              }
+          }
+    return 0;
+}
+
+/* ---- backward: db, dW, dx -------------------------------------------------
+ *
+ *   [Hand-writing Conv2D, 5.1]  with upstream gradient dout (the shape of y):
+ *        db[oc] = sum over n, oh, ow of dout[n][oc][oh][ow];
+ *        dW[oc][ic][kh][kw] = sum over n, oh, ow of dout[n][oc][oh][ow] times
+ *            the input the tap read, x[n][ic][oh*s + kh - p][ow*s + kw - p]
+ *            (taps outside the input add nothing);
+ *        dx scatters each dout[n][oc][oh][ow] * w[oc][ic][kh][kw] back onto
+ *            the input position that tap read, accumulating (several windows
+ *            cover one input).
+ *   [Hand-writing Conv2D, 5.2]  the same loop computes dW and dx, since they
+ *        visit the same input coordinates; written here over the general
+ *        geometry (dilation d, groups G, 3D) of the forward functions above.
+ *   [Why use matrix multiplication for convolution, 3.3]  the same results as
+ *        dW_row = dout_col @ X_col^T and dx = col2im(W_row^T @ dout_col); see
+ *        oracle_col2im_dilated below.
+ * Besides the gradients, S_dx, S_dw and S_db hold the sums of the magnitudes
+ * of the same products (|w * dout|, |dout * x|, |dout|): the scale against
+ * which a low-precision result is judged.  Any of the outputs may be NULL.
+ */
+int oracle_conv_backward(int ndim, const double *x, const double *w, const double *dout,
+                         double *dx, double *dw, double *db,
+                         double *S_dx, double *S_dw, double *S_db,
+                         int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                         int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, Co, K, s, p, d, G) != 0) return -1;
+    const int64_t Cg = C / G, Cog = Co / G;
+    const int64_t nx = N * C * g.Dd * H * W, nw = Co * Cg * g.Kz * K * K;
+    for (int64_t i = 0; i < nx; ++i) { if (dx) dx[i] = 0.0; if (S_dx) S_dx[i] = 0.0; }
+    for (int64_t i = 0; i < nw; ++i) { if (dw) dw[i] = 0.0; if (S_dw) S_dw[i] = 0.0; }
+    for (int64_t oc = 0; oc < Co; ++oc) { if (db) db[oc] = 0.0; if (S_db) S_db[oc] = 0.0; }
+    /* Sequential on purpose: dx and dW are accumulated from many outputs. */
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t oc = 0; oc < Co; ++oc) {
+        const int64_t grp = oc / Cog;
+        for (int64_t od = 0; od < g.Do; ++od)
+          for (int64_t oh = 0; oh < g.Ho; ++oh)
+            for (int64_t ow = 0; ow < g.Wo; ++ow) {
+              const double gout = dout[(((n * Co + oc) * g.Do + od) * g.Ho + oh) * g.Wo + ow];
+              if (db) db[oc] += gout;
+              if (S_db) S_db[oc] += fabs(gout);
+              for (int64_t j = 0; j < Cg; ++j) {
+                const int64_t ic = grp * Cg + j;
+                for (int64_t kz = 0; kz < g.Kz; ++kz) {
+                  const int64_t iz = od * g.sz + kz * g.dz - g.pz;
+                  if (iz < 0 || iz >= g.Dd) continue;
+                  for (int64_t kh = 0; kh < K; ++kh) {
+                    const int64_t iy = oh * s + kh * d - p;
+                    if (iy < 0 || iy >= H) continue;
+                    for (int64_t kw = 0; kw < K; ++kw) {
+                      const int64_t ix = ow * s + kw * d - p;
+                      if (ix < 0 || ix >= W) continue;
+                      const int64_t xi = (((n * C + ic) * g.Dd + iz) * H + iy) * W + ix;
+                      const int64_t wi = (((oc * Cg + j) * g.Kz + kz) * K + kh) * K + kw;
+                      if (dw) dw[wi] += gout * x[xi];
+                      if (S_dw) S_dw[wi] += fabs(gout * x[xi]);
+                      if (dx) dx[xi] += w[wi] * gout;
+                      if (S_dx) S_dx[xi] += fabs(w[wi] * gout);
+                    }
+                  }
+                }
+              }
+            }
+      }
+    return 0;
+}
+
+/* col2im, the adjoint of oracle_im2col_dilated [Why use matrix multiplication
+ * for convolution, 3.3]: every entry of col (C*K^ndim rows, N*Do*Ho*Wo
+ * columns, the im2col layout) is added onto the input position its tap read;
+ * entries whose tap fell in the padding are dropped (the page pads, adds,
+ * then crops the padding away, which is the same).  dx has x's shape. */
+int oracle_col2im_dilated(int ndim, const double *col, double *dx,
+                          int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                          int64_t K, int64_t s, int64_t p, int64_t d)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, 1, K, s, p, d, 1) != 0) return -1;
+    const int64_t plane = g.Do * g.Ho * g.Wo, cols = N * plane;
+    for (int64_t i = 0; i < N * C * g.Dd * H * W; ++i) dx[i] = 0.0;
+    for (int64_t ic = 0; ic < C; ++ic)
+      for (int64_t kz = 0; kz < g.Kz; ++kz)
+        for (int64_t kh = 0; kh < K; ++kh)
+          for (int64_t kw = 0; kw < K; ++kw) {
+            const int64_t r = ((ic * g.Kz + kz) * K + kh) * K + kw;
+            for (int64_t n = 0; n < N; ++n)
+              for (int64_t q = 0; q < plane; ++q) {
+                const int64_t ow = q % g.Wo, oh = (q / g.Wo) % g.Ho, od = q / (g.Wo * g.Ho);
+                const int64_t iz = od * g.sz + kz * g.dz - g.pz;
+                const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw * d - p;
+                if (0 <= iz && iz < g.Dd && 0 <= iy && iy < H && 0 <= ix && ix < W)
+                    dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] += col[r * cols + n * plane + q];
               }
           }
     return 0;

@@ -76,6 +76,10 @@ def lib():
                                                  _dp, _dp] + [_i64] * 11
         L.oracle_im2col_dilated.restype = ctypes.c_int
         L.oracle_im2col_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
+        L.oracle_conv_backward.restype = ctypes.c_int
+        L.oracle_conv_backward.argtypes = [ctypes.c_int] + [_dp] * 9 + [_i64] * 11
+        L.oracle_col2im_dilated.restype = ctypes.c_int
+        L.oracle_col2im_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -292,6 +296,40 @@ def im2col_dilated(x, K, stride, pad, dilation):
     if lib().oracle_im2col_dilated(ndim, _p(x), _p(col), N, C, D, H, W, K, stride, pad, dilation) != 0:
         raise ValueError("bad im2col shape")
     return col
+
+
+def conv_backward(x, w, dout, stride=1, pad=0, dilation=1, groups=1):
+    """(dx, dw, db) and their magnitude sums (S_dx, S_dw, S_db) of a 2D or 3D
+    convolution, fp64 [Hand-writing Conv2D, 5.1-5.2].  dout has y's shape."""
+    x, w, dout = decode(x), decode(w), decode(dout)
+    ndim, N, C, D, H, W, Co, K = _general_dims(x, w, groups)
+    sizes = [out_dim_dilated(n, K, stride, pad, dilation) for n in ((D, H, W) if ndim == 3 else (H, W))]
+    if min(sizes) < 0 or dout.shape != (N, Co) + tuple(sizes):
+        raise ValueError("dout shape %s does not match the output (N, C_out) + %s" % (dout.shape, sizes))
+    dx, Sdx = np.empty_like(x), np.empty_like(x)
+    dw, Sdw = np.empty_like(w), np.empty_like(w)
+    db, Sdb = np.empty(Co), np.empty(Co)
+    rc = lib().oracle_conv_backward(ndim, _p(x), _p(w), _p(dout), _p(dx), _p(dw), _p(db), _p(Sdx), _p(Sdw),
+                                    _p(Sdb), N, C, D, H, W, Co, K, stride, pad, dilation, groups)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward rejected the shape")
+    return (dx, dw, db), (Sdx, Sdw, Sdb)
+
+
+def col2im_dilated(col, x_shape, K, stride, pad, dilation=1):
+    """Adjoint of im2col_dilated: add each X_col entry onto the input position
+    its tap read [Why use matrix multiplication for convolution, 3.3]."""
+    col = _f64(col)
+    ndim = len(x_shape) - 2
+    if ndim == 2:
+        N, C, H, W = x_shape
+        D = 1
+    else:
+        N, C, D, H, W = x_shape
+    dx = np.empty(tuple(x_shape), np.float64)
+    if lib().oracle_col2im_dilated(ndim, _p(col), _p(dx), N, C, D, H, W, K, stride, pad, dilation) != 0:
+        raise ValueError("bad col2im shape")
+    return dx
 
 
 def num_threads() -> int:

@@ -5,9 +5,11 @@ slip: sign of the padding offset, kh/kw swapped, bias dropped, X_col columns
 transposed, a depth offset lost, |x*w| replaced by x*w, ceil for floor, an
 off-by-one bounds check; in the dilation/groups functions: dilation dropped
 from an axis, groups interleaved, the group's channel offset lost, the dilated
-span mis-sized), builds it with gcc, and runs the matching pin file
-(tests/test_oracle_pins.py or tests/test_oracle_pins_general.py) against that
-build in a subprocess.  The run must fail.  Runs on the CPU only.
+span mis-sized; in the backward pass: dx overwritten, dW from w, db over one
+image, the stride or group offset lost, col2im overwriting), builds it with
+gcc, and runs the matching pin file (tests/test_oracle_pins.py,
+tests/test_oracle_pins_general.py or tests/test_oracle_pins_backward.py)
+against that build in a subprocess.  The run must fail.  Runs on the CPU only.
 """
 import os
 import subprocess
@@ -41,21 +43,35 @@ MUTANTS_GENERAL = {
                            "const int64_t iy = oh * g->s + kh - g->p;"),
     "depth_dilation_dropped": ("const int64_t iz = od * g->sz + kz * g->dz - g->pz;",
                                "const int64_t iz = od * g->sz + kz - g->pz;"),
-    "groups_interleaved": ("const int64_t grp = oc / Cog;", "const int64_t grp = oc % g->G;"),
-    "group_offset_dropped": ("const int64_t ic = grp * Cg + j;", "const int64_t ic = j + 0 * grp;"),
+    "groups_interleaved": ("const int64_t grp = oc / Cog;\n    double acc", "const int64_t grp = oc % g->G;\n    double acc"),
+    "group_offset_dropped": ("const int64_t ic = grp * Cg + j;\n        for (int64_t kz = 0; kz < g->Kz; ++kz) {",
+                             "const int64_t ic = j + 0 * grp;\n        for (int64_t kz = 0; kz < g->Kz; ++kz) {"),
     "dilated_span_wrong": ("int64_t span = d * (k - 1) + 1;", "int64_t span = d * k - d + 1 + (d > 1);"),
-    "im2col_dilation_dropped_w": ("const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw * d - p;",
-                                  "const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw - p;"),
+    "im2col_dilation_dropped_w": ("const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw * d - p;\n                double v",
+                                  "const int64_t iy = oh * s + kh * d - p, ix = ow * s + kw - p;\n                double v"),
 }
 
 
+# Mistakes in the backward pass and col2im, caught by test_oracle_pins_backward.py.
+MUTANTS_BACKWARD = {
+    "dx_overwritten": ("if (dx) dx[xi] += w[wi] * gout;", "if (dx) dx[xi] = w[wi] * gout;"),
+    "dw_from_w": ("if (dw) dw[wi] += gout * x[xi];", "if (dw) dw[wi] += gout * w[wi];"),
+    "db_one_image": ("if (db) db[oc] += gout;", "if (db && n == 0) db[oc] += gout;"),
+    "bwd_stride_dropped": ("const int64_t iy = oh * s + kh * d - p;\n", "const int64_t iy = oh + kh * d - p;\n"),
+    "bwd_group_offset_dropped": ("const int64_t ic = grp * Cg + j;\n                for (int64_t kz = 0; kz < g.Kz; ++kz) {",
+                                 "const int64_t ic = j + 0 * grp;\n                for (int64_t kz = 0; kz < g.Kz; ++kz) {"),
+    "col2im_overwrites": ("dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] += col[r * cols + n * plane + q];",
+                          "dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] = col[r * cols + n * plane + q];"),
+}
+
 CASES = [(n, "test_oracle_pins.py") for n in sorted(MUTANTS)] + \
-        [(n, "test_oracle_pins_general.py") for n in sorted(MUTANTS_GENERAL)]
+        [(n, "test_oracle_pins_general.py") for n in sorted(MUTANTS_GENERAL)] + \
+        [(n, "test_oracle_pins_backward.py") for n in sorted(MUTANTS_BACKWARD)]
 
 
 @pytest.mark.parametrize("name,pins", CASES)
 def test_planted_mistake_is_caught(name, pins, tmp_path):
-    old, new = {**MUTANTS, **MUTANTS_GENERAL}[name]
+    old, new = {**MUTANTS, **MUTANTS_GENERAL, **MUTANTS_BACKWARD}[name]
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not found once: %s" % name
     mutant_c = tmp_path / "conv_ref_mutant.c"
