@@ -30,7 +30,9 @@ EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
            "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit",
            "conv_out_dim_dilated", "conv_fwd_bf16", "conv_fwd_f32", "conv_xcol_bytes",
-           "conv_im2col_bf16", "conv_fwd_explicit_bf16")
+           "conv_im2col_bf16", "conv_fwd_explicit_bf16",
+           "conv_bwd_data_workspace_bytes", "conv_bwd_data_bf16",
+           "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_bf16")
 
 
 class ConvParams(ctypes.Structure):
@@ -99,6 +101,13 @@ def lib():
         L.conv_im2col_bf16.argtypes = [_pp, _vp, _vp, _vp]
         L.conv_fwd_explicit_bf16.restype = _i
         L.conv_fwd_explicit_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        for name in ("conv_bwd_data_workspace_bytes", "conv_bwd_weight_workspace_bytes"):
+            getattr(L, name).restype = _sz
+            getattr(L, name).argtypes = [_pp]
+        L.conv_bwd_data_bf16.restype = _i
+        L.conv_bwd_data_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.conv_bwd_weight_bf16.restype = _i
+        L.conv_bwd_weight_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -207,6 +216,22 @@ def conv_im2col_bf16(params, x, xcol, stream=None):
 
 def conv_fwd_explicit_bf16(params, x, w, bias, y, ws, ws_bytes, stream=None):
     return lib().conv_fwd_explicit_bf16(_pref(params), x, w, bias, y, ws, ws_bytes, stream)
+
+
+def conv_bwd_data_workspace_bytes(params):
+    return int(lib().conv_bwd_data_workspace_bytes(_pref(params)))
+
+
+def conv_bwd_data_bf16(params, dout, w, dx, ws, ws_bytes, stream=None):
+    return lib().conv_bwd_data_bf16(_pref(params), dout, w, dx, ws, ws_bytes, stream)
+
+
+def conv_bwd_weight_workspace_bytes(params):
+    return int(lib().conv_bwd_weight_workspace_bytes(_pref(params)))
+
+
+def conv_bwd_weight_bf16(params, x, dout, dw, db, ws, ws_bytes, stream=None):
+    return lib().conv_bwd_weight_bf16(_pref(params), x, dout, dw, db, ws, ws_bytes, stream)
 
 
 def make_params(x_shape, w_shape, stride=1, pad=0, dilation=1, groups=1):
@@ -492,3 +517,34 @@ def conv_explicit_general(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1
     if st != CONV_OK:
         raise ConvError(st, "conv_fwd_explicit_bf16")
     return y
+
+
+def conv_backward(x, w, dout, stride=1, pad=0, dilation=1, groups=1, with_db=True, out=None):
+    """(dx, dw, db) of y = conv(x, w) + b for upstream gradient dout, all bf16
+    inputs (conv_bwd_data_bf16 + conv_bwd_weight_bf16); fp32 results.  `out`:
+    optional (dx, dw, db) tensors to write into."""
+    torch = _torch()
+    _general_check(x, w, groups)
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    for t, n in ((x, "x"), (w, "w"), (dout, "dout")):
+        _check_tensor(t, n, half)
+    prm = make_params(tuple(x.shape), tuple(w.shape), stride, pad, dilation, groups)
+    yshape = _general_out_shape(x, w, stride, pad, dilation)
+    if tuple(dout.shape) != tuple(yshape):
+        raise ValueError("dout has shape %s, the output is %s" % (tuple(dout.shape), yshape))
+    if out is None:
+        dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        dw = torch.empty(w.shape, dtype=torch.float32, device=x.device)
+        db = torch.empty((w.shape[0],), dtype=torch.float32, device=x.device) if with_db else None
+    else:
+        dx, dw, db = out
+    nd, nw = conv_bwd_data_workspace_bytes(prm), conv_bwd_weight_workspace_bytes(prm)
+    wsd = torch.empty(max(nd, 16), dtype=torch.uint8, device=x.device)
+    wsw = torch.empty(max(nw, 16), dtype=torch.uint8, device=x.device)
+    st = conv_bwd_data_bf16(prm, _ptr(dout), _ptr(w), _ptr(dx), _ptr(wsd), wsd.numel(), _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_bwd_data_bf16")
+    st = conv_bwd_weight_bf16(prm, _ptr(x), _ptr(dout), _ptr(dw), _ptr(db), _ptr(wsw), wsw.numel(), _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_bwd_weight_bf16")
+    return dx, dw, db

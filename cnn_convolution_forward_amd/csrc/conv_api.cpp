@@ -192,6 +192,46 @@ conv_status_t explicit_bf16(int ndim, const uint16_t *x, const uint16_t *w, cons
     return explicit_bf16_sh(sh, x, w, bias, y, ws, ws_bytes, stream);
 }
 
+// ---- backward helpers ----
+
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// The data gradient as a forward problem: dout (N, C_out, out...) convolved
+// with the flipped, per-group transposed weights, stride 1, pad d(K-1) - p,
+// dilation d, groups G, gives dx (N, C_in, in...).  With stride s > 1 (or a
+// pad beyond d(K-1)) the general kernel reads dout through zero insertion.
+struct DgradPlan {
+    Shape sh;        // the forward problem on dout
+    bool upsampled;  // general kernel, upsampled mode (sh.Do/Ho/Wo set by hand)
+};
+
+DgradPlan dgrad_plan(const Shape &fw) {
+    DgradPlan d;
+    Shape &s = d.sh;
+    const int pt = fw.dil * (fw.K - 1) - fw.p;            // pad of the flipped convolution
+    s.ndim = fw.ndim;
+    s.N = fw.N; s.C = fw.Co; s.D = fw.Do; s.H = fw.Ho; s.W = fw.Wo; s.Co = fw.C;
+    s.K = fw.K; s.s = 1; s.p = pt;
+    s.Kd = fw.Kd; s.sd = 1; s.pd = fw.ndim == 3 ? pt : 0;
+    s.dil = fw.dil; s.dild = fw.dild; s.G = fw.G;
+    s.Do = fw.D; s.Ho = fw.H; s.Wo = fw.W;
+    s.ups = fw.s; s.upsd = fw.ndim == 3 ? fw.s : 1;
+    d.upsampled = fw.s != 1 || pt < 0;
+    return d;
+}
+
+size_t dgrad_workspace(const Shape &fw) {
+    const DgradPlan d = dgrad_plan(fw);
+    size_t n = align_up((size_t)fw.w_elems() * 2);
+    if (!d.upsampled) n += convfwd::igemm_workspace_bytes(d.sh, (const void *)256, (const void *)256);
+    return n;
+}
+
+size_t wgrad_workspace(const Shape &fw) {
+    return (size_t)convfwd::wgrad_splits(fw) * (size_t)fw.w_elems() * 4;
+}
+
 }  // namespace
 
 namespace convfwd {
@@ -423,6 +463,68 @@ conv_status_t conv_fwd_explicit_bf16(const conv_params_t *prm, const uint16_t *x
     conv_status_t st = shape_from_params(prm, sh);
     if (st != CONV_OK) return st;
     return explicit_bf16_sh(sh, x, w, bias, y, workspace, workspace_bytes, stream);
+}
+
+// ---- backward ----
+
+size_t conv_bwd_data_workspace_bytes(const conv_params_t *prm) {
+    if (!prm) return 0;
+    Shape sh;
+    if (shape_from_params(prm, sh) != CONV_OK) return 0;
+    return dgrad_workspace(sh);
+}
+
+conv_status_t conv_bwd_data_bf16(const conv_params_t *prm, const uint16_t *dout, const uint16_t *w, float *dx,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!prm || !dout || !w || !dx || !workspace) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    const size_t need = dgrad_workspace(sh);
+    if (workspace_bytes < need || (uintptr_t)workspace % 16) return CONV_ERR_WORKSPACE;
+    const int64_t dxb = sh.x_elems() * 4, db_ = sh.y_elems() * 2, wb = sh.w_elems() * 2;
+    if (overlaps(dx, dxb, dout, db_) || overlaps(dx, dxb, w, wb) || overlaps(dx, dxb, workspace, (int64_t)workspace_bytes) ||
+        overlaps(workspace, (int64_t)workspace_bytes, dout, db_) || overlaps(workspace, (int64_t)workspace_bytes, w, wb))
+        return CONV_ERR_ALIAS;
+    hipStream_t hs = (hipStream_t)stream;
+    uint16_t *wflip = (uint16_t *)workspace;
+    convfwd::launch_flip_weights_bf16(sh, w, wflip, hs);
+    if (hipGetLastError() != hipSuccess) return CONV_ERR_HIP;
+    const DgradPlan d = dgrad_plan(sh);
+    if (d.upsampled) return to_status(convfwd::launch_igemm_upsampled_bf16(d.sh, dout, wflip, nullptr, dx, hs));
+    // the forward problem on dout takes the forward's own route choice
+    if (pick_route(d.sh, CONV_ALGO_AUTO) == CONV_ALGO_VALU)
+        return to_status(convfwd::launch_valu_bf16(d.sh, dout, wflip, nullptr, dx, hs));
+    const size_t off = align_up((size_t)sh.w_elems() * 2);
+    return to_status(convfwd::launch_igemm_bf16(d.sh, dout, wflip, nullptr, dx, hs, (char *)workspace + off,
+                                                workspace_bytes - off));
+}
+
+size_t conv_bwd_weight_workspace_bytes(const conv_params_t *prm) {
+    if (!prm) return 0;
+    Shape sh;
+    if (shape_from_params(prm, sh) != CONV_OK) return 0;
+    return wgrad_workspace(sh);
+}
+
+conv_status_t conv_bwd_weight_bf16(const conv_params_t *prm, const uint16_t *x, const uint16_t *dout, float *dw,
+                                   float *db, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!prm || !x || !dout || !dw || !workspace) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    if (workspace_bytes < wgrad_workspace(sh) || (uintptr_t)workspace % 16) return CONV_ERR_WORKSPACE;
+    const int64_t xb = sh.x_elems() * 2, dob = sh.y_elems() * 2, dwb = sh.w_elems() * 4, dbb = (int64_t)sh.Co * 4;
+    const int64_t wsb = (int64_t)workspace_bytes;
+    const void *ins[3] = {x, dout, workspace};
+    const int64_t insb[3] = {xb, dob, wsb};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(dw, dwb, ins[i], insb[i]) || overlaps(db, dbb, ins[i], insb[i])) return CONV_ERR_ALIAS;
+    if (overlaps(dw, dwb, db, dbb) || overlaps(workspace, wsb, x, xb) || overlaps(workspace, wsb, dout, dob))
+        return CONV_ERR_ALIAS;
+    hipStream_t hs = (hipStream_t)stream;
+    if (db && convfwd::launch_bias_grad_bf16(sh, dout, db, hs) != hipSuccess) return CONV_ERR_HIP;
+    return to_status(convfwd::launch_wgrad_bf16(sh, x, dout, (float *)workspace, dw, hs));
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@ struct Shape {
     int Do, Ho, Wo;         // output spatial extents (Do = 1 in 2D)
     int dil = 1, dild = 1;  // dilation in H/W and in depth (dild = 1 in 2D)
     int G = 1;              // groups: divides C and Co
+    int ups = 1, upsd = 1;  // zero insertion of the input (data gradient of a strided
+                            // convolution; only the general kernel's upsampled mode reads these)
 
     __host__ __device__ int Cg() const { return C / G; }                                // input channels per group
     __host__ __device__ int Cog() const { return Co / G; }                              // output channels per group
@@ -55,6 +57,21 @@ hipError_t launch_valu_bf16(const Shape &sh, const uint16_t *x, const uint16_t *
 // Route-specific launchers behind the two dispatchers above.
 hipError_t launch_igemm_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                      const float *bias, float *y, hipStream_t st);
+// The general kernel over x seen through zero insertion: a virtual coordinate
+// v of the (D-1)*upsd+1 x (H-1)*ups+1 x (W-1)*ups+1 input reads x[v/ups] when
+// ups divides v, else 0.  sh.Do/Ho/Wo are set by the caller.
+hipError_t launch_igemm_upsampled_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, hipStream_t st);
+// Backward pieces (k_bwd.hip).  wflip: w (Co, C/G, taps) -> (C, Co/G, taps)
+// with the taps reversed, the weight of the data gradient as a convolution.
+void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wflip, hipStream_t st);
+// Weight gradient: partial sums over `splits` pixel ranges into part
+// (splits x Co x C/G*taps fp32), then their fixed-order sum into dw.
+int wgrad_splits(const Shape &sh);
+hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
+                             hipStream_t st);
+// db[oc] = sum of dout over images and positions (fixed order).
+hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *db, hipStream_t st);
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);
 // Workspace for the repacked weights of the 3x3 kernel (bytes).
 size_t conv3x3s1_workspace_bytes(const Shape &sh);

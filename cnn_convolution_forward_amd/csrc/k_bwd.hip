@@ -1,0 +1,286 @@
+// k_bwd.hip -- the backward pass's own kernels: the weight gradient on the
+// matrix cores, the bias gradient, and the weight flip that turns the data
+// gradient into a forward convolution.
+//
+// Gradients ("Hand-writing Conv2D", 5.1; "Why use matrix multiplication for
+// convolution", 3.3), for y = conv(x, w) + b and upstream gradient dout:
+//   db[oc]  = sum over (n, positions) of dout[n][oc];
+//   dW_row  = dout_col @ X_col^T : per group g, a GEMM of C_out/G x
+//             (C_in/G * K^dims) whose reduction runs over all N * H_out * W_out
+//             output positions;
+//   dx      = col2im(W_row^T @ dout_col) : the same as a convolution of dout
+//             (zero-inserted by the stride) with the weights transposed per
+//             group (C_in x C_out/G) and every tap reversed -- the flip below
+//             feeds that convolution to the forward kernels.
+//
+// Weight gradient kernel: the reduction over positions is long and the output
+// small (128 x 1152 for a 3x3, 128-channel layer), so the positions are cut
+// into `splits` ranges, one workgroup per (128-column tile, channel tile,
+// range, group).  Each writes its partial product to a workspace; a second
+// kernel adds the partials in a fixed order, so the result is bitwise
+// reproducible (no atomics).  Tiles: A = dout rows (C_out/G channels x 32
+// positions per stage, contiguous along positions), B = X_col^T gathered from
+// x with bounds checks (32 positions x 128 columns (ic, kd, kh, kw)), both
+// staged in LDS with the reduction contiguous, v_mfma_f32_32x32x16_bf16.
+#include "conv_internal.h"
+#include "mfma_common.h"
+
+namespace convfwd {
+namespace {
+
+constexpr int kBN = 128;      // X_col columns per tile
+constexpr int kBK = 32;       // positions per LDS stage
+constexpr int kLdk = kBK + 8; // 80-byte rows: 16-byte reads of 8 consecutive rows are conflict-free
+constexpr int kTargetBlocks = 512;
+
+__global__ __launch_bounds__(256)
+void flip_weights_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wf, int Cg, int Cog, int G,
+                         int taps, int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    // e indexes w as (oc = g*Cog + ocl, j, t)
+    const int t = (int)(e % taps);
+    const int64_t r = e / taps;
+    const int j = (int)(r % Cg);
+    const int oc = (int)(r / Cg);
+    const int g = oc / Cog, ocl = oc - g * Cog;
+    wf[(((int64_t)g * Cg + j) * Cog + ocl) * taps + (taps - 1 - t)] = w[e];
+}
+
+template <int BM>
+__global__ __launch_bounds__(256)
+void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
+                  float *__restrict__ part, int64_t P, int Kg, int64_t chunk, int splits, int g0, int a_vec) {
+    constexpr int MI = BM / 64;
+    __shared__ __align__(16) uint16_t As[2][BM][kLdk];
+    __shared__ __align__(16) uint16_t Bs[2][kBN][kLdk];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * kBN;                      // first X_col column
+    const int m0 = blockIdx.y * BM;                       // first channel inside the group
+    const int split = (int)blockIdx.z % splits;
+    const int grp = g0 + (int)blockIdx.z / splits;
+    const int Cog = sh.Co / sh.G, Cg = sh.C / sh.G;
+    const int64_t k_begin = (int64_t)split * chunk;
+    const int64_t k_end = k_begin + chunk < P ? k_begin + chunk : P;
+    const int64_t plane = sh.out_plane();
+    const int64_t HW = (int64_t)sh.H * sh.W;
+
+    // B loader: column bj of the tile, position quads bkq and bkq + 2
+    const int bj = tid & (kBN - 1), bkq = tid >> 7;
+    const int jcol = n0 + bj;
+    const bool jvalid = jcol < Kg;
+    int ic = 0, kd = 0, kh = 0, kw = 0;
+    if (jvalid) {
+        const int taps = sh.Kd * sh.K * sh.K;
+        ic = jcol / taps;
+        int rem = jcol - ic * taps;
+        kd = rem / (sh.K * sh.K);
+        rem -= kd * sh.K * sh.K;
+        kh = rem / sh.K;
+        kw = rem - kh * sh.K;
+    }
+    const int dz = kd * sh.dild - sh.pd, dy = kh * sh.dil - sh.p, dxo = kw * sh.dil - sh.p;
+    const uint16_t *xg = x + (int64_t)(grp * Cg + ic) * sh.in_plane();    // channel of image 0
+    const int64_t img_stride = (int64_t)sh.C * sh.in_plane();
+    const uint16_t *dg = dout + (int64_t)grp * Cog * plane;                // channel g*Cog of image 0
+    const int64_t dimg = (int64_t)sh.Co * plane;
+
+    uint4 a_reg[MI], b_reg[2];
+    auto load_stage = [&](int64_t k0) {
+        // A: dout[n][oc][q] for 8 consecutive positions of row m
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int u = tid + 256 * i;
+            const int row = u >> 2, kq = u & 3;
+            const int oc = m0 + row;
+            const int64_t kk = k0 + kq * 8;
+            if (a_vec && oc < Cog && kk + 8 <= k_end) {
+                const int64_t n = kk / plane, q = kk - n * plane;
+                a_reg[i] = *reinterpret_cast<const uint4 *>(dg + n * dimg + (int64_t)oc * plane + q);
+            } else {
+                uint16_t v[8];
+                int64_t n = kk / plane, q = kk - n * plane;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] = (oc < Cog && kk + e < k_end) ? dg[n * dimg + (int64_t)oc * plane + q] : (uint16_t)0;
+                    if (++q == plane) { q = 0; ++n; }
+                }
+                a_reg[i] = pack8(v);
+            }
+        }
+        // B: x at the tap of column jcol for 8 consecutive positions
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t kk = k0 + (bkq + 2 * i) * 8;
+            uint16_t v[8];
+            int64_t t = kk;
+            int ow = (int)(t % sh.Wo); t /= sh.Wo;
+            int oh = (int)(t % sh.Ho); t /= sh.Ho;
+            int od = (int)(t % sh.Do);
+            int64_t n = t / sh.Do;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint16_t val = 0;
+                if (jvalid && kk + e < k_end) {
+                    const int id = od * sh.sd + dz, ih = oh * sh.s + dy, iw = ow * sh.s + dxo;
+                    if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W)
+                        val = xg[n * img_stride + (int64_t)id * HW + (int64_t)ih * sh.W + iw];
+                }
+                v[e] = val;
+                if (++ow == sh.Wo) { ow = 0; if (++oh == sh.Ho) { oh = 0; if (++od == sh.Do) { od = 0; ++n; } } }
+            }
+            b_reg[i] = pack8(v);
+        }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int u = tid + 256 * i;
+            *reinterpret_cast<uint4 *>(&As[buf][u >> 2][(u & 3) * 8]) = a_reg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<uint4 *>(&Bs[buf][bj][(bkq + 2 * i) * 8]) = b_reg[i];
+    };
+
+    f32x16_t acc[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = k_end > k_begin ? (int)((k_end - k_begin + kBK - 1) / kBK) : 0;
+    if (nk > 0) {
+        load_stage(k_begin);
+        store_stage(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_stage(k_begin + (int64_t)(kt + 1) * kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            uint4 a[MI], b[2];
+            const int kof = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                a[i] = *reinterpret_cast<const uint4 *>(&As[buf][wm * (BM / 2) + i * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const uint4 *>(&Bs[buf][wn * 64 + j * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // partial[split][oc][jcol]: 32 lanes on 32 consecutive columns
+    float *pp = part + (int64_t)split * sh.Co * Kg;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (col >= Kg) continue;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ocl = m0 + wm * (BM / 2) + i * 32 + mfma32_row(r, lane);
+                if (ocl < Cog) pp[(int64_t)(grp * Cog + ocl) * Kg + col] = acc[i][j][r];
+            }
+    }
+}
+
+// dw[e] = sum over splits, in order, of part[split][e].
+__global__ __launch_bounds__(256)
+void sum_splits_kernel(const float *__restrict__ part, float *__restrict__ dw, int64_t n, int splits) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    float s = 0.f;
+    for (int i = 0; i < splits; ++i) s += part[(int64_t)i * n + e];
+    dw[e] = s;
+}
+
+// db[oc]: one workgroup per channel; each thread sums a strided subset in
+// order, then a fixed-shape tree in LDS.
+__global__ __launch_bounds__(256)
+void bias_grad_kernel(const uint16_t *__restrict__ dout, float *__restrict__ db, int N, int Co, int64_t plane) {
+    __shared__ float red[256];
+    const int oc = blockIdx.x, tid = threadIdx.x;
+    float s = 0.f;
+    for (int n = 0; n < N; ++n) {
+        const uint16_t *p = dout + ((int64_t)n * Co + oc) * plane;
+        for (int64_t q = tid; q < plane; q += 256) s += bf16_to_f32(p[q]);
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    if (tid == 0) db[oc] = red[0];
+}
+
+}  // namespace
+
+void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wflip, hipStream_t st) {
+    const int64_t total = sh.w_elems();
+    hipLaunchKernelGGL(flip_weights_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, w, wflip,
+                       sh.Cg(), sh.Cog(), sh.G, (int)sh.taps(), total);
+}
+
+int wgrad_splits(const Shape &sh) {
+    const int64_t P = sh.pixels();
+    const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
+    const int bm = Cog > 64 ? 128 : 64;
+    const int64_t tiles = (int64_t)((Kg + kBN - 1) / kBN) * ((Cog + bm - 1) / bm) * sh.G;
+    int64_t s = (kTargetBlocks + tiles - 1) / tiles;
+    const int64_t most = (P + 8 * kBK - 1) / (8 * kBK);        // at least 8 stages per range
+    if (s > most) s = most;
+    if (s < 1) s = 1;
+    if (s > 256) s = 256;
+    return (int)s;
+}
+
+hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
+                             hipStream_t st) {
+    const int64_t P = sh.pixels();
+    const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
+    const int splits = wgrad_splits(sh);
+    const int64_t chunk = ((P + splits - 1) / splits + kBK - 1) / kBK * kBK;
+    const int64_t plane = sh.out_plane();
+    const int a_vec = (plane % 8 == 0) && ((uintptr_t)dout % 16 == 0);
+    const unsigned gx = (unsigned)((Kg + kBN - 1) / kBN);
+    const int gmax = 65535 / splits;                    // groups per launch (grid z = splits * groups)
+    for (int g0 = 0; g0 < sh.G; g0 += gmax) {
+        const int ng = sh.G - g0 < gmax ? sh.G - g0 : gmax;
+        if (Cog > 64) {
+            dim3 grid(gx, (unsigned)((Cog + 127) / 128), (unsigned)(splits * ng));
+            hipLaunchKernelGGL((wgrad_kernel<128>), grid, dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits,
+                               g0, a_vec);
+        } else {
+            dim3 grid(gx, (unsigned)((Cog + 63) / 64), (unsigned)(splits * ng));
+            hipLaunchKernelGGL((wgrad_kernel<64>), grid, dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits,
+                               g0, a_vec);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t n = sh.w_elems();
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, n, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *db, hipStream_t st) {
+    hipLaunchKernelGGL(bias_grad_kernel, dim3((unsigned)sh.Co), dim3(256), 0, st, dout, db, sh.N, sh.Co,
+                       sh.out_plane());
+    return hipGetLastError();
+}
+
+}  // namespace convfwd

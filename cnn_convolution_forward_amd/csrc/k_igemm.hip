@@ -20,6 +20,11 @@
 // order: the reshape + axis swap of "Why use matrix multiplication for
 // convolution", 3.2, fused into the store.
 //
+// A third flavour serves the data gradient of a strided convolution: the
+// input it gathers is dout seen through zero insertion (ups - 1 zeros between
+// neighbours, the transposed convolution), so a virtual coordinate v reads
+// dout[v / ups] when v % ups == 0 and 0 otherwise.
+//
 // This is the route for every shape the specialised kernels do not cover.
 #include "conv_internal.h"
 #include "mfma_common.h"
@@ -31,7 +36,9 @@ constexpr int kBN = 128;      // pixels per block
 constexpr int kBK = 32;       // k per LDS stage
 constexpr int kLdk = kBK + 8; // padded k stride in LDS: 80-byte rows keep 16-byte reads conflict-free
 
-template <int BM, bool kExplicit>
+enum { kImplicit = 0, kExplicit = 1, kUpsampled = 2 };
+
+template <int BM, int kMode>
 __global__ __launch_bounds__(256)
 void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint16_t *__restrict__ w,
                           const float *__restrict__ bias, float *__restrict__ y,
@@ -56,7 +63,7 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
     const bool pvalid = jp < P;
     int id0 = 0, ih0 = 0, iw0 = 0;
     const uint16_t *xn = src;
-    if (!kExplicit && pvalid) {
+    if (kMode != kExplicit && pvalid) {
         int64_t t = jp;
         int ow = (int)(t % sh.Wo); t /= sh.Wo;
         int oh = (int)(t % sh.Ho); t /= sh.Ho;
@@ -96,7 +103,7 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
             int kq = bkq + 2 * i;
             int k = k0 + kq * 8;
             uint16_t v[8];
-            if (kExplicit) {
+            if (kMode == kExplicit) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     v[e] = (pvalid && k + e < Kg) ? src[((int64_t)grp * Kg + k + e) * P + jp] : (uint16_t)0;
@@ -109,8 +116,17 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
                     uint16_t val = 0;
                     if (pvalid && ic < Cg) {
                         int id = id0 + kd * sh.dild, ih = ih0 + kh * sh.dil, iw = iw0 + kw * sh.dil;
-                        if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W)
+                        if (kMode == kUpsampled) {
+                            // virtual coordinates over the zero-inserted input
+                            const bool on = 0 <= id && id < (sh.D - 1) * sh.upsd + 1 && id % sh.upsd == 0 &&
+                                            0 <= ih && ih < (sh.H - 1) * sh.ups + 1 && ih % sh.ups == 0 &&
+                                            0 <= iw && iw < (sh.W - 1) * sh.ups + 1 && iw % sh.ups == 0;
+                            if (on)
+                                val = xn[((int64_t)ic * sh.D + id / sh.upsd) * HW + (int64_t)(ih / sh.ups) * sh.W +
+                                         iw / sh.ups];
+                        } else if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W) {
                             val = xn[((int64_t)ic * sh.D + id) * HW + (int64_t)ih * sh.W + iw];
+                        }
                     }
                     v[e] = val;
                     if (++kw == sh.K) { kw = 0; if (++kh == sh.K) { kh = 0; if (++kd == sh.Kd) { kd = 0; ++ic; } } }
@@ -183,7 +199,7 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
     }
 }
 
-template <bool kExplicit>
+template <int kMode>
 hipError_t launch_generic(const Shape &sh, const uint16_t *src, const uint16_t *w,
                           const float *bias, float *y, hipStream_t st) {
     const int64_t P = sh.pixels();
@@ -197,11 +213,11 @@ hipError_t launch_generic(const Shape &sh, const uint16_t *src, const uint16_t *
         const unsigned gz = (unsigned)(sh.G - g0 < kMaxGridZ ? sh.G - g0 : kMaxGridZ);
         if (Cog > 64) {
             dim3 grid(gx, (unsigned)((Cog + 127) / 128), gz);
-            hipLaunchKernelGGL((igemm_generic_kernel<128, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
+            hipLaunchKernelGGL((igemm_generic_kernel<128, kMode>), grid, dim3(256), 0, st, sh, src, w,
                                bias, y, P, Kg, w_vec, g0);
         } else {
             dim3 grid(gx, (unsigned)((Cog + 63) / 64), gz);
-            hipLaunchKernelGGL((igemm_generic_kernel<64, kExplicit>), grid, dim3(256), 0, st, sh, src, w,
+            hipLaunchKernelGGL((igemm_generic_kernel<64, kMode>), grid, dim3(256), 0, st, sh, src, w,
                                bias, y, P, Kg, w_vec, g0);
         }
         const hipError_t e = hipGetLastError();
@@ -214,12 +230,17 @@ hipError_t launch_generic(const Shape &sh, const uint16_t *src, const uint16_t *
 
 hipError_t launch_igemm_generic_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                                      const float *bias, float *y, hipStream_t st) {
-    return launch_generic<false>(sh, x, w, bias, y, st);
+    return launch_generic<kImplicit>(sh, x, w, bias, y, st);
 }
 
 hipError_t launch_gemm_xcol_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol,
                                  const float *bias, float *y, hipStream_t st) {
-    return launch_generic<true>(sh, xcol, w, bias, y, st);
+    return launch_generic<kExplicit>(sh, xcol, w, bias, y, st);
+}
+
+hipError_t launch_igemm_upsampled_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias,
+                                       float *y, hipStream_t st) {
+    return launch_generic<kUpsampled>(sh, x, w, bias, y, st);
 }
 
 }  // namespace convfwd

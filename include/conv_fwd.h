@@ -267,6 +267,46 @@ CONV_API conv_status_t conv_fwd_explicit_bf16(const conv_params_t *params, const
                                               const uint16_t *w, const float *bias, float *y,
                                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- backward: gradients of y = conv(x, w) + b ----------------------------
+ *
+ * With upstream gradient dout (the shape of y) ("Hand-writing Conv2D", 5.1;
+ * "Why use matrix multiplication for convolution", 3.3):
+ *     db[oc]             = sum over n and output positions of dout[n][oc]
+ *     dw[oc][j][taps]    = sum over n, output positions of dout[n][oc][o] *
+ *                          x[n][g*C_in/G + j][o*s + k*d - p]   (dW_row = dout_col @ X_col^T)
+ *     dx[n][ic][i]       = sum over the (oc, o, k) whose tap k of output o read
+ *                          input i of w[oc][j][k] * dout[n][oc][o]  (col2im(W_row^T @ dout_col))
+ * for the general problem of conv_params_t (dilation, groups, 2D/3D).  x, w and
+ * dout are bf16 bits; dx, dw, db are fp32; accumulation is fp32.  Results are
+ * bitwise reproducible (fixed summation order, no atomics).  Errors as for
+ * conv_fwd_bf16, plus CONV_ERR_WORKSPACE when the workspace is missing, too
+ * small or not 16-byte aligned, and CONV_ERR_ALIAS when an output overlaps an
+ * input or the workspace. */
+
+/* Device workspace for conv_bwd_data_bf16: the flipped weights (and, for 3x3
+ * stride-1 layers, their per-stage packing); 0 on invalid parameters. */
+CONV_API size_t conv_bwd_data_workspace_bytes(const conv_params_t *params);
+
+/* dx (N, C_in, [D,] H, W) from dout and w.  The data gradient is computed as
+ * a forward convolution of dout with w transposed per group (C_in x C_out/G)
+ * and every tap reversed, pad d(K-1) - p, on the forward kernels; a strided
+ * layer reads dout through zero insertion (the transposed convolution) on the
+ * general implicit-GEMM kernel.  The workspace is overwritten. */
+CONV_API conv_status_t conv_bwd_data_bf16(const conv_params_t *params, const uint16_t *dout, const uint16_t *w,
+                                          float *dx, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device workspace for conv_bwd_weight_bf16: fp32 partial sums of dw over
+ * ranges of output positions; 0 on invalid parameters. */
+CONV_API size_t conv_bwd_weight_workspace_bytes(const conv_params_t *params);
+
+/* dw (C_out, C_in/G, K, K[, K]) and, when db is not NULL, db (C_out) from x
+ * and dout.  dw is reduced over output positions in ranges on the matrix
+ * cores, then the ranges are added in a fixed order.  The workspace is
+ * overwritten. */
+CONV_API conv_status_t conv_bwd_weight_bf16(const conv_params_t *params, const uint16_t *x, const uint16_t *dout,
+                                            float *dw, float *db, void *workspace, size_t workspace_bytes,
+                                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

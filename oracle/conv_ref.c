@@ -493,6 +493,92 @@ int oracle_conv_backward(int ndim, const double *x, const double *w, const doubl
     return 0;
 }
 
+/* The gradients at chosen points, in gather form, for checks at sizes where
+ * the scatter loop above is too slow.  Same definitions [Hand-writing Conv2D,
+ * 5.1], each element summed on its own:
+ *   dw at flat index idx of (Co, C/G, Kz, K, K): sum over n and every output
+ *     position o of dout[n][oc][o] * x[n][ic][o*s + k*d - p] (in range);
+ *   dx at flat index idx of (N, C, Dd, H, W): sum over the group's output
+ *     channels and the taps k for which (i + p - k*d) is a multiple of s and
+ *     o = (i + p - k*d)/s is an output position, of w[oc][j][k] * dout[n][oc][o].
+ * S_* as in oracle_conv_backward.  Returns -1 on a bad shape or index. */
+int oracle_conv_backward_points(int ndim, const double *x, const double *w, const double *dout,
+                                const int64_t *dw_idx, int64_t n_dw, double *dw, double *S_dw,
+                                const int64_t *dx_idx, int64_t n_dx, double *dx, double *S_dx,
+                                int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                                int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, Co, K, s, p, d, G) != 0) return -1;
+    const int64_t Cg = C / G, Cog = Co / G;
+    const int64_t nw = Co * Cg * g.Kz * K * K, nx = N * C * g.Dd * H * W;
+    for (int64_t i = 0; i < n_dw; ++i) if (dw_idx[i] < 0 || dw_idx[i] >= nw) return -1;
+    for (int64_t i = 0; i < n_dx; ++i) if (dx_idx[i] < 0 || dx_idx[i] >= nx) return -1;
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < n_dw; ++i) {
+        int64_t r = dw_idx[i];
+        const int64_t kw = r % K; r /= K;
+        const int64_t kh = r % K; r /= K;
+        const int64_t kz = r % g.Kz; r /= g.Kz;
+        const int64_t j = r % Cg;
+        const int64_t oc = r / Cg;
+        const int64_t ic = (oc / Cog) * Cg + j;
+        double acc = 0.0, S = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+          for (int64_t od = 0; od < g.Do; ++od) {
+            const int64_t iz = od * g.sz + kz * g.dz - g.pz;
+            if (iz < 0 || iz >= g.Dd) continue;
+            for (int64_t oh = 0; oh < g.Ho; ++oh) {
+              const int64_t iy = oh * s + kh * d - p;
+              if (iy < 0 || iy >= H) continue;
+              for (int64_t ow = 0; ow < g.Wo; ++ow) {
+                const int64_t ix = ow * s + kw * d - p;
+                if (ix < 0 || ix >= W) continue;
+                const double t = dout[(((n * Co + oc) * g.Do + od) * g.Ho + oh) * g.Wo + ow] *
+                                 x[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix];
+                acc += t;
+                S += fabs(t);
+              }
+            }
+          }
+        dw[i] = acc;
+        if (S_dw) S_dw[i] = S;
+    }
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_dx; ++i) {
+        int64_t r = dx_idx[i];
+        const int64_t ix = r % W; r /= W;
+        const int64_t iy = r % H; r /= H;
+        const int64_t iz = r % g.Dd; r /= g.Dd;
+        const int64_t ic = r % C;
+        const int64_t n = r / C;
+        const int64_t grp = ic / Cg, j = ic % Cg;
+        double acc = 0.0, S = 0.0;
+        for (int64_t ocl = 0; ocl < Cog; ++ocl) {
+          const int64_t oc = grp * Cog + ocl;
+          for (int64_t kz = 0; kz < g.Kz; ++kz) {
+            const int64_t tz = iz + g.pz - kz * g.dz;
+            if (tz < 0 || tz % g.sz != 0 || tz / g.sz >= g.Do) continue;
+            for (int64_t kh = 0; kh < K; ++kh) {
+              const int64_t ty = iy + p - kh * d;
+              if (ty < 0 || ty % s != 0 || ty / s >= g.Ho) continue;
+              for (int64_t kw = 0; kw < K; ++kw) {
+                const int64_t tx = ix + p - kw * d;
+                if (tx < 0 || tx % s != 0 || tx / s >= g.Wo) continue;
+                const double t = w[(((oc * Cg + j) * g.Kz + kz) * K + kh) * K + kw] *
+                                 dout[(((n * Co + oc) * g.Do + tz / g.sz) * g.Ho + ty / s) * g.Wo + tx / s];
+                acc += t;
+                S += fabs(t);
+              }
+            }
+          }
+        }
+        dx[i] = acc;
+        if (S_dx) S_dx[i] = S;
+    }
+    return 0;
+}
+
 /* col2im, the adjoint of oracle_im2col_dilated [Why use matrix multiplication
  * for convolution, 3.3]: every entry of col (C*K^ndim rows, N*Do*Ho*Wo
  * columns, the im2col layout) is added onto the input position its tap read;

@@ -78,6 +78,9 @@ def lib():
         L.oracle_im2col_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_conv_backward.restype = ctypes.c_int
         L.oracle_conv_backward.argtypes = [ctypes.c_int] + [_dp] * 9 + [_i64] * 11
+        L.oracle_conv_backward_points.restype = ctypes.c_int
+        L.oracle_conv_backward_points.argtypes = ([ctypes.c_int, _dp, _dp, _dp, ctypes.c_void_p, _i64, _dp, _dp,
+                                                   ctypes.c_void_p, _i64, _dp, _dp] + [_i64] * 11)
         L.oracle_col2im_dilated.restype = ctypes.c_int
         L.oracle_col2im_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_num_threads.restype = ctypes.c_int
@@ -314,6 +317,23 @@ def conv_backward(x, w, dout, stride=1, pad=0, dilation=1, groups=1):
     if rc != 0:
         raise ValueError("oracle_conv_backward rejected the shape")
     return (dx, dw, db), (Sdx, Sdw, Sdb)
+
+
+def conv_backward_points(x, w, dout, stride, pad, dilation, groups, dw_idx, dx_idx):
+    """dw and dx (with S) at flat indices only, each summed in gather form
+    [Hand-writing Conv2D, 5.1]; for checks at full size."""
+    x, w, dout = decode(x), decode(w), decode(dout)
+    ndim, N, C, D, H, W, Co, K = _general_dims(x, w, groups)
+    dw_idx = np.ascontiguousarray(dw_idx, dtype=np.int64)
+    dx_idx = np.ascontiguousarray(dx_idx, dtype=np.int64)
+    dw, Sdw = np.empty(dw_idx.shape), np.empty(dw_idx.shape)
+    dx, Sdx = np.empty(dx_idx.shape), np.empty(dx_idx.shape)
+    rc = lib().oracle_conv_backward_points(ndim, _p(x), _p(w), _p(dout), dw_idx.ctypes.data, dw_idx.size, _p(dw),
+                                           _p(Sdw), dx_idx.ctypes.data, dx_idx.size, _p(dx), _p(Sdx),
+                                           N, C, D, H, W, Co, K, stride, pad, dilation, groups)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward_points rejected the request")
+    return (dw, Sdw), (dx, Sdx)
 
 
 def col2im_dilated(col, x_shape, K, stride, pad, dilation=1):

@@ -214,3 +214,26 @@ def test_general_xcol_bytes_and_explicit_validation():
     assert B.conv_im2col_bf16(prm, None, Y, None) == 1
     assert B.conv_im2col_bf16(prm, X, X + 2, None) == 5
     assert B.conv_im2col_bf16(_gp(dilation=-1), X, Y, None) == 2
+
+
+def test_backward_validation():
+    prm = _gp()                       # (2,8,9,11), (16,2,3,3), s1 p1 d2 G4
+    nd, nw = B.conv_bwd_data_workspace_bytes(prm), B.conv_bwd_weight_workspace_bytes(prm)
+    assert nd >= 16 * 2 * 9 * 2 and nw >= 16 * 2 * 9 * 4 and nw % (16 * 2 * 9 * 4) == 0
+    assert B.conv_bwd_data_workspace_bytes(None) == 0 and B.conv_bwd_weight_workspace_bytes(_gp(groups=3)) == 0
+    DO = X + 0x01000000
+    bd = lambda prm=prm, dout=DO, w=Wp, dx=Y, ws=WS, nb=nd: B.conv_bwd_data_bf16(prm, dout, w, dx, ws, nb, None)
+    assert bd(prm=None) == 1 and bd(dout=None) == 1 and bd(dx=None) == 1 and bd(ws=None) == 1
+    assert bd(prm=_gp(dilation=0)) == 2
+    assert bd(nb=nd - 1) == 6
+    assert bd(ws=WS + 8) == 6
+    assert bd(dx=DO + 64) == 5            # dx over dout
+    assert bd(ws=Y + 64) == 5             # workspace over dx
+    bw = lambda prm=prm, x=X, dout=DO, dw=Y, db=BIAS, ws=WS, nb=nw: B.conv_bwd_weight_bf16(prm, x, dout, dw, db, ws, nb, None)
+    assert bw(prm=None) == 1 and bw(x=None) == 1 and bw(dout=None) == 1 and bw(dw=None) == 1 and bw(ws=None) == 1
+    assert bw(prm=_gp(groups=0)) == 2
+    assert bw(nb=nw - 4) == 6
+    assert bw(dw=X + 2) == 5              # dw over x
+    assert bw(db=DO) == 5                 # db over dout
+    assert bw(db=Y + 8) == 5              # db over dw
+    assert bw(ws=DO + 32) == 5            # workspace over dout

@@ -1,0 +1,122 @@
+"""GPU parity for the backward pass (conv_bwd_data_bf16, conv_bwd_weight_bf16)
+against the oracle's backward loop and its gather-form points.
+
+Acceptance per element, in fp64: |gpu - ref| <= 1e-3 * S with S the sum of
+|products| of that element (bf16 inputs, fp32 accumulation, as the forward
+contract); integer-valued inputs must match bit for bit.  Paths covered:
+stride-1 data gradient through the forward kernels (the column-group 3x3
+kernel, the depthwise kernel, the general implicit GEMM), the zero-inserted
+(strided) data gradient, a pad beyond the dilated span, groups, dilation, 3D,
+and the split weight-gradient kernel with ragged ranges.  The full-size 3x3
+layer is checked on sampled gradient entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cnn_convolution_forward_amd import binding as B
+from cnn_convolution_forward_amd import synth
+from parity import compare, dev
+
+pytestmark = pytest.mark.gpu
+TAU = 1e-3
+
+
+def _inputs(ndim, N, C, sp, Co, K, s, p, d, G, seed, integer=False):
+    wl = synth.Workload("bwd", ndim, N, C, tuple(sp), Co, K, s, p, "bf16", "normal", seed, dilation=d, groups=G)
+    t = synth.make_inputs(wl, integer=integer)
+    rng = np.random.default_rng(seed + 1000)
+    if integer:
+        dout = rng.integers(-2, 3, size=wl.y_shape).astype(np.float32)
+    else:
+        dout = rng.standard_normal(size=wl.y_shape, dtype=np.float32)
+    return wl, t.x, t.w, synth.f32_to_bf16_bits(dout)
+
+
+def _gpu(wl, x, w, dout):
+    xt, wt, dt = dev(x, None), dev(w, None), dev(dout, None)
+    dx = torch.full(wl.x_shape, float("nan"), dtype=torch.float32, device="cuda")
+    dw = torch.full(wl.w_shape, float("nan"), dtype=torch.float32, device="cuda")
+    db = torch.full((wl.C_out,), float("nan"), dtype=torch.float32, device="cuda")
+    B.conv_backward(xt, wt, dt, wl.stride, wl.pad, wl.dilation, wl.groups, out=(dx, dw, db))
+    torch.cuda.synchronize()
+    return dx.cpu().numpy(), dw.cpu().numpy(), db.cpu().numpy()
+
+
+SMALL = [
+    # (ndim, N, C, spatial, Co, K, s, p, d, G)
+    (2, 2, 3, (8, 10), 4, 3, 1, 1, 1, 1),        # the page's check shape
+    (2, 2, 128, (16, 32), 32, 3, 1, 1, 1, 1),     # dx on the column-group 3x3 kernel (C_out' = 128)
+    (2, 3, 20, (13, 17), 70, 3, 1, 1, 1, 1),      # ragged channels: general kernel, several tiles
+    (2, 2, 16, (15, 14), 24, 3, 2, 1, 1, 1),      # stride 2: zero-inserted dout
+    (2, 1, 12, (11, 13), 18, 3, 3, 2, 2, 3),      # stride 3, dilation 2, groups 3
+    (2, 1, 8, (9, 9), 8, 3, 1, 3, 1, 1),          # pad 3 > K - 1: negative pad of the flipped conv
+    (2, 2, 32, (12, 12), 32, 3, 1, 1, 1, 32),     # depthwise: dx on the depthwise kernel
+    (2, 1, 8, (10, 12), 16, 5, 1, 4, 2, 2),       # K 5, dilation 2, groups 2
+    (2, 2, 40, (7, 6), 64, 1, 1, 0, 1, 1),        # pointwise
+    (3, 2, 4, (5, 6, 7), 6, 3, 1, 1, 1, 2),       # 3D, groups
+    (3, 1, 3, (6, 5, 7), 8, 3, 2, 2, 2, 1),       # 3D, stride 2, dilation 2
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:3] + tuple(c[3]) + c[4:])))
+def test_backward_small(case):
+    wl, x, w, dout = _inputs(*case, seed=sum(case[3]) + case[4])
+    dx, dw, db = _gpu(wl, x, w, dout)
+    (rdx, rdw, rdb), (Sdx, Sdw, Sdb) = oracle.conv_backward(x, w, dout, wl.stride, wl.pad, wl.dilation, wl.groups)
+    compare(dx, rdx, Sdx, TAU, label="dx %s" % (case,))
+    compare(dw, rdw, Sdw, TAU, label="dw %s" % (case,))
+    compare(db, rdb, Sdb, TAU, label="db %s" % (case,))
+
+
+@pytest.mark.parametrize("case", SMALL[:6] + SMALL[9:], ids=lambda c: "x".join(map(str, c[:3] + tuple(c[3]) + c[4:])))
+def test_backward_integer_exact(case):
+    wl, x, w, dout = _inputs(*case, seed=7, integer=True)
+    dx, dw, db = _gpu(wl, x, w, dout)
+    (rdx, rdw, rdb), _ = oracle.conv_backward(x, w, dout, wl.stride, wl.pad, wl.dilation, wl.groups)
+    compare(dx, rdx, None, 0, exact=True, label="dx %s" % (case,))
+    compare(dw, rdw, None, 0, exact=True, label="dw %s" % (case,))
+    compare(db, rdb, None, 0, exact=True, label="db %s" % (case,))
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_backward_full_3x3_layer_sampled(integer):
+    """x (64,128,56,56), w (128,128,3,3), s1 p1: every db entry, 256 dw entries
+    (each a sum over 200704 positions) and 4000 dx entries."""
+    wl = synth.WORKLOADS["conv3x3_bf16"]
+    t = synth.make_inputs(wl, integer=integer)
+    rng = np.random.default_rng(99)
+    if integer:
+        dout = synth.f32_to_bf16_bits(rng.integers(-2, 3, size=wl.y_shape).astype(np.float32))
+    else:
+        dout = synth.f32_to_bf16_bits(rng.standard_normal(size=wl.y_shape, dtype=np.float32))
+    dx, dw, db = _gpu(wl, t.x, t.w, dout)
+    iw = rng.choice(dw.size, size=256, replace=False)
+    ix = rng.choice(dx.size, size=4000, replace=False)
+    (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(t.x, t.w, dout, 1, 1, 1, 1, iw, ix)
+    tau = 0 if integer else TAU
+    compare(dw.reshape(-1)[iw], pdw, pSdw, tau, exact=integer, label="dw")
+    compare(dx.reshape(-1)[ix], pdx, pSdx, tau, exact=integer, label="dx")
+    d64 = synth.bf16_bits_to_f32(dout).astype(np.float64)
+    rdb = d64.sum(axis=(0, 2, 3))
+    compare(db, rdb, np.abs(d64).sum(axis=(0, 2, 3)), tau, exact=integer, label="db")
+
+
+def test_backward_deterministic():
+    wl, x, w, dout = _inputs(2, 4, 64, (28, 28), 64, 3, 1, 1, 1, 1, seed=5)
+    a = _gpu(wl, x, w, dout)
+    b = _gpu(wl, x, w, dout)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_backward_without_db():
+    wl, x, w, dout = _inputs(2, 2, 8, (9, 9), 8, 3, 1, 1, 1, 2, seed=3)
+    xt, wt, dt = dev(x, None), dev(w, None), dev(dout, None)
+    dx, dw, db = B.conv_backward(xt, wt, dt, 1, 1, 1, 2, with_db=False)
+    torch.cuda.synchronize()
+    assert db is None
+    (rdx, rdw, _), (Sdx, Sdw, _) = oracle.conv_backward(x, w, dout, 1, 1, 1, 2)
+    compare(dw.cpu().numpy(), rdw, Sdw, TAU, label="dw")
+    compare(dx.cpu().numpy(), rdx, Sdx, TAU, label="dx")

@@ -11,7 +11,8 @@ Each check ties the gradients to something other than the backward loop itself:
   * the im2col form of the page "Why use matrix multiplication for
     convolution" (3.3): dW_row = dout_col @ X_col^T and dx =
     col2im(W_row^T @ dout_col), with im2col and matmul pinned elsewhere;
-  * col2im as the adjoint of im2col, and against torch.nn.functional.fold.
+  * col2im as the adjoint of im2col, and against torch.nn.functional.fold;
+  * the gather (point) form equals the scatter loop element for element.
 
 A plausible mistake (dx overwritten instead of accumulated, dW built from w,
 db summed over one image, the stride dropped from the scatter, the group
@@ -187,3 +188,22 @@ def test_backward_rejects_bad_dout():
     x, w = np.zeros((1, 2, 5, 5)), np.zeros((3, 2, 3, 3))
     with pytest.raises(ValueError):
         oracle.conv_backward(x, w, np.zeros((1, 3, 4, 5)), 1, 1)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:2] + c[2:3] + tuple(c[3]) + c[4:])))
+def test_gather_points_equal_scatter(case):
+    """The point (gather) form sums the same terms as the scatter loop: with
+    integer data every point matches exactly, S included."""
+    ndim, N, C, sp, Co, K, s, p, d, G = case
+    rng = np.random.default_rng(21 + Co)
+    x, w, _, dout = _case(ndim, N, C, sp, Co, K, s, p, d, G, rng, integer=True)
+    (dx, dw, db), (Sdx, Sdw, Sdb) = oracle.conv_backward(x, w, dout, s, p, d, G)
+    iw = np.arange(dw.size)
+    ix = np.arange(dx.size)
+    (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(x, w, dout, s, p, d, G, iw, ix)
+    np.testing.assert_array_equal(pdw, dw.reshape(-1))
+    np.testing.assert_array_equal(pSdw, Sdw.reshape(-1))
+    np.testing.assert_array_equal(pdx, dx.reshape(-1))
+    np.testing.assert_array_equal(pSdx, Sdx.reshape(-1))
+    with pytest.raises(ValueError):
+        oracle.conv_backward_points(x, w, dout, s, p, d, G, np.array([dw.size]), np.array([0]))
