@@ -534,10 +534,10 @@ int oracle_conv_backward_points(int ndim, const double *x, const double *w, cons
               for (int64_t ow = 0; ow < g.Wo; ++ow) {
                 const int64_t ix = ow * s + kw * d - p;
                 if (ix < 0 || ix >= W) continue;
-                const double t = dout[(((n * Co + oc) * g.Do + od) * g.Ho + oh) * g.Wo + ow] *
+                const double term = dout[(((n * Co + oc) * g.Do + od) * g.Ho + oh) * g.Wo + ow] *
                                  x[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix];
-                acc += t;
-                S += fabs(t);
+                acc += term;
+                S += fabs(term);
               }
             }
           }
@@ -565,10 +565,10 @@ int oracle_conv_backward_points(int ndim, const double *x, const double *w, cons
               for (int64_t kw = 0; kw < K; ++kw) {
                 const int64_t tx = ix + p - kw * d;
                 if (tx < 0 || tx % s != 0 || tx / s >= g.Wo) continue;
-                const double t = w[(((oc * Cg + j) * g.Kz + kz) * K + kh) * K + kw] *
+                const double term = w[(((oc * Cg + j) * g.Kz + kz) * K + kh) * K + kw] *
                                  dout[(((n * Co + oc) * g.Do + tz / g.sz) * g.Ho + ty / s) * g.Wo + tx / s];
-                acc += t;
-                S += fabs(t);
+                acc += term;
+                S += fabs(term);
               }
             }
           }

@@ -57,7 +57,8 @@ MUTANTS_BACKWARD = {
     "dx_overwritten": ("if (dx) dx[xi] += w[wi] * gout;", "if (dx) dx[xi] = w[wi] * gout;"),
     "dw_from_w": ("if (dw) dw[wi] += gout * x[xi];", "if (dw) dw[wi] += gout * w[wi];"),
     "db_one_image": ("if (db) db[oc] += gout;", "if (db && n == 0) db[oc] += gout;"),
-    "bwd_stride_dropped": ("const int64_t iy = oh * s + kh * d - p;\n", "const int64_t iy = oh + kh * d - p;\n"),
+    "bwd_stride_dropped": ("                    const int64_t iy = oh * s + kh * d - p;\n",
+                           "                    const int64_t iy = oh + kh * d - p;\n"),
     "bwd_group_offset_dropped": ("const int64_t ic = grp * Cg + j;\n                for (int64_t kz = 0; kz < g.Kz; ++kz) {",
                                  "const int64_t ic = j + 0 * grp;\n                for (int64_t kz = 0; kz < g.Kz; ++kz) {"),
     "col2im_overwrites": ("dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] += col[r * cols + n * plane + q];",
