@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="conv3x3_bf16")
     ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit"])
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass instead (data + weight + bias gradients of the layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images in the oracle's timed sample (0 = the whole batch)")
@@ -87,11 +89,11 @@ class Runner:
     convolution (conv2d_fwd_bf16_prepacked); otherwise the one library call.
     `main()` is the launch whose duration the roofline uses (the convolution)."""
 
-    def __init__(self, wl, route, seed=None):
+    def __init__(self, wl, route, seed=None, backward=False):
         import torch
         from cnn_convolution_forward_amd import binding as B
         from cnn_convolution_forward_amd import synth
-        self.wl, self.route = wl, route
+        self.wl, self.route, self.backward = wl, route, backward
         self.t = synth.make_inputs(wl, seed=seed)
         t = self.t
         if t.x.dtype == np.uint16:
@@ -116,6 +118,19 @@ class Runner:
                 nbytes = B.conv_im2col_bytes(wl.ndim, wl.N, wl.C_in, wl.spatial[0] if wl.ndim == 3 else 1,
                                              wl.spatial[-2], wl.spatial[-1], wl.K, wl.stride, wl.pad)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        if backward:
+            # upstream gradient: N(0,1), bf16, from the workload seed + 1000
+            rng = np.random.default_rng(wl.seed + 1000)
+            self.dout_np = synth.f32_to_bf16_bits(rng.standard_normal(size=wl.y_shape, dtype=np.float32))
+            self.dout = torch.from_numpy(self.dout_np.view(np.int16)).cuda()
+            self.dx = torch.empty(wl.x_shape, dtype=torch.float32, device="cuda")
+            self.dw = torch.empty(wl.w_shape, dtype=torch.float32, device="cuda")
+            self.db = torch.empty((wl.C_out,), dtype=torch.float32, device="cuda")
+            self.params = B.make_params(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups)
+            self.wsd = torch.empty(max(16, B.conv_bwd_data_workspace_bytes(self.params)), dtype=torch.uint8,
+                                   device="cuda")
+            self.wsw = torch.empty(max(16, B.conv_bwd_weight_workspace_bytes(self.params)), dtype=torch.uint8,
+                                   device="cuda")
         self.B = B
         self._bind()
 
@@ -133,7 +148,13 @@ class Runner:
         algo = B.ALGO.get(self.route, 0)
         x, w, b, y = ptr(self.x), ptr(self.w), ptr(self.b), ptr(self.y)
         self._pre = None
-        if self.params is not None:
+        if self.backward:
+            prm = ctypes.byref(self.params)
+            self._pre = (L.conv_bwd_data_bf16, (prm, ptr(self.dout), w, ptr(self.dx), ptr(self.wsd),
+                                                self.wsd.numel(), st))
+            self._main = (L.conv_bwd_weight_bf16, (prm, x, ptr(self.dout), ptr(self.dw), ptr(self.db),
+                                                   ptr(self.wsw), self.wsw.numel(), st))
+        elif self.params is not None:
             prm = ctypes.byref(self.params)
             if self.route == "explicit":
                 self._main = (L.conv_fwd_explicit_bf16, (prm, x, w, b, y, ptr(self.ws), self.ws.numel(), st))
@@ -207,12 +228,16 @@ def time_steps(runner, steps, warmup):
     wall = time.perf_counter() - t0
     gpu = g0.elapsed_time(g1) * 1e-3
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
+        evp[i][0].record(stream)
         runner.pre()
+        evp[i][1].record(stream)
         ev[i][0].record(stream)
         runner.main()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    runner.pre_per = np.array([a.elapsed_time(b) for a, b in evp]) * 1e-3
     per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3     # seconds
     return wall, gpu, per
 
@@ -272,6 +297,29 @@ def cpu_baseline(wl, runner, sample_images):
             "parity_on_sample": {"max_abs_delta_over_S": rel, "tau": tau, "pass": ok}}
 
 
+def cpu_baseline_backward(wl, runner, sample_images):
+    """The oracle's backward loop on the first `sample_images` images (with
+    their dout); parity of the GPU dx on those images (dx of an image depends
+    on that image's dout only)."""
+    import oracle
+    n = sample_images
+    t = runner.t
+    t0 = time.perf_counter()
+    (dx, _, _), (Sdx, _, _) = oracle.conv_backward(t.x[:n], t.w, runner.dout_np[:n], wl.stride, wl.pad,
+                                                   wl.dilation, wl.groups)
+    dt = time.perf_counter() - t0
+    flops = 2 * wl.flops() * n / wl.N
+    g = runner.dx[:n].cpu().numpy().astype(np.float64)
+    d = np.abs(g - dx)
+    ok = bool(np.all(d <= 1e-3 * Sdx))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = float(np.max(np.where(Sdx > 0, d / np.where(Sdx > 0, Sdx, 1), 0.0)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d of %d images of the same seeded inputs and upstream gradient (dx, dW and db over "
+                      "them, the scatter loop, one thread), fp64" % (n, wl.N),
+            "parity_on_sample": {"dx_max_abs_delta_over_S": rel, "tau": 1e-3, "pass": ok}}
+
+
 def describe(wl):
     extra = {} if wl.plain else {"dilation": wl.dilation, "groups": wl.groups}
     return {"workload": wl.name, "x": list(wl.x_shape), "w": list(wl.w_shape), "y": list(wl.y_shape),
@@ -279,8 +327,8 @@ def describe(wl):
             "seed": wl.seed, "flop_per_step": wl.flops(), "algorithmic_bytes_per_step": algorithmic_bytes(wl)}
 
 
-def measure(wl, route, steps, warmup):
-    runner = Runner(wl, route)
+def measure(wl, route, steps, warmup, backward=False):
+    runner = Runner(wl, route, backward=backward)
     wall, gpu, per = time_steps(runner, steps, warmup)
     return runner, wall, gpu, per
 
@@ -323,18 +371,29 @@ def main():
     from cnn_convolution_forward_amd import synth
 
     wl = synth.ALL_WORKLOADS[args.workload]
-    print("bench: %s route=%s steps=%d warmup=%d" % (wl.name, args.route, args.steps, args.warmup),
+    if args.backward and wl.dtype != "bf16":
+        print("the backward pass takes bf16 inputs; %s is %s" % (wl.name, wl.dtype), file=sys.stderr)
+        sys.exit(2)
+    print("bench: %s route=%s steps=%d warmup=%d%s" % (wl.name, args.route, args.steps, args.warmup,
+                                                       " backward" if args.backward else ""),
           file=sys.stderr, flush=True)
-    runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup)
-    flops = wl.flops()
+    runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup, backward=args.backward)
+    # backward: the data and the weight gradient each cost the forward's FLOP
+    flops = wl.flops() * (2 if args.backward else 1)
     value = flops * args.steps / wall / 1e12
+    kern_flops = wl.flops()
+    dominant = "conv_bwd_weight_bf16" if args.backward else "convolution"
+    bwd_us = {"conv_bwd_data_bf16": round(float(np.mean(runner.pre_per)) * 1e6, 3),
+              "conv_bwd_weight_bf16": round(float(np.mean(per)) * 1e6, 3)}
+    if args.backward and bwd_us["conv_bwd_data_bf16"] > bwd_us["conv_bwd_weight_bf16"]:
+        per, dominant = runner.pre_per, "conv_bwd_data_bf16"
     kern = float(np.mean(per))
-    traffic, traffic_src = traffic_from_profiles(wl.name, args.route)
+    traffic, traffic_src = traffic_from_profiles(wl.name + ("_backward" if args.backward else ""), args.route)
     bound = bound_of(wl, args.route)
     if bound == "mfma":
-        ach, peak, unit = flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        ach, peak, unit = kern_flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     elif bound == "alu":
-        ach, peak, unit = flops / kern / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
+        ach, peak, unit = kern_flops / kern / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
     else:
         ach, peak, unit = algorithmic_bytes(wl) / kern / 1e9, PEAK_HBM_GBS, "GB/s"
     out = {
@@ -346,19 +405,27 @@ def main():
             "N(0,1)" if wl.x_dist == "normal" else "U[-1,1]",
             "U[-1,1]" if wl.dtype == "f32" else "N(0,1/sqrt(fan_in))",
             "; bf16 by RNE" if wl.dtype == "bf16" else ""),
-        "config": describe(wl) | {"route": args.route},
+        "config": describe(wl) | {"route": args.route, "pass": "backward" if args.backward else "forward"},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                      "frac": round(ach / peak, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
+                     "kernel": dominant,
                      "kernel_avg_us": round(kern * 1e6, 3), "kernel_median_us": round(float(np.median(per)) * 1e6, 3),
                      "timing": "HIP events on the library's stream around each convolution launch of a "
                                "second pass of the same steps (the weight repack before it is in the step, "
                                "not in this figure)"},
     }
+    if args.backward:
+        out["roofline"]["timing"] = ("HIP events on the library's stream around each call of a second pass of "
+                                     "the same steps; per call (us): %s; the longer call is the roofline's "
+                                     "kernel (db is inside conv_bwd_weight_bf16)" % json.dumps(bwd_us))
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_images or wl.N
-        out["cpu_baseline"] = cpu_baseline(wl, runner, n)
+        if args.backward:
+            out["cpu_baseline"] = cpu_baseline_backward(wl, runner, args.cpu_sample_images or 2)
+        else:
+            n = args.cpu_sample_images or wl.N
+            out["cpu_baseline"] = cpu_baseline(wl, runner, n)
     print(json.dumps(out), flush=True)
     if args.report:
         report_all(max(5, args.steps // 5), max(2, args.warmup // 2))

@@ -22,6 +22,7 @@
 // positions per stage, contiguous along positions), B = X_col^T gathered from
 // x with bounds checks (32 positions x 128 columns (ic, kd, kh, kw)), both
 // staged in LDS with the reduction contiguous, v_mfma_f32_32x32x16_bf16.
+// Depthwise layers (one input channel per group) have their own VALU kernel.
 #include "conv_internal.h"
 #include "mfma_common.h"
 
@@ -97,11 +98,11 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
             const int oc = m0 + row;
             const int64_t kk = k0 + kq * 8;
             if (a_vec && oc < Cog && kk + 8 <= k_end) {
-                const int64_t n = kk / plane, q = kk - n * plane;
+                const int n = (int)kk / (int)plane, q = (int)kk - n * (int)plane;
                 a_reg[i] = *reinterpret_cast<const uint4 *>(dg + n * dimg + (int64_t)oc * plane + q);
             } else {
                 uint16_t v[8];
-                int64_t n = kk / plane, q = kk - n * plane;
+                int64_t n = (int)kk / (int)plane, q = (int)kk - n * plane;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     v[e] = (oc < Cog && kk + e < k_end) ? dg[n * dimg + (int64_t)oc * plane + q] : (uint16_t)0;
@@ -111,14 +112,15 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
             }
         }
         // B: x at the tap of column jcol for 8 consecutive positions
+        // (32-bit position arithmetic: P = N * output positions < 2^31)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int64_t kk = k0 + (bkq + 2 * i) * 8;
             uint16_t v[8];
-            int64_t t = kk;
-            int ow = (int)(t % sh.Wo); t /= sh.Wo;
-            int oh = (int)(t % sh.Ho); t /= sh.Ho;
-            int od = (int)(t % sh.Do);
+            int t = (int)kk;
+            int ow = t % sh.Wo; t /= sh.Wo;
+            int oh = t % sh.Ho; t /= sh.Ho;
+            int od = t % sh.Do;
             int64_t n = t / sh.Do;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -197,6 +199,84 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
     }
 }
 
+// Weight gradient with one input channel per group (2D depthwise layers):
+// nothing to contract across channels, so no GEMM -- one workgroup per
+// (output channel, range of images) sums dout * x over its positions for all
+// K*K taps on the vector ALUs (x read through buffer loads that return 0
+// outside the image), reduces the taps across the workgroup in a fixed tree,
+// and writes one partial per tap.
+template <int KS>
+__global__ __launch_bounds__(256)
+void wgrad_dw_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
+                     float *__restrict__ part, int splits, int imgs_per_split) {
+    // KS: compile-time kernel size (0: runtime K <= 7, taps held in a 49-entry array)
+    constexpr int KK = KS ? KS * KS : 49;
+    __shared__ float red[256];
+    const int oc = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+    const int M = sh.Co / sh.C, ic = oc / M;
+    const int K = KS ? KS : sh.K, taps = K * K;
+    const int64_t plane = sh.out_plane(), HW = (int64_t)sh.H * sh.W;
+    const int n0 = split * imgs_per_split;
+    const int n1 = n0 + imgs_per_split < sh.N ? n0 + imgs_per_split : sh.N;
+    float acc[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) acc[t] = 0.f;
+    // kU positions per thread per iteration, all their loads issued before the
+    // FMAs use them (positions past the plane read 0 through kOob)
+    constexpr int kU = KS ? 4 : 1;
+    for (int n = n0; n < n1; ++n) {
+        const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout + ((int64_t)n * sh.Co + oc) * plane, (uint32_t)(plane * 2));
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + ((int64_t)n * sh.C + ic) * HW, (uint32_t)(HW * 2));
+        // 32-bit position arithmetic: a plane is below 2^31 elements
+        const int pl = (int)plane;
+        for (int q0 = tid; q0 < pl; q0 += 256 * kU) {
+            float g[kU], xv[kU][KK];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int q = q0 + 256 * u;
+                const bool qin = q < pl;
+                const int oh = q / sh.Wo, ow = q - oh * sh.Wo;
+                g[u] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                    dr, (int)(qin ? (uint32_t)q * 2u : kOob), 0, 0));
+                const int ih0 = oh * sh.s - sh.p, iw0 = ow * sh.s - sh.p;
+#pragma unroll
+                for (int t = 0; t < KK; ++t) {
+                    const int kh = t / K, kw = t - kh * K;
+                    const int ih = ih0 + kh * sh.dil, iw = iw0 + kw * sh.dil;
+                    const bool in = qin && t < taps && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W;
+                    const uint32_t off = in ? (uint32_t)(ih * sh.W + iw) * 2u : kOob;
+                    xv[u][t] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)off, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+#pragma unroll
+                for (int t = 0; t < KK; ++t) acc[t] = __builtin_fmaf(g[u], xv[u][t], acc[t]);
+        }
+    }
+    float *pp = part + ((int64_t)split * sh.Co + oc) * taps;
+#pragma unroll
+    for (int t = 0; t < KK; ++t) {
+        if (t < taps) {
+            red[tid] = acc[t];
+            __syncthreads();
+            for (int h = 128; h > 0; h >>= 1) {
+                if (tid < h) red[tid] += red[tid + h];
+                __syncthreads();
+            }
+            if (tid == 0) pp[t] = red[0];
+            __syncthreads();
+        }
+    }
+}
+
+constexpr int kDwMaxTaps = 49;   // K <= 7
+
+bool wgrad_dw_ok(const Shape &sh) {
+    return sh.ndim == 2 && sh.Cg() == 1 && sh.K * sh.K <= kDwMaxTaps && (int64_t)sh.H * sh.W * 2 < (INT64_C(1) << 31) &&
+           sh.out_plane() * 2 < (INT64_C(1) << 31);
+}
+
 // dw[e] = sum over splits, in order, of part[split][e].
 __global__ __launch_bounds__(256)
 void sum_splits_kernel(const float *__restrict__ part, float *__restrict__ dw, int64_t n, int splits) {
@@ -236,6 +316,11 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
 }
 
 int wgrad_splits(const Shape &sh) {
+    if (wgrad_dw_ok(sh)) {
+        // about 1024 workgroups: output channels x ranges of images
+        int s = (1024 + sh.Co - 1) / sh.Co;
+        return s < sh.N ? s : sh.N;
+    }
     const int64_t P = sh.pixels();
     const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
     const int bm = Cog > 64 ? 128 : 64;
@@ -253,6 +338,22 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     const int64_t P = sh.pixels();
     const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
     const int splits = wgrad_splits(sh);
+    if (wgrad_dw_ok(sh)) {
+        const int per = (sh.N + splits - 1) / splits;
+        const int used = (sh.N + per - 1) / per;          // ranges that hold images
+        if (sh.K == 3)
+            hipLaunchKernelGGL((wgrad_dw_kernel<3>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
+                               dout, part, used, per);
+        else
+            hipLaunchKernelGGL((wgrad_dw_kernel<0>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
+                               dout, part, used, per);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n = sh.w_elems();
+        hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, n,
+                           used);
+        return hipGetLastError();
+    }
     const int64_t chunk = ((P + splits - 1) / splits + kBK - 1) / kBK * kBK;
     const int64_t plane = sh.out_plane();
     const int a_vec = (plane % 8 == 0) && ((uintptr_t)dout % 16 == 0);

@@ -57,6 +57,8 @@ SMALL = [
     (2, 2, 40, (7, 6), 64, 1, 1, 0, 1, 1),        # pointwise
     (3, 2, 4, (5, 6, 7), 6, 3, 1, 1, 1, 2),       # 3D, groups
     (3, 1, 3, (6, 5, 7), 8, 3, 2, 2, 2, 1),       # 3D, stride 2, dilation 2
+    (2, 2, 6, (13, 11), 12, 5, 2, 2, 2, 6),       # depthwise, multiplier 2, K 5, stride 2, dilation 2
+    (2, 3, 5, (9, 10), 5, 3, 1, 1, 1, 5),         # depthwise 3x3 on the depthwise weight-gradient kernel
 ]
 
 
@@ -120,3 +122,19 @@ def test_backward_without_db():
     (rdx, rdw, _), (Sdx, Sdw, _) = oracle.conv_backward(x, w, dout, 1, 1, 1, 2)
     compare(dw.cpu().numpy(), rdw, Sdw, TAU, label="dw")
     compare(dx.cpu().numpy(), rdx, Sdx, TAU, label="dx")
+
+
+def test_backward_full_depthwise_layer_sampled():
+    """x (64,128,56,56), w (128,1,3,3), groups 128: every dw and db entry, 4000 dx entries."""
+    wl = synth.ALL_WORKLOADS["depthwise3x3_bf16"]
+    t = synth.make_inputs(wl)
+    rng = np.random.default_rng(98)
+    dout = synth.f32_to_bf16_bits(rng.standard_normal(size=wl.y_shape, dtype=np.float32))
+    dx, dw, db = _gpu(wl, t.x, t.w, dout)
+    iw = np.arange(dw.size)
+    ix = rng.choice(dx.size, size=4000, replace=False)
+    (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(t.x, t.w, dout, 1, 1, 1, wl.groups, iw, ix)
+    compare(dw.reshape(-1), pdw, pSdw, TAU, label="dw")
+    compare(dx.reshape(-1)[ix], pdx, pSdx, TAU, label="dx")
+    d64 = synth.bf16_bits_to_f32(dout).astype(np.float64)
+    compare(db, d64.sum(axis=(0, 2, 3)), np.abs(d64).sum(axis=(0, 2, 3)), TAU, label="db")
