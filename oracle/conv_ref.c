@@ -28,8 +28,10 @@
  * (bias excluded), the scale against which a low-precision result is judged.
  *
  * Parity pins live in tests/test_oracle_pins.py (plain convolution),
- * tests/test_oracle_pins_general.py (dilation and groups) and
- * tests/test_oracle_pins_backward.py (gradients); every function here is pinned.
+ * tests/test_oracle_pins_general.py (dilation and groups),
+ * tests/test_oracle_pins_backward.py (gradients) and
+ * tests/test_oracle_pins_epilogue.py (ReLU, bf16 output, channels-last); every
+ * function here is pinned.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -606,6 +608,83 @@ int oracle_col2im_dilated(int ndim, const double *col, double *dx,
                     dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] += col[r * cols + n * plane + q];
               }
           }
+    return 0;
+}
+
+/* ---- output epilogue and channels-last layout -----------------------------
+ *
+ * Rectification: out = max(y, 0) (the ReLU that follows the convolution in
+ * [PyTorch tensor products and conv2d/conv3d dimension semantics, 6.2]).
+ * bf16 output: y rounded to the nearest value with an 8-bit significand, ties
+ * to the even significand (IEEE 754 round-to-nearest-even applied to bfloat16,
+ * the top 16 bits of a binary32).  Values are finite here; zero stays zero.
+ */
+double oracle_round_bf16(double v)
+{
+    if (v == 0.0 || !isfinite(v)) return v;
+    int ex;
+    (void)frexp(v, &ex);                 /* v = f * 2^ex, 0.5 <= |f| < 1 */
+    const double scale = ldexp(1.0, 8 - ex);
+    const double t = v * scale;          /* |t| in [128, 256): 8 significant bits above the point */
+    double r = floor(t);
+    const double frac = t - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    return r / scale;
+}
+
+/* out[i] = bf16?(relu?(y[i])) for the requested steps. */
+void oracle_epilogue(const double *y, double *out, int64_t n, int relu, int to_bf16)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double v = y[i];
+        if (relu && v < 0.0) v = 0.0;
+        if (to_bf16) v = oracle_round_bf16(v);
+        out[i] = v;
+    }
+}
+
+/* The general convolution with channels-last activations: x (N, [D,] H, W, C)
+ * and y (N, [Do,] Ho, Wo, Co), the channel index fastest
+ * [PyTorch tensor products and conv2d/conv3d dimension semantics, 6.3];
+ * weights stay (Co, C/G, K, K[, K]).  Written with its own indexing, not by
+ * transposing into the NCHW function.  bias and S may be NULL. */
+int oracle_conv_nhwc(int ndim, const double *x, const double *w, const double *bias, double *y, double *S,
+                     int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                     int64_t Co, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G)
+{
+    gen_geom g;
+    if (gen_geom_make(&g, ndim, N, C, D, H, W, Co, K, s, p, d, G) != 0) return -1;
+    const int64_t Cg = C / G, Cog = Co / G;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t od = 0; od < g.Do; ++od)
+        for (int64_t oh = 0; oh < g.Ho; ++oh)
+          for (int64_t ow = 0; ow < g.Wo; ++ow)
+            for (int64_t oc = 0; oc < Co; ++oc) {
+              const int64_t grp = oc / Cog;
+              double acc = 0.0, mag = 0.0;
+              for (int64_t kz = 0; kz < g.Kz; ++kz) {
+                const int64_t iz = od * g.sz + kz * g.dz - g.pz;
+                if (iz < 0 || iz >= g.Dd) continue;
+                for (int64_t kh = 0; kh < K; ++kh) {
+                  const int64_t iy = oh * s + kh * d - p;
+                  if (iy < 0 || iy >= H) continue;
+                  for (int64_t kw = 0; kw < K; ++kw) {
+                    const int64_t ix = ow * s + kw * d - p;
+                    if (ix < 0 || ix >= W) continue;
+                    const double *px = x + (((n * g.Dd + iz) * H + iy) * W + ix) * C + grp * Cg;
+                    for (int64_t j = 0; j < Cg; ++j) {
+                      const double prod = px[j] * w[(((oc * Cg + j) * g.Kz + kz) * K + kh) * K + kw];
+                      acc += prod;
+                      mag += fabs(prod);
+                    }
+                  }
+                }
+              }
+              const int64_t o = (((n * g.Do + od) * g.Ho + oh) * g.Wo + ow) * Co + oc;
+              y[o] = acc + (bias ? bias[oc] : 0.0);
+              if (S) S[o] = mag;
+            }
     return 0;
 }
 

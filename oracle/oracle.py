@@ -81,6 +81,11 @@ def lib():
         L.oracle_conv_backward_points.restype = ctypes.c_int
         L.oracle_conv_backward_points.argtypes = ([ctypes.c_int, _dp, _dp, _dp, ctypes.c_void_p, _i64, _dp, _dp,
                                                    ctypes.c_void_p, _i64, _dp, _dp] + [_i64] * 11)
+        L.oracle_round_bf16.restype = ctypes.c_double
+        L.oracle_round_bf16.argtypes = [ctypes.c_double]
+        L.oracle_epilogue.argtypes = [_dp, _dp, _i64, ctypes.c_int, ctypes.c_int]
+        L.oracle_conv_nhwc.restype = ctypes.c_int
+        L.oracle_conv_nhwc.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp] + [_i64] * 11
         L.oracle_col2im_dilated.restype = ctypes.c_int
         L.oracle_col2im_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_num_threads.restype = ctypes.c_int
@@ -350,6 +355,48 @@ def col2im_dilated(col, x_shape, K, stride, pad, dilation=1):
     if lib().oracle_col2im_dilated(ndim, _p(col), _p(dx), N, C, D, H, W, K, stride, pad, dilation) != 0:
         raise ValueError("bad col2im shape")
     return dx
+
+
+def round_bf16(v: float) -> float:
+    """Nearest bfloat16 value, ties to even (8-bit significand)."""
+    return float(lib().oracle_round_bf16(float(v)))
+
+
+def epilogue(y, relu=False, to_bf16=False):
+    """max(y, 0) if relu, then rounded to bf16 if to_bf16 (fp64 in and out)."""
+    y = _f64(y)
+    out = np.empty_like(y)
+    lib().oracle_epilogue(_p(y), _p(out), y.size, int(bool(relu)), int(bool(to_bf16)))
+    return out
+
+
+def conv_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, with_S=True):
+    """The general convolution on channels-last x (N, [D,] H, W, C) -> y
+    (N, [Do,] Ho, Wo, Co); w stays (Co, C/groups, K, ...)
+    [PyTorch tensor products and conv2d/conv3d dimension semantics, 6.3]."""
+    x, w = decode(x), decode(w)
+    b = None if bias is None else decode(bias)
+    ndim = x.ndim - 2
+    if ndim == 2:
+        N, H, W, C = x.shape
+        D = 1
+    elif ndim == 3:
+        N, D, H, W, C = x.shape
+    else:
+        raise ValueError("x must be NHWC or NDHWC")
+    Co, Cg, K = w.shape[0], w.shape[1], w.shape[2]
+    if w.ndim != ndim + 2 or groups < 1 or Cg * groups != C or Co % groups:
+        raise ValueError("weight %s does not fit C_in=%d, groups=%d" % (w.shape, C, groups))
+    sizes = [out_dim_dilated(n, K, stride, pad, dilation) for n in ((D, H, W) if ndim == 3 else (H, W))]
+    if min(sizes) < 0:
+        raise ValueError("dilated kernel larger than padded input")
+    y = np.empty((N,) + tuple(sizes) + (Co,), np.float64)
+    S = np.empty_like(y) if with_S else None
+    rc = lib().oracle_conv_nhwc(ndim, _p(x), _p(w), _p(b), _p(y), _p(S), N, C, D, H, W, Co, K, stride, pad,
+                                dilation, groups)
+    if rc != 0:
+        raise ValueError("oracle_conv_nhwc rejected the shape")
+    return (y, S) if with_S else y
 
 
 def num_threads() -> int:

@@ -6,10 +6,10 @@ transposed, a depth offset lost, |x*w| replaced by x*w, ceil for floor, an
 off-by-one bounds check; in the dilation/groups functions: dilation dropped
 from an axis, groups interleaved, the group's channel offset lost, the dilated
 span mis-sized; in the backward pass: dx overwritten, dW from w, db over one
-image, the stride or group offset lost, col2im overwriting), builds it with
-gcc, and runs the matching pin file (tests/test_oracle_pins.py,
-tests/test_oracle_pins_general.py or tests/test_oracle_pins_backward.py)
-against that build in a subprocess.  The run must fail.  Runs on the CPU only.
+image, the stride or group offset lost, col2im overwriting; in the epilogue:
+bf16 ties rounded away or truncated, ReLU keeping negatives, the channels-last
+group offset lost), builds it with gcc, and runs the matching pin file
+(tests/test_oracle_pins*.py) against that build in a subprocess.  The run must fail.  Runs on the CPU only.
 """
 import os
 import subprocess
@@ -65,14 +65,25 @@ MUTANTS_BACKWARD = {
                           "dx[(((n * C + ic) * g.Dd + iz) * H + iy) * W + ix] = col[r * cols + n * plane + q];"),
 }
 
+# Mistakes in the epilogue and the channels-last convolution, caught by test_oracle_pins_epilogue.py.
+MUTANTS_EPILOGUE = {
+    "bf16_ties_away": ("if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
+                       "if (frac >= 0.5) r += 1.0;"),
+    "bf16_truncates": ("if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
+                       "if (frac > 2.0) r += 1.0;"),
+    "relu_keeps_negatives": ("if (relu && v < 0.0) v = 0.0;", "if (relu && v < -1e300) v = 0.0;"),
+    "nhwc_group_offset_dropped": ("* W + ix) * C + grp * Cg;", "* W + ix) * C + 0 * grp * Cg;"),
+}
+
 CASES = [(n, "test_oracle_pins.py") for n in sorted(MUTANTS)] + \
         [(n, "test_oracle_pins_general.py") for n in sorted(MUTANTS_GENERAL)] + \
-        [(n, "test_oracle_pins_backward.py") for n in sorted(MUTANTS_BACKWARD)]
+        [(n, "test_oracle_pins_backward.py") for n in sorted(MUTANTS_BACKWARD)] + \
+        [(n, "test_oracle_pins_epilogue.py") for n in sorted(MUTANTS_EPILOGUE)]
 
 
 @pytest.mark.parametrize("name,pins", CASES)
 def test_planted_mistake_is_caught(name, pins, tmp_path):
-    old, new = {**MUTANTS, **MUTANTS_GENERAL, **MUTANTS_BACKWARD}[name]
+    old, new = {**MUTANTS, **MUTANTS_GENERAL, **MUTANTS_BACKWARD, **MUTANTS_EPILOGUE}[name]
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not found once: %s" % name
     mutant_c = tmp_path / "conv_ref_mutant.c"
