@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="conv3x3_bf16")
     ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit"])
+    ap.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"], help="layout of x and y (forward)")
+    ap.add_argument("--out", default="f32", choices=["f32", "bf16"], help="output dtype (forward)")
+    ap.add_argument("--relu", action="store_true", help="fused ReLU after the bias (forward)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass instead (data + weight + bias gradients of the layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,21 +67,22 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(wl):
-    """x, w, bias read once + y written once (fp32 output)."""
+def algorithmic_bytes(wl, out_bytes=4):
+    """x, w, bias read once + y written once (fp32 output, or bf16 with out_bytes=2)."""
     esz = 4 if wl.dtype == "f32" else 2
     x = int(np.prod(wl.x_shape)) * esz
     w = int(np.prod(wl.w_shape)) * esz
     b = wl.C_out * 4
-    y = int(np.prod(wl.y_shape)) * 4
+    y = int(np.prod(wl.y_shape)) * out_bytes
     return x + w + b + y
 
 
-def bound_of(wl, route):
+def bound_of(wl, route, out_bytes=4):
+    ab = algorithmic_bytes(wl, out_bytes)
     if wl.dtype == "f32" or route == "valu":
-        return "alu" if wl.flops() / algorithmic_bytes(wl) > PEAK_FP32_VALU_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+        return "alu" if wl.flops() / ab > PEAK_FP32_VALU_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    return "mfma" if wl.flops() / algorithmic_bytes(wl) > ridge else "hbm"
+    return "mfma" if wl.flops() / ab > ridge else "hbm"
 
 
 class Runner:
@@ -89,11 +93,13 @@ class Runner:
     convolution (conv2d_fwd_bf16_prepacked); otherwise the one library call.
     `main()` is the launch whose duration the roofline uses (the convolution)."""
 
-    def __init__(self, wl, route, seed=None, backward=False):
+    def __init__(self, wl, route, seed=None, backward=False, options=None):
         import torch
         from cnn_convolution_forward_amd import binding as B
         from cnn_convolution_forward_amd import synth
         self.wl, self.route, self.backward = wl, route, backward
+        # (layout, out dtype, relu); None = NCHW, fp32, no ReLU
+        self.options = None if options in (None, ("nchw", "f32", False)) else options
         self.t = synth.make_inputs(wl, seed=seed)
         t = self.t
         if t.x.dtype == np.uint16:
@@ -104,12 +110,27 @@ class Runner:
             self.w = torch.from_numpy(t.w).cuda()
         self.b = None if t.b is None else torch.from_numpy(t.b).cuda()
         self.y = torch.empty(wl.y_shape, dtype=torch.float32, device="cuda")
+        if self.options is not None:
+            layout, out, relu = self.options
+            if layout == "nhwc":
+                # the same values, stored channels-last
+                perm = (0,) + tuple(range(2, wl.ndim + 2)) + (1,)
+                self.x = self.x.permute(*perm).contiguous()
+                yshape = (wl.y_shape[0],) + tuple(wl.y_shape[2:]) + (wl.y_shape[1],)
+            else:
+                yshape = wl.y_shape
+            self.y = torch.empty(yshape, dtype=torch.int16 if out == "bf16" else torch.float32, device="cuda")
+            self.opts = B.ConvOptions(B.LAYOUT[layout], B.OUT_DTYPE[out], int(bool(relu)))
         self.ws = None
         self.packed = None
         # dilation / groups go through the general entry points (conv_params_t)
         self.params = None if wl.plain else B.make_params(wl.x_shape, wl.w_shape, wl.stride, wl.pad,
                                                           wl.dilation, wl.groups)
-        if route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16" and wl.plain:
+        if self.options is not None:
+            self.params = B.make_params(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups)
+            n = B.conv_fwd_ex_workspace_bytes(self.params, self.opts, B.ALGO.get(route, 0))
+            self.ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+        elif route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16" and wl.plain:
             self.packed = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
         if route == "explicit":
             if self.params is not None:
@@ -148,7 +169,14 @@ class Runner:
         algo = B.ALGO.get(self.route, 0)
         x, w, b, y = ptr(self.x), ptr(self.w), ptr(self.b), ptr(self.y)
         self._pre = None
-        if self.backward:
+        if self.options is not None:
+            prm, opt = ctypes.byref(self.params), ctypes.byref(self.opts)
+            if wl.dtype == "f32":
+                self._main = (L.conv_fwd_ex_f32, (prm, opt, x, w, b, y, algo, st))
+            else:
+                nb = 0 if self.ws is None else self.ws.numel()
+                self._main = (L.conv_fwd_ex_bf16, (prm, opt, x, w, b, y, ptr(self.ws), nb, algo, st))
+        elif self.backward:
             prm = ctypes.byref(self.params)
             self._pre = (L.conv_bwd_data_bf16, (prm, ptr(self.dout), w, ptr(self.dx), ptr(self.wsd),
                                                 self.wsd.numel(), st))
@@ -276,18 +304,29 @@ def cpu_baseline(wl, runner, sample_images):
     t = runner.t
     n = sample_images
     xs = t.x[:n]
+    layout, out, relu = runner.options or ("nchw", "f32", False)
     t0 = time.perf_counter()
-    if wl.plain:
+    if wl.plain and runner.options is None:
         f = oracle.conv2d if wl.ndim == 2 else oracle.conv3d
         y_ref, S = f(xs, t.w, t.b, wl.stride, wl.pad)
     else:
         y_ref, S = oracle.conv_general(xs, t.w, t.b, wl.stride, wl.pad, wl.dilation, wl.groups)
+        if relu or out == "bf16":
+            y_ref = oracle.epilogue(y_ref, relu=relu)
     dt = time.perf_counter() - t0
     flops = wl.flops() * n / wl.N
-    y_gpu = runner.y[:n].cpu().numpy().astype(np.float64)
+    y_gpu = runner.y[:n].cpu()
+    if out == "bf16":
+        from cnn_convolution_forward_amd import synth
+        y_gpu = synth.bf16_bits_to_f32(y_gpu.numpy().view(np.uint16))
+    else:
+        y_gpu = y_gpu.numpy()
+    if layout == "nhwc":
+        y_gpu = np.moveaxis(y_gpu, -1, 1)
+    y_gpu = y_gpu.astype(np.float64)
     d = np.abs(y_gpu - y_ref)
     tau = 1e-3 if wl.dtype == "bf16" else 1e-5
-    ok = bool(np.all(d <= tau * S))
+    ok = bool(np.all(d <= tau * S + (2.0 ** -8 * np.abs(y_ref) if out == "bf16" else 0.0)))
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = float(np.max(np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -327,8 +366,8 @@ def describe(wl):
             "seed": wl.seed, "flop_per_step": wl.flops(), "algorithmic_bytes_per_step": algorithmic_bytes(wl)}
 
 
-def measure(wl, route, steps, warmup, backward=False):
-    runner = Runner(wl, route, backward=backward)
+def measure(wl, route, steps, warmup, backward=False, options=None):
+    runner = Runner(wl, route, backward=backward, options=options)
     wall, gpu, per = time_steps(runner, steps, warmup)
     return runner, wall, gpu, per
 
@@ -377,7 +416,15 @@ def main():
     print("bench: %s route=%s steps=%d warmup=%d%s" % (wl.name, args.route, args.steps, args.warmup,
                                                        " backward" if args.backward else ""),
           file=sys.stderr, flush=True)
-    runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup, backward=args.backward)
+    options = (args.layout, args.out, args.relu)
+    if args.backward and options != ("nchw", "f32", False):
+        print("--layout/--out/--relu apply to the forward pass only", file=sys.stderr)
+        sys.exit(2)
+    if args.route == "explicit" and options != ("nchw", "f32", False):
+        print("the explicit route takes NCHW, fp32 output, no ReLU", file=sys.stderr)
+        sys.exit(2)
+    runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup, backward=args.backward,
+                                     options=options)
     # backward: the data and the weight gradient each cost the forward's FLOP
     flops = wl.flops() * (2 if args.backward else 1)
     value = flops * args.steps / wall / 1e12
@@ -389,13 +436,14 @@ def main():
         per, dominant = runner.pre_per, "conv_bwd_data_bf16"
     kern = float(np.mean(per))
     traffic, traffic_src = traffic_from_profiles(wl.name + ("_backward" if args.backward else ""), args.route)
-    bound = bound_of(wl, args.route)
+    out_bytes = 2 if args.out == "bf16" else 4
+    bound = bound_of(wl, args.route, out_bytes)
     if bound == "mfma":
         ach, peak, unit = kern_flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     elif bound == "alu":
         ach, peak, unit = kern_flops / kern / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
     else:
-        ach, peak, unit = algorithmic_bytes(wl) / kern / 1e9, PEAK_HBM_GBS, "GB/s"
+        ach, peak, unit = algorithmic_bytes(wl, out_bytes) / kern / 1e9, PEAK_HBM_GBS, "GB/s"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
@@ -405,7 +453,8 @@ def main():
             "N(0,1)" if wl.x_dist == "normal" else "U[-1,1]",
             "U[-1,1]" if wl.dtype == "f32" else "N(0,1/sqrt(fan_in))",
             "; bf16 by RNE" if wl.dtype == "bf16" else ""),
-        "config": describe(wl) | {"route": args.route, "pass": "backward" if args.backward else "forward"},
+        "config": describe(wl) | {"route": args.route, "pass": "backward" if args.backward else "forward",
+                                  "layout": args.layout, "out_dtype": args.out, "relu": args.relu},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                      "frac": round(ach / peak, 4), "traffic": traffic,

@@ -32,13 +32,22 @@ EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv_out_dim_dilated", "conv_fwd_bf16", "conv_fwd_f32", "conv_xcol_bytes",
            "conv_im2col_bf16", "conv_fwd_explicit_bf16",
            "conv_bwd_data_workspace_bytes", "conv_bwd_data_bf16",
-           "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_bf16")
+           "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_bf16",
+           "conv_fwd_ex_workspace_bytes", "conv_fwd_ex_bf16", "conv_fwd_ex_f32")
+
+LAYOUT = {"nchw": 0, "nhwc": 1}
+OUT_DTYPE = {"f32": 0, "bf16": 1}
 
 
 class ConvParams(ctypes.Structure):
     """conv_params_t: a general problem (dilation and groups)."""
     _fields_ = [(n, ctypes.c_int) for n in ("ndim", "N", "C_in", "D", "H", "W", "C_out", "K", "stride",
                                              "pad", "dilation", "groups")]
+
+
+class ConvOptions(ctypes.Structure):
+    """conv_options_t: layout of x and y, output dtype, ReLU."""
+    _fields_ = [("layout", ctypes.c_int), ("out_dtype", ctypes.c_int), ("relu", ctypes.c_int)]
 
 
 class ConvError(RuntimeError):
@@ -108,6 +117,13 @@ def lib():
         L.conv_bwd_data_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.conv_bwd_weight_bf16.restype = _i
         L.conv_bwd_weight_bf16.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        _po = ctypes.POINTER(ConvOptions)
+        L.conv_fwd_ex_workspace_bytes.restype = _sz
+        L.conv_fwd_ex_workspace_bytes.argtypes = [_pp, _po, _i]
+        L.conv_fwd_ex_bf16.restype = _i
+        L.conv_fwd_ex_bf16.argtypes = [_pp, _po, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]
+        L.conv_fwd_ex_f32.restype = _i
+        L.conv_fwd_ex_f32.argtypes = [_pp, _po, _vp, _vp, _vp, _vp, _i, _vp]
         _lib = L
     return _lib
 
@@ -232,6 +248,22 @@ def conv_bwd_weight_workspace_bytes(params):
 
 def conv_bwd_weight_bf16(params, x, dout, dw, db, ws, ws_bytes, stream=None):
     return lib().conv_bwd_weight_bf16(_pref(params), x, dout, dw, db, ws, ws_bytes, stream)
+
+
+def _oref(opts):
+    return None if opts is None else ctypes.byref(opts)
+
+
+def conv_fwd_ex_workspace_bytes(params, opts, algo=0):
+    return int(lib().conv_fwd_ex_workspace_bytes(_pref(params), _oref(opts), algo))
+
+
+def conv_fwd_ex_bf16(params, opts, x, w, bias, y, ws, ws_bytes, algo=0, stream=None):
+    return lib().conv_fwd_ex_bf16(_pref(params), _oref(opts), x, w, bias, y, ws, ws_bytes, algo, stream)
+
+
+def conv_fwd_ex_f32(params, opts, x, w, bias, y, algo=0, stream=None):
+    return lib().conv_fwd_ex_f32(_pref(params), _oref(opts), x, w, bias, y, algo, stream)
 
 
 def make_params(x_shape, w_shape, stride=1, pad=0, dilation=1, groups=1):
@@ -548,3 +580,50 @@ def conv_backward(x, w, dout, stride=1, pad=0, dilation=1, groups=1, with_db=Tru
     if st != CONV_OK:
         raise ConvError(st, "conv_bwd_weight_bf16")
     return dx, dw, db
+
+
+def conv_ex(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, layout="nchw", out_dtype="f32", relu=False,
+            algo="auto", workspace=None, out=None):
+    """conv_fwd_ex_bf16 / conv_fwd_ex_f32.  layout "nhwc": x is (N, [D,] H, W, C)
+    and y comes back (N, [D,] H, W, C_out); w stays (C_out, C_in/groups, K...).
+    out_dtype "bf16": y holds bf16 bits (int16).  workspace: a tensor from
+    workspace_ex() (packed 3x3 weights) or None."""
+    torch = _torch()
+    f32 = x.dtype == torch.float32
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_tensor(x, "x", (torch.float32,) if f32 else half)
+    _check_tensor(w, "w", (torch.float32,) if f32 else half)
+    _check_tensor(bias, "bias", (torch.float32,))
+    if layout == "nhwc":
+        logical = (x.shape[0], x.shape[-1]) + tuple(x.shape[1:-1])
+    else:
+        logical = tuple(x.shape)
+    prm = make_params(logical, tuple(w.shape), stride, pad, dilation, groups)
+    opts = ConvOptions(LAYOUT[layout], OUT_DTYPE[out_dtype], int(bool(relu)))
+    K = w.shape[2]
+    outs = [conv_out_dim_dilated(d, K, stride, pad, dilation) for d in logical[2:]]
+    if min(outs) < 1:
+        raise ConvError(3, "conv_ex")
+    shape = (logical[0], *outs, w.shape[0]) if layout == "nhwc" else (logical[0], w.shape[0], *outs)
+    dt = torch.float32 if out_dtype == "f32" else torch.int16
+    y = out if out is not None else torch.empty(shape, dtype=dt, device=x.device)
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    if f32:
+        st = conv_fwd_ex_f32(prm, opts, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), a, _stream())
+    else:
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = conv_fwd_ex_bf16(prm, opts, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(workspace), wsb, a, _stream())
+    if st != CONV_OK:
+        raise ConvError(st, "conv_fwd_ex")
+    return y
+
+
+def workspace_ex(x_shape, w_shape, stride=1, pad=0, dilation=1, groups=1, layout="nchw", out_dtype="f32",
+                 relu=False, algo="auto", device="cuda"):
+    """Workspace tensor for conv_ex (None when no route uses one); x_shape logical NC(D)HW."""
+    torch = _torch()
+    prm = make_params(tuple(x_shape), tuple(w_shape), stride, pad, dilation, groups)
+    opts = ConvOptions(LAYOUT[layout], OUT_DTYPE[out_dtype], int(bool(relu)))
+    a = ALGO[algo] if isinstance(algo, str) else int(algo)
+    n = conv_fwd_ex_workspace_bytes(prm, opts, a)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None

@@ -76,7 +76,7 @@ conv_status_t make_shape(int ndim, int N, int C, int D, int H, int W, int Co,
 
 conv_status_t check_alias(const Shape &sh, int esize, const void *x, const void *w,
                           const void *bias, const void *y, const void *ws, size_t ws_bytes) {
-    int64_t yb = sh.y_elems() * 4;
+    int64_t yb = sh.y_elems() * (sh.out_bf16 ? 2 : 4);
     if (overlaps(y, yb, x, sh.x_elems() * esize) || overlaps(y, yb, w, sh.w_elems() * esize) ||
         overlaps(y, yb, bias, (int64_t)sh.Co * 4) || overlaps(y, yb, ws, (int64_t)ws_bytes))
         return CONV_ERR_ALIAS;
@@ -525,6 +525,52 @@ conv_status_t conv_bwd_weight_bf16(const conv_params_t *prm, const uint16_t *x, 
     hipStream_t hs = (hipStream_t)stream;
     if (db && convfwd::launch_bias_grad_bf16(sh, dout, db, hs) != hipSuccess) return CONV_ERR_HIP;
     return to_status(convfwd::launch_wgrad_bf16(sh, x, dout, (float *)workspace, dw, hs));
+}
+
+// ---- options: channels-last layout, ReLU, bf16 output ----
+
+namespace {
+
+conv_status_t apply_options(const conv_options_t *o, Shape &sh) {
+    if (!o) return CONV_OK;
+    if ((o->layout != CONV_LAYOUT_NCHW && o->layout != CONV_LAYOUT_NHWC) ||
+        (o->out_dtype != CONV_OUT_F32 && o->out_dtype != CONV_OUT_BF16) || (o->relu != 0 && o->relu != 1))
+        return CONV_ERR_PARAM;
+    sh.nhwc = o->layout == CONV_LAYOUT_NHWC;
+    sh.out_bf16 = o->out_dtype == CONV_OUT_BF16;
+    sh.relu = o->relu;
+    return CONV_OK;
+}
+
+}  // namespace
+
+size_t conv_fwd_ex_workspace_bytes(const conv_params_t *prm, const conv_options_t *opts, int algo) {
+    if (!prm) return 0;
+    Shape sh;
+    if (shape_from_params(prm, sh) != CONV_OK || apply_options(opts, sh) != CONV_OK) return 0;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU || pick_route(sh, algo) != CONV_ALGO_MFMA) return 0;
+    return convfwd::igemm_workspace_bytes(sh, (const void *)256, (const void *)256);
+}
+
+conv_status_t conv_fwd_ex_bf16(const conv_params_t *prm, const conv_options_t *opts, const uint16_t *x,
+                               const uint16_t *w, const float *bias, void *y, void *workspace, size_t workspace_bytes,
+                               int algo, void *stream) {
+    if (!prm || !x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    if ((st = apply_options(opts, sh)) != CONV_OK) return st;
+    return fwd_bf16_sh(sh, x, w, bias, (float *)y, algo, stream, workspace != nullptr, workspace, workspace_bytes);
+}
+
+conv_status_t conv_fwd_ex_f32(const conv_params_t *prm, const conv_options_t *opts, const float *x, const float *w,
+                              const float *bias, void *y, int algo, void *stream) {
+    if (!prm || !x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = shape_from_params(prm, sh);
+    if (st != CONV_OK) return st;
+    if ((st = apply_options(opts, sh)) != CONV_OK) return st;
+    return fwd_f32_sh(sh, x, w, bias, (float *)y, algo, stream);
 }
 
 }  // extern "C"

@@ -23,10 +23,14 @@ struct Shape {
     int G = 1;              // groups: divides C and Co
     int ups = 1, upsd = 1;  // zero insertion of the input (data gradient of a strided
                             // convolution; only the general kernel's upsampled mode reads these)
+    int out_bf16 = 0;       // y holds bf16 bits (fp32 result rounded to nearest even), not fp32
+    int relu = 0;           // y = max(y, 0) before the store
+    int nhwc = 0;           // x and y channels-last: (N, [D,] H, W, C); w stays (Co, C/G, taps)
 
     __host__ __device__ int Cg() const { return C / G; }                                // input channels per group
     __host__ __device__ int Cog() const { return Co / G; }                              // output channels per group
     __host__ __device__ bool plain() const { return dil == 1 && G == 1; }
+    __host__ __device__ bool plain_io() const { return !out_bf16 && !relu && !nhwc; }
     __host__ __device__ int64_t taps() const { return (int64_t)Kd * K * K; }            // K^ndim
     __host__ __device__ int64_t kgemm() const { return (int64_t)Cg() * taps(); }       // reduction per group
     __host__ __device__ int64_t xcol_rows() const { return (int64_t)C * taps(); }      // rows of X_col

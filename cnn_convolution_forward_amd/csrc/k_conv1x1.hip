@@ -50,7 +50,7 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const float *__restrict__ bias, float *__restrict__ y,
-                    int C, int Co, int plane, int64_t P, int npt, int ncb, int remap) {
+                    int C, int Co, int plane, int64_t P, int npt, int ncb, int remap, int out_bf16, int relu) {
     __shared__ __align__(16) uint16_t As[2][kBM][kLdA];
     __shared__ __align__(16) uint16_t Bs[2][kBK][kLdB];
 
@@ -146,9 +146,11 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
         __syncthreads();
     }
 
-    // epilogue: y[n][oc][q] = acc + bias[oc], through buffer resources (32-bit
-    // offsets; a bias resource with no records reads 0 when there is no bias)
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)(P * Co * 4));
+    // epilogue: y[n][oc][q] = acc + bias[oc] (then ReLU, bf16 rounding), through
+    // buffer resources (32-bit offsets; a bias resource with no records reads 0
+    // when there is no bias).  Offsets are in fp32 elements * 4; a bf16 output
+    // stores 2-byte elements at half those offsets.
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)(P * Co * (out_bf16 ? 2 : 4)));
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bias ? (const void *)bias : (const void *)y,
                                                 bias ? (uint32_t)Co * 4 : 0u);
     uint32_t base[2];
@@ -166,8 +168,15 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
             const float bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, oc * 4, 0, 0));
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const uint32_t vo = (oc < Co) ? base[j] + (uint32_t)oc * plane * 4 : kOob;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] + bv), yr, (int)vo, 0, 0);
+                const bool ok = oc < Co && base[j] != kOob;
+                const uint32_t vo = ok ? base[j] + (uint32_t)oc * plane * 4 : kOob;
+                float v = acc[i][j][r] + bv;
+                if (relu) v = fmaxf(v, 0.f);
+                if (out_bf16)
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(v), yr, (int)(ok ? vo >> 1 : kOob),
+                                                          0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)vo, 0, 0);
             }
         }
 }
@@ -176,7 +185,7 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
 
 bool conv1x1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t plane = sh.out_plane();
-    return sh.plain() && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
+    return sh.plain() && !sh.nhwc && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
            plane < (INT64_C(1) << 31) && sh.x_elems() * 2 < (INT64_C(1) << 31) &&
            sh.y_elems() * 4 < (INT64_C(1) << 31) &&
            sh.w_elems() * 2 < (INT64_C(1) << 31) &&
@@ -192,7 +201,7 @@ hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_
     const int64_t T = (int64_t)npt * ncb;
     const int remap = (T % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co,
-                       plane, P, npt, ncb, remap);
+                       plane, P, npt, ncb, remap, sh.out_bf16, sh.relu);
     return hipGetLastError();
 }
 

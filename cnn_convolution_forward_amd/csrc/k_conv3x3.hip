@@ -604,7 +604,7 @@ void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipSt
 
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t HW = (int64_t)sh.H * sh.W;
-    return sh.plain() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIcStage == 0 &&
+    return sh.plain() && sh.plain_io() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIcStage == 0 &&
            sh.C >= 2 * kIcStage &&
            sh.Co % kOcTile == 0 && sh.W % 8 == 0 && sh.W >= 8 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&            // one image within a buffer range

@@ -138,11 +138,13 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (
     if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, tb, row7, mid);
 }
 
-template <int D>
+// OUT: 0 = fp32 output, 1 = bf16 output (rounded to nearest even); relu:
+// max(y, 0) before the store.
+template <int D, int OUT>
 __global__ __launch_bounds__(kThreads, 2)
 void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
                       const float *__restrict__ bias, float *__restrict__ y,
-                      int C, int H, int Co, int rb_per_img, int remap) {
+                      int C, int H, int Co, int rb_per_img, int remap, int relu) {
     using G = Geo<D>;
     constexpr int W = G::W, J = G::J, RP = G::RP;
     __shared__ __align__(16) uint8_t smem[G::LDS];
@@ -289,9 +291,12 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     // one channel's 8 rows -- a contiguous 32*W-byte block of y -- so every
     // store instruction writes 1 KB of consecutive output.
     float *const epi = reinterpret_cast<float *>(smem);
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + ((int64_t)n * Co + ocb) * HW, (uint32_t)kOc * HW * 4);
+    constexpr int kOutB = OUT ? 2 : 4;                   // bytes per output element
+    constexpr int kPer = 16 / kOutB;                     // outputs per 16-byte store
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB,
+                                                (uint32_t)kOc * HW * kOutB);
     constexpr int kChPitch = kRows * W + 4;
-    constexpr int kChunks = kEpiOc * kRows * W / 4;      // 16-byte chunks per pass
+    constexpr int kChunks = kEpiOc * kRows * W / kPer;   // 16-byte chunks per pass
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         __builtin_amdgcn_sched_barrier(0);
@@ -310,13 +315,30 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
         for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
             const int cid = k * kThreads + tid;
             if (kChunks % kThreads == 0 || cid < kChunks) {
-                const int ocl = cid / (kRows * W / 4), e = cid - ocl * (kRows * W / 4);   // e: chunk within the 8 rows
-                const int row = (4 * e) / W;
-                const float4 a4 = *reinterpret_cast<const float4 *>(epi + ocl * kChPitch + 4 * e);
+                const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
+                const int row = (kPer * e) / W;
                 const bool ok = r0 + row < H;
-                const uint32_t vo = ok ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + 4 * e) * 4) : kOob;
-                const u32x4_t va = {__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
-                                    __float_as_uint(a4.w)};
+                const uint32_t vo =
+                    ok ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + kPer * e) * kOutB) : kOob;
+                const float *src = epi + ocl * kChPitch + kPer * e;
+                u32x4_t va;
+                if (OUT == 0) {
+                    float4 a4 = *reinterpret_cast<const float4 *>(src);
+                    if (relu) {
+                        a4.x = fmaxf(a4.x, 0.f); a4.y = fmaxf(a4.y, 0.f);
+                        a4.z = fmaxf(a4.z, 0.f); a4.w = fmaxf(a4.w, 0.f);
+                    }
+                    va = (u32x4_t){__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
+                                   __float_as_uint(a4.w)};
+                } else {
+                    const float4 lo = *reinterpret_cast<const float4 *>(src);
+                    const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+                    const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    uint32_t b[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(relu ? fmaxf(f[u], 0.f) : f[u]);
+                    va = (u32x4_t){b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+                }
                 __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
             }
         }
@@ -329,7 +351,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
     (void)w;
     const int64_t HW = (int64_t)sh.H * sh.W;
-    return sh.plain() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
+    return sh.plain() && !sh.nhwc && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
            sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
            (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range
@@ -344,9 +366,13 @@ hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint1
     const int64_t blocks = (int64_t)sh.N * rb * 2;       // tiles x two 64-channel halves
     const int remap = (blocks % 8 == 0) ? 1 : 0;
     dim3 grid((unsigned)blocks, (unsigned)(sh.Co / kPackOcBlock));
-#define CONV3X3CG_LAUNCH(DV)                                                                          \
-    hipLaunchKernelGGL((conv3x3cg_kernel<DV>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
-                       sh.Co, rb, remap)
+#define CONV3X3CG_LAUNCH(DV)                                                                                   \
+    if (sh.out_bf16)                                                                                           \
+        hipLaunchKernelGGL((conv3x3cg_kernel<DV, 1>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
+                           sh.Co, rb, remap, sh.relu);                                                         \
+    else                                                                                                       \
+        hipLaunchKernelGGL((conv3x3cg_kernel<DV, 0>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
+                           sh.Co, rb, remap, sh.relu)
     switch (sh.W / 4) {
         case 8: CONV3X3CG_LAUNCH(8); break;
         case 10: CONV3X3CG_LAUNCH(10); break;

@@ -175,12 +175,20 @@ __device__ __forceinline__ void dw_compute(const Shape &sh, const DwGeom &g, con
                 for (int i = 0; i < RB; ++i) acc[i] = __builtin_fmaf(pt[i * S * g.PCP], wv, acc[i]);
             }
         }
-        // rows past the output go to kOob: the store is dropped, no branch
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + (d.n * sh.Co + oc) * oplane, (uint32_t)(oplane * 4));
+        // rows past the output go to kOob: the store is dropped, no branch.
+        // Optional ReLU, then an fp32 or a bf16 (rounded to nearest even) store.
+        const int ob = sh.out_bf16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t yr =
+            make_rsrc((char *)y + (d.n * sh.Co + oc) * oplane * ob, (uint32_t)(oplane * ob));
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-            const uint32_t o = ohs + i < sh.Ho ? (uint32_t)((ohs + i) * sh.Wo + ow) * 4u : kOob;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i] + bv), yr, (int)o, 0, 0);
+            const uint32_t o = ohs + i < sh.Ho ? (uint32_t)((ohs + i) * sh.Wo + ow) * (uint32_t)ob : kOob;
+            float v = acc[i] + bv;
+            if (sh.relu) v = fmaxf(v, 0.f);
+            if (sh.out_bf16)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(v), yr, (int)o, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)o, 0, 0);
         }
     }
 }
@@ -352,7 +360,7 @@ hipError_t launch_dw(const Shape &sh, const T *x, const T *w, const float *bias,
 }  // namespace
 
 bool depthwise_supported(const Shape &sh) {
-    if (sh.ndim != 2 || sh.Cg() != 1) return false;
+    if (sh.ndim != 2 || sh.Cg() != 1 || sh.nhwc) return false;
     // one input or output plane per buffer resource, byte offsets below kOob
     if ((int64_t)sh.H * sh.W * 4 >= (INT64_C(1) << 31) || (int64_t)sh.Ho * sh.Wo * 4 >= (INT64_C(1) << 31))
         return false;

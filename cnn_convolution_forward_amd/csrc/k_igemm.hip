@@ -25,6 +25,9 @@
 // neighbours, the transposed convolution), so a virtual coordinate v reads
 // dout[v / ups] when v % ups == 0 and 0 otherwise.
 //
+// Options of the general entry point: channels-last x and y (sh.nhwc), and an
+// epilogue with ReLU and/or bf16 output (sh.relu, sh.out_bf16).
+//
 // This is the route for every shape the specialised kernels do not cover.
 #include "conv_internal.h"
 #include "mfma_common.h"
@@ -68,7 +71,9 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
         int ow = (int)(t % sh.Wo); t /= sh.Wo;
         int oh = (int)(t % sh.Ho); t /= sh.Ho;
         int od = (int)(t % sh.Do); t /= sh.Do;
-        xn = src + (t * sh.C + (int64_t)grp * Cg) * sh.in_plane();
+        // image t, first channel of the group: NCHW (channel planes) or NHWC (channel fastest)
+        xn = src + (sh.nhwc ? t * sh.C * sh.in_plane() + (int64_t)grp * Cg
+                            : (t * sh.C + (int64_t)grp * Cg) * sh.in_plane());
         id0 = od * sh.sd - sh.pd;
         ih0 = oh * sh.s - sh.p;
         iw0 = ow * sh.s - sh.p;
@@ -76,6 +81,8 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
     const int KK = sh.K * sh.K;
     const int taps = sh.Kd * KK;
     const int64_t HW = (int64_t)sh.H * sh.W;
+    // element (ic, spatial s) of an image sits at ic * cstride + s * pstride
+    const int64_t cstride = sh.nhwc ? 1 : sh.in_plane(), pstride = sh.nhwc ? sh.C : 1;
 
     uint4 a_reg[MI];
     uint4 b_reg[2];
@@ -122,10 +129,11 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
                                             0 <= ih && ih < (sh.H - 1) * sh.ups + 1 && ih % sh.ups == 0 &&
                                             0 <= iw && iw < (sh.W - 1) * sh.ups + 1 && iw % sh.ups == 0;
                             if (on)
-                                val = xn[((int64_t)ic * sh.D + id / sh.upsd) * HW + (int64_t)(ih / sh.ups) * sh.W +
-                                         iw / sh.ups];
+                                val = xn[(int64_t)ic * cstride +
+                                         ((int64_t)(id / sh.upsd) * HW + (int64_t)(ih / sh.ups) * sh.W + iw / sh.ups) *
+                                             pstride];
                         } else if (0 <= id && id < sh.D && 0 <= ih && ih < sh.H && 0 <= iw && iw < sh.W) {
-                            val = xn[((int64_t)ic * sh.D + id) * HW + (int64_t)ih * sh.W + iw];
+                            val = xn[(int64_t)ic * cstride + ((int64_t)id * HW + (int64_t)ih * sh.W + iw) * pstride];
                         }
                     }
                     v[e] = val;
@@ -180,21 +188,25 @@ void igemm_generic_kernel(Shape sh, const uint16_t *__restrict__ src, const uint
         __syncthreads();
     }
 
-    // ---- epilogue: y[n][oc][q] = acc + bias[oc]
+    // ---- epilogue: y[n][oc][q] (NHWC: y[n][q][oc]) = acc + bias[oc], then the
+    // optional ReLU and bf16 rounding
     const int64_t plane = sh.out_plane();
+    const int64_t ocs = sh.nhwc ? 1 : plane, qs = sh.nhwc ? sh.Co : 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t px = j0 + wn * 64 + j * 32 + (lane & 31);
         if (px >= P) continue;
         const int64_t n = px / plane, q = px - n * plane;
-        float *yb = y + n * sh.Co * plane + q;
+        const int64_t yb = n * sh.Co * plane + q * qs;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ocl = m0 + wm * (BM / 2) + i * 32 + mfma32_row(r, lane);
                 const int oc = oc_base + ocl;
-                if (ocl < Cog) yb[(int64_t)oc * plane] = acc[i][j][r] + (bias ? bias[oc] : 0.f);
+                if (ocl < Cog)
+                    store_out(y, yb + (int64_t)oc * ocs, acc[i][j][r] + (bias ? bias[oc] : 0.f), sh.out_bf16,
+                              sh.relu);
             }
     }
 }

@@ -161,7 +161,9 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     const uint32_t q0 = (uint32_t)(((int64_t)od * sh.Ho + oh0) * sh.Wo);
     // this workgroup's 64 output channels of image n, 32-bit offsets
     const int nch = min(kOcBlock, sh.Co - oc0);
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + ((int64_t)n * sh.Co + oc0) * plane, (uint32_t)(nch * plane * 4));
+    const int ob_ = sh.out_bf16 ? 2 : 4;                 // output element bytes (bf16 or fp32)
+    const __amdgpu_buffer_rsrc_t yr =
+        make_rsrc((char *)y + ((int64_t)n * sh.Co + oc0) * plane * ob_, (uint32_t)(nch * plane * ob_));
     const int nfrag = (npx + 31) / 32;
     for (int f = wave; f < nfrag; f += 4) {
         const int p = f * 32 + (lane & 31);
@@ -194,7 +196,7 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
         // rows), so it splits into soffset + voffset; bias comes from LDS in
         // the loop (volatile: not held in registers across fragments).
         const int hrow = 4 * (lane >> 5);
-        const uint32_t pvo = p < npx ? (q0 + (uint32_t)p + (uint32_t)hrow * (uint32_t)plane) * 4 : kOob;
+        const uint32_t pvo = p < npx ? (q0 + (uint32_t)p + (uint32_t)hrow * (uint32_t)plane) * (uint32_t)ob_ : kOob;
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
@@ -206,8 +208,13 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
                 for (int e = 0; e < 4; ++e) {
                     const int c = ob * 32 + 8 * g + e;             // channel without the lane-half rows
                     const uint32_t vo = c + hrow < nch ? pvo : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ob][4 * g + e] + bb[e]), yr, (int)vo,
-                                                          (int)((uint32_t)c * (uint32_t)plane * 4), 0);
+                    const int so = (int)((uint32_t)c * (uint32_t)plane * (uint32_t)ob_);
+                    float v = acc[ob][4 * g + e] + bb[e];
+                    if (sh.relu) v = fmaxf(v, 0.f);
+                    if (sh.out_bf16)
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(v), yr, (int)vo, so, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)vo, so, 0);
                 }
             }
     }
@@ -264,7 +271,7 @@ size_t smem_bytes(const SmallKPlan &pl) {
 }  // namespace
 
 bool smallk_supported(const Shape &sh) {
-    if (!sh.plain() || sh.kgemm() > kMaxK) return false;
+    if (!sh.plain() || sh.nhwc || sh.kgemm() > kMaxK) return false;
     if (patch_elems(sh, 1, false) > kPatchElems) return false;
     if ((int64_t)kOcBlock * sh.out_plane() * 4 >= (INT64_C(1) << 31)) return false;   // one output block per buffer range
     return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);

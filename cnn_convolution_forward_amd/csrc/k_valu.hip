@@ -14,6 +14,9 @@
 // Dilation d places the taps d inputs apart ("PyTorch tensor products and
 // conv2d/conv3d dimension semantics", 4.2-4.3).
 //
+// x and y may be channels-last (sh.nhwc), and the store may apply ReLU and
+// round to bf16 (sh.relu, sh.out_bf16).
+//
 // Used for the fp32 path and for thin layers (C_in*K^dims small) where the
 // reduction is too short for the matrix cores.
 #include "conv_internal.h"
@@ -46,21 +49,25 @@ void direct_kernel(Shape sh, const T *__restrict__ x, const T *__restrict__ w,
     const int64_t HW = (int64_t)sh.H * sh.W;
     const int64_t taps = sh.taps();
     const int id0 = od * sh.sd - sh.pd, ih0 = oh * sh.s - sh.p, iw0 = ow * sh.s - sh.p;
-    float *yp = y + n * sh.Co * plane + (px - n * plane);
+    const int64_t q = px - n * plane;
+    // NCHW: channel planes; NHWC: channel fastest (x and y)
+    const int64_t cstride = sh.nhwc ? 1 : sh.in_plane(), pstride = sh.nhwc ? sh.C : 1;
+    const int64_t ocs = sh.nhwc ? 1 : plane;
+    const int64_t yb = n * sh.Co * plane + (sh.nhwc ? q * sh.Co : q);
 
     // (group, channel block) pairs, nblk blocks per group, strided over grid.y
     for (int by = blockIdx.y; by < sh.G * nblk; by += gridDim.y) {
         const int grp = by / nblk;
         const int ocl0 = (by - grp * nblk) * OCB;      // first channel of the block inside its group
         const int oc0 = grp * Cog + ocl0;
-        const T *xn = x + (n * sh.C + (int64_t)grp * Cg) * sh.in_plane();
+        const T *xn = x + n * sh.C * sh.in_plane() + (int64_t)grp * Cg * cstride;
 
         float acc[OCB];
 #pragma unroll
         for (int o = 0; o < OCB; ++o) acc[o] = 0.f;
 
         for (int ic = 0; ic < Cg; ++ic) {
-            const T *xc = xn + (int64_t)ic * sh.in_plane();
+            const T *xc = xn + (int64_t)ic * cstride;
             const T *wc = w + (int64_t)ic * taps;
             for (int kd = 0; kd < sh.Kd; ++kd) {
                 const int id = id0 + kd * sh.dild;
@@ -71,7 +78,7 @@ void direct_kernel(Shape sh, const T *__restrict__ x, const T *__restrict__ w,
                     for (int kw = 0; kw < sh.K; ++kw) {
                         const int iw = iw0 + kw * sh.dil;
                         if (iw < 0 || iw >= sh.W) continue;
-                        const float xv = ld(xc, (int64_t)id * HW + (int64_t)ih * sh.W + iw);
+                        const float xv = ld(xc, ((int64_t)id * HW + (int64_t)ih * sh.W + iw) * pstride);
                         const int64_t tap = ((int64_t)kd * sh.K + kh) * sh.K + kw;
 #pragma unroll
                         for (int o = 0; o < OCB; ++o) {
@@ -86,7 +93,7 @@ void direct_kernel(Shape sh, const T *__restrict__ x, const T *__restrict__ w,
 #pragma unroll
         for (int o = 0; o < OCB; ++o) {
             const int oc = oc0 + o;
-            if (ocl0 + o < Cog) yp[(int64_t)oc * plane] = acc[o] + (bias ? bias[oc] : 0.f);
+            if (ocl0 + o < Cog) store_out(y, yb + (int64_t)oc * ocs, acc[o] + (bias ? bias[oc] : 0.f), sh.out_bf16, sh.relu);
         }
     }
 }

@@ -50,4 +50,20 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 constexpr uint32_t kOob = 0x80000000u;     // buffer offset past any valid byte: loads 0, stores dropped
 
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The output epilogue of every kernel: optional ReLU, then an fp32 store or a
+// bf16 store (y then holds uint16 bits) at element index i.
+__device__ __forceinline__ void store_out(float *y, int64_t i, float v, int out_bf16, int relu) {
+    if (relu) v = fmaxf(v, 0.f);
+    if (out_bf16)
+        reinterpret_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else
+        y[i] = v;
+}
+
 }  // namespace convfwd

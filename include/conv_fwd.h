@@ -267,6 +267,44 @@ CONV_API conv_status_t conv_fwd_explicit_bf16(const conv_params_t *params, const
                                               const uint16_t *w, const float *bias, float *y,
                                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- options: channels-last layout, ReLU, bf16 output ---------------------
+ *
+ * layout CONV_LAYOUT_NHWC: x is (N, [D,] H, W, C_in) and y is (N, [D_out,]
+ * H_out, W_out, C_out), the channel index fastest (channels_last, "PyTorch
+ * tensor products and conv2d/conv3d dimension semantics", 6.3); w stays
+ * (C_out, C_in/G, K, K[, K]).  relu = 1: y = max(y, 0) after the bias (the
+ * activation that follows the convolution in the same page, 6.2).
+ * out_dtype CONV_OUT_BF16: y holds bf16 bits, the fp32 result rounded to the
+ * nearest bf16, ties to even; accumulation stays fp32.  A NULL options
+ * pointer means NCHW, fp32, no ReLU. */
+typedef enum { CONV_LAYOUT_NCHW = 0, CONV_LAYOUT_NHWC = 1 } conv_layout_t;
+typedef enum { CONV_OUT_F32 = 0, CONV_OUT_BF16 = 1 } conv_out_t;
+typedef struct {
+    int layout;      /* conv_layout_t, for x and y                  */
+    int out_dtype;   /* conv_out_t                                   */
+    int relu;        /* 0 or 1                                       */
+} conv_options_t;
+
+/* Workspace conv_fwd_ex_bf16 can use (the packed weights of the 3x3 kernels,
+ * which take NCHW with any epilogue); 0 when none, or on invalid arguments. */
+CONV_API size_t conv_fwd_ex_workspace_bytes(const conv_params_t *params, const conv_options_t *opts, int algo);
+
+/* conv_fwd_bf16 with options.  y is float* (fp32) or uint16_t* (bf16 bits)
+ * as out_dtype says.  workspace: NULL, or 16-byte aligned device memory of
+ * at least conv_fwd_ex_workspace_bytes() bytes (overwritten).  Kernels that
+ * do not take an option step aside for the general ones: channels-last runs
+ * on the general implicit GEMM and the direct VALU kernel; the 3x3, pointwise
+ * and depthwise kernels apply ReLU and bf16 output in their own epilogue.
+ * Extra errors: CONV_ERR_PARAM for an unknown layout, out_dtype or relu
+ * value; CONV_ERR_WORKSPACE as for conv2d_fwd_bf16_ws. */
+CONV_API conv_status_t conv_fwd_ex_bf16(const conv_params_t *params, const conv_options_t *opts, const uint16_t *x,
+                                        const uint16_t *w, const float *bias, void *y, void *workspace,
+                                        size_t workspace_bytes, int algo, void *stream);
+
+/* fp32 twin (VALU route). */
+CONV_API conv_status_t conv_fwd_ex_f32(const conv_params_t *params, const conv_options_t *opts, const float *x,
+                                       const float *w, const float *bias, void *y, int algo, void *stream);
+
 /* ---- backward: gradients of y = conv(x, w) + b ----------------------------
  *
  * With upstream gradient dout (the shape of y) ("Hand-writing Conv2D", 5.1;

@@ -237,3 +237,21 @@ def test_backward_validation():
     assert bw(db=DO) == 5                 # db over dout
     assert bw(db=Y + 8) == 5              # db over dw
     assert bw(ws=DO + 32) == 5            # workspace over dout
+
+
+def test_options_validation():
+    prm = _gp()
+    f = lambda o, y=Y, algo=0: B.conv_fwd_ex_bf16(prm, o, X, Wp, BIAS, y, None, 0, algo, None)
+    assert f(B.ConvOptions(2, 0, 0)) == 2           # unknown layout
+    assert f(B.ConvOptions(0, 3, 0)) == 2           # unknown output dtype
+    assert f(B.ConvOptions(0, 0, 2)) == 2           # relu not 0/1
+    assert B.conv_fwd_ex_bf16(None, None, X, Wp, BIAS, Y, None, 0, 0, None) == 1
+    assert B.conv_fwd_ex_f32(prm, B.ConvOptions(0, 0, 0), X, Wp, BIAS, None, 0, None) == 1
+    assert B.conv_fwd_ex_f32(prm, B.ConvOptions(1, 1, 1), X, Wp, BIAS, Y, 1, None) == 7   # MFMA is bf16-only
+    assert f(B.ConvOptions(0, 1, 0), y=X + 2) == 5   # bf16 output over x
+    # 3x3 NCHW layers offer the packed-weight workspace with any epilogue; NHWC does not
+    big = B.make_params((64, 128, 56, 56), (128, 128, 3, 3), 1, 1, 1, 1)
+    assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(0, 1, 1), 0) == 128 * 128 * 9 * 2
+    assert B.conv_fwd_ex_workspace_bytes(big, None, 0) == 128 * 128 * 9 * 2
+    assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(1, 0, 0), 0) == 0
+    assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(0, 0, 5), 0) == 0
