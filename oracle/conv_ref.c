@@ -30,10 +30,12 @@
  * Parity pins live in tests/test_oracle_pins.py (plain convolution),
  * tests/test_oracle_pins_general.py (dilation and groups),
  * tests/test_oracle_pins_backward.py (gradients) and
- * tests/test_oracle_pins_epilogue.py (ReLU, bf16 output, channels-last); every
- * function here is pinned.
+ * tests/test_oracle_pins_epilogue.py (ReLU, bf16 output, channels-last) and
+ * tests/test_oracle_pins_winograd.py (Winograd F(2x2,3x3)); every function here
+ * is pinned.
  */
 #include <stdint.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <string.h>
 #include <math.h>
@@ -685,6 +687,121 @@ int oracle_conv_nhwc(int ndim, const double *x, const double *w, const double *b
               y[o] = acc + (bias ? bias[oc] : 0.0);
               if (S) S[o] = mag;
             }
+    return 0;
+}
+
+/* ---- Winograd F(2x2, 3x3) ---------------------------------------------------
+ *
+ * [Why use matrix multiplication for convolution, 5.1]: for an r x r kernel
+ * and an m x m output block the minimal filtering algorithm uses (m+r-1)^2
+ * multiplications instead of m^2 r^2 (F(2x2,3x3): 16 instead of 36), for 3x3
+ * kernels, stride 1 and dilation 1 only; it trades multiplications for
+ * transform additions and loses accuracy at low precision.  The page names
+ * the method but not its matrices; these are the published minimal-filtering
+ * ones of F(2,3) (Lavin and Gray, "Fast Algorithms for Convolutional Neural
+ * Networks", 2016), nested for two dimensions:
+ *     B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1]
+ *     G   = [1 0 0; 1/2 1/2 1/2; 1/2 -1/2 1/2; 0 0 1]
+ *     A^T = [1 1 1 0; 0 1 -1 -1]
+ * Steps for each output channel k and 2x2 output block b (input block d:
+ * the 4x4 input patch starting at (2*bh - p, 2*bw - p), zero outside):
+ *     U[k][c] = G g[k][c] G^T       (4x4, the transformed 3x3 filter)
+ *     V[c][b] = B^T d[c][b] B       (4x4, the transformed input block)
+ *     M[k][b] = sum over c of U[k][c] * V[c][b]   (elementwise: 16 products per c)
+ *     Y[k][b] = A^T M[k][b] A       (2x2, cropped at the output edge)
+ * plus bias.  In fp64 this equals the direct convolution up to rounding (and
+ * exactly on integer data, the halves in G being exact).
+ * Besides y, Sw holds per output the sum over c and the 16 transform points of
+ * |A coefficient| * |U| * |V|: the scale of the error when U and V are rounded
+ * to a narrow format before the products.  Sw may be NULL. */
+static void wino_mat_4x3_3x4(const double G[4][3], const double g[3][3], double out[4][4])
+{
+    double t[4][3];
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 3; ++j) {
+            t[i][j] = 0.0;
+            for (int l = 0; l < 3; ++l) t[i][j] += G[i][l] * g[l][j];
+        }
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+            out[i][j] = 0.0;
+            for (int l = 0; l < 3; ++l) out[i][j] += t[i][l] * G[j][l];
+        }
+}
+
+int oracle_winograd_f2x2_3x3(const double *x, const double *w, const double *bias, double *y, double *Sw,
+                             int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t p)
+{
+    static const double BT[4][4] = {{1, 0, -1, 0}, {0, 1, 1, 0}, {0, -1, 1, 0}, {0, 1, 0, -1}};
+    static const double Gm[4][3] = {{1, 0, 0}, {0.5, 0.5, 0.5}, {0.5, -0.5, 0.5}, {0, 0, 1}};
+    static const double AT[2][4] = {{1, 1, 1, 0}, {0, 1, -1, -1}};
+    const int64_t Ho = oracle_out_dim(H, 3, 1, p), Wo = oracle_out_dim(W, 3, 1, p);
+    if (Ho < 0 || Wo < 0 || N < 1 || C < 1 || Co < 1) return -1;
+    const int64_t TH = (Ho + 1) / 2, TW = (Wo + 1) / 2;
+    /* U for every (k, c) */
+    double *U = (double *)malloc(sizeof(double) * 16 * Co * C);
+    if (!U) return -1;
+    for (int64_t k = 0; k < Co; ++k)
+        for (int64_t c = 0; c < C; ++c) {
+            double g[3][3], u[4][4];
+            for (int i = 0; i < 3; ++i)
+                for (int j = 0; j < 3; ++j) g[i][j] = w[((k * C + c) * 3 + i) * 3 + j];
+            wino_mat_4x3_3x4(Gm, g, u);
+            for (int i = 0; i < 16; ++i) U[(k * C + c) * 16 + i] = u[i / 4][i % 4];
+        }
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t bh = 0; bh < TH; ++bh)
+        for (int64_t bw = 0; bw < TW; ++bw) {
+            /* V for every c of this block */
+            double *V = (double *)malloc(sizeof(double) * 16 * C);
+            if (!V) continue;
+            for (int64_t c = 0; c < C; ++c) {
+                double d[4][4], t[4][4];
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 4; ++j) {
+                        const int64_t ih = 2 * bh - p + i, iw = 2 * bw - p + j;
+                        d[i][j] = (0 <= ih && ih < H && 0 <= iw && iw < W) ? x[((n * C + c) * H + ih) * W + iw] : 0.0;
+                    }
+                for (int i = 0; i < 4; ++i)          /* t = B^T d */
+                    for (int j = 0; j < 4; ++j) {
+                        t[i][j] = 0.0;
+                        for (int l = 0; l < 4; ++l) t[i][j] += BT[i][l] * d[l][j];
+                    }
+                for (int i = 0; i < 4; ++i)          /* V = t B */
+                    for (int j = 0; j < 4; ++j) {
+                        double v = 0.0;
+                        for (int l = 0; l < 4; ++l) v += t[i][l] * BT[j][l];
+                        V[c * 16 + i * 4 + j] = v;
+                    }
+            }
+            for (int64_t k = 0; k < Co; ++k) {
+                double M[16], Ma[16];
+                for (int i = 0; i < 16; ++i) { M[i] = 0.0; Ma[i] = 0.0; }
+                for (int64_t c = 0; c < C; ++c)
+                    for (int i = 0; i < 16; ++i) {
+                        const double uv = U[(k * C + c) * 16 + i] * V[c * 16 + i];
+                        M[i] += uv;
+                        Ma[i] += fabs(uv);
+                    }
+                for (int a = 0; a < 2; ++a)
+                    for (int b = 0; b < 2; ++b) {
+                        const int64_t oh = 2 * bh + a, ow = 2 * bw + b;
+                        if (oh >= Ho || ow >= Wo) continue;
+                        double acc = 0.0, mag = 0.0;  /* (A^T M A)[a][b] */
+                        for (int i = 0; i < 4; ++i)
+                            for (int j = 0; j < 4; ++j) {
+                                acc += AT[a][i] * M[i * 4 + j] * AT[b][j];
+                                mag += fabs(AT[a][i] * AT[b][j]) * Ma[i * 4 + j];
+                            }
+                        const int64_t o = ((n * Co + k) * Ho + oh) * Wo + ow;
+                        y[o] = acc + (bias ? bias[k] : 0.0);
+                        if (Sw) Sw[o] = mag;
+                    }
+            }
+            free(V);
+        }
+    free(U);
     return 0;
 }
 

@@ -86,6 +86,8 @@ def lib():
         L.oracle_epilogue.argtypes = [_dp, _dp, _i64, ctypes.c_int, ctypes.c_int]
         L.oracle_conv_nhwc.restype = ctypes.c_int
         L.oracle_conv_nhwc.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp] + [_i64] * 11
+        L.oracle_winograd_f2x2_3x3.restype = ctypes.c_int
+        L.oracle_winograd_f2x2_3x3.argtypes = [_dp, _dp, _dp, _dp, _dp] + [_i64] * 6
         L.oracle_col2im_dilated.restype = ctypes.c_int
         L.oracle_col2im_dilated.argtypes = [ctypes.c_int, _dp, _dp] + [_i64] * 9
         L.oracle_num_threads.restype = ctypes.c_int
@@ -397,6 +399,26 @@ def conv_nhwc(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, with_S=Tru
     if rc != 0:
         raise ValueError("oracle_conv_nhwc rejected the shape")
     return (y, S) if with_S else y
+
+
+def winograd_f2x2_3x3(x, w, bias=None, pad=1):
+    """y and Sw of a 3x3, stride-1 convolution by Winograd F(2x2, 3x3) in fp64
+    [Why use matrix multiplication for convolution, 5.1]; Sw is the
+    transform-domain magnitude sum (see conv_ref.c)."""
+    x, w = decode(x), decode(w)
+    b = None if bias is None else decode(bias)
+    N, C, H, W = x.shape
+    Co = w.shape[0]
+    if w.shape != (Co, C, 3, 3):
+        raise ValueError("Winograd F(2x2,3x3) takes (C_out, C_in, 3, 3) weights")
+    Ho, Wo = out_dim(H, 3, 1, pad), out_dim(W, 3, 1, pad)
+    if Ho < 0 or Wo < 0:
+        raise ValueError("kernel larger than padded input")
+    y = np.empty((N, Co, Ho, Wo), np.float64)
+    Sw = np.empty_like(y)
+    if lib().oracle_winograd_f2x2_3x3(_p(x), _p(w), _p(b), _p(y), _p(Sw), N, C, H, W, Co, pad) != 0:
+        raise ValueError("oracle_winograd_f2x2_3x3 rejected the shape")
+    return y, Sw
 
 
 def num_threads() -> int:

@@ -8,7 +8,8 @@ from an axis, groups interleaved, the group's channel offset lost, the dilated
 span mis-sized; in the backward pass: dx overwritten, dW from w, db over one
 image, the stride or group offset lost, col2im overwriting; in the epilogue:
 bf16 ties rounded away or truncated, ReLU keeping negatives, the channels-last
-group offset lost), builds it with gcc, and runs the matching pin file
+group offset lost; in Winograd: a transform sign or coefficient, the output
+rows, the block origin), builds it with gcc, and runs the matching pin file
 (tests/test_oracle_pins*.py) against that build in a subprocess.  The run must fail.  Runs on the CPU only.
 """
 import os
@@ -75,15 +76,27 @@ MUTANTS_EPILOGUE = {
     "nhwc_group_offset_dropped": ("* W + ix) * C + grp * Cg;", "* W + ix) * C + 0 * grp * Cg;"),
 }
 
+# Mistakes in Winograd F(2x2,3x3), caught by test_oracle_pins_winograd.py.
+MUTANTS_WINOGRAD = {
+    "wino_bt_sign": ("static const double BT[4][4] = {{1, 0, -1, 0}, {0, 1, 1, 0}, {0, -1, 1, 0}, {0, 1, 0, -1}};",
+                     "static const double BT[4][4] = {{1, 0, 1, 0}, {0, 1, 1, 0}, {0, -1, 1, 0}, {0, 1, 0, -1}};"),
+    "wino_g_coefficient": ("{0.5, -0.5, 0.5}, {0, 0, 1}};", "{0.5, -0.5, 1.0}, {0, 0, 1}};"),
+    "wino_at_rows_swapped": ("static const double AT[2][4] = {{1, 1, 1, 0}, {0, 1, -1, -1}};",
+                             "static const double AT[2][4] = {{0, 1, -1, -1}, {1, 1, 1, 0}};"),
+    "wino_block_origin": ("const int64_t ih = 2 * bh - p + i, iw = 2 * bw - p + j;",
+                          "const int64_t ih = 2 * bh - p + i, iw = 2 * bw + j;"),
+}
+
 CASES = [(n, "test_oracle_pins.py") for n in sorted(MUTANTS)] + \
         [(n, "test_oracle_pins_general.py") for n in sorted(MUTANTS_GENERAL)] + \
         [(n, "test_oracle_pins_backward.py") for n in sorted(MUTANTS_BACKWARD)] + \
-        [(n, "test_oracle_pins_epilogue.py") for n in sorted(MUTANTS_EPILOGUE)]
+        [(n, "test_oracle_pins_epilogue.py") for n in sorted(MUTANTS_EPILOGUE)] + \
+        [(n, "test_oracle_pins_winograd.py") for n in sorted(MUTANTS_WINOGRAD)]
 
 
 @pytest.mark.parametrize("name,pins", CASES)
 def test_planted_mistake_is_caught(name, pins, tmp_path):
-    old, new = {**MUTANTS, **MUTANTS_GENERAL, **MUTANTS_BACKWARD, **MUTANTS_EPILOGUE}[name]
+    old, new = {**MUTANTS, **MUTANTS_GENERAL, **MUTANTS_BACKWARD, **MUTANTS_EPILOGUE, **MUTANTS_WINOGRAD}[name]
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not found once: %s" % name
     mutant_c = tmp_path / "conv_ref_mutant.c"
