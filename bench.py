@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="conv3x3_bf16")
-    ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit"])
+    ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit", "winograd"])
     ap.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"], help="layout of x and y (forward)")
     ap.add_argument("--out", default="f32", choices=["f32", "bf16"], help="output dtype (forward)")
     ap.add_argument("--relu", action="store_true", help="fused ReLU after the bias (forward)")
@@ -100,6 +100,8 @@ class Runner:
         self.wl, self.route, self.backward = wl, route, backward
         # (layout, out dtype, relu); None = NCHW, fp32, no ReLU
         self.options = None if options in (None, ("nchw", "f32", False)) else options
+        if route == "winograd" and self.options is None:
+            self.options = ("nchw", "f32", False)       # Winograd runs through the options entry point
         self.t = synth.make_inputs(wl, seed=seed)
         t = self.t
         if t.x.dtype == np.uint16:

@@ -20,7 +20,7 @@ CONV_OK = 0
 STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_NULL", 2: "CONV_ERR_PARAM", 3: "CONV_ERR_SHAPE",
                 4: "CONV_ERR_OVERFLOW", 5: "CONV_ERR_ALIAS", 6: "CONV_ERR_WORKSPACE",
                 7: "CONV_ERR_ALGO", 8: "CONV_ERR_HIP"}
-ALGO = {"auto": 0, "mfma": 1, "valu": 2}
+ALGO = {"auto": 0, "mfma": 1, "valu": 2, "winograd": 3}
 
 # Every symbol include/conv_fwd.h declares.
 EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",

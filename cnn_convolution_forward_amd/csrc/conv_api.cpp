@@ -548,6 +548,8 @@ size_t conv_fwd_ex_workspace_bytes(const conv_params_t *prm, const conv_options_
     if (!prm) return 0;
     Shape sh;
     if (shape_from_params(prm, sh) != CONV_OK || apply_options(opts, sh) != CONV_OK) return 0;
+    if (algo == CONV_ALGO_WINOGRAD)
+        return convfwd::winograd_supported(sh) ? convfwd::winograd_workspace_bytes(sh) : 0;
     if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU || pick_route(sh, algo) != CONV_ALGO_MFMA) return 0;
     return convfwd::igemm_workspace_bytes(sh, (const void *)256, (const void *)256);
 }
@@ -560,6 +562,13 @@ conv_status_t conv_fwd_ex_bf16(const conv_params_t *prm, const conv_options_t *o
     conv_status_t st = shape_from_params(prm, sh);
     if (st != CONV_OK) return st;
     if ((st = apply_options(opts, sh)) != CONV_OK) return st;
+    if (algo == CONV_ALGO_WINOGRAD) {
+        if (!convfwd::winograd_supported(sh)) return CONV_ERR_ALGO;
+        const size_t need = convfwd::winograd_workspace_bytes(sh);
+        if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256) return CONV_ERR_WORKSPACE;
+        if ((st = check_alias(sh, 2, x, w, bias, y, workspace, workspace_bytes)) != CONV_OK) return st;
+        return to_status(convfwd::launch_winograd_bf16(sh, x, w, bias, (float *)y, workspace, (hipStream_t)stream));
+    }
     return fwd_bf16_sh(sh, x, w, bias, (float *)y, algo, stream, workspace != nullptr, workspace, workspace_bytes);
 }
 

@@ -74,6 +74,12 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
 int wgrad_splits(const Shape &sh);
 hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
                              hipStream_t st);
+// Winograd F(2x2, 3x3): 2D, K=3, stride 1, dilation 1, groups 1, NCHW, C % 16 == 0.
+bool winograd_supported(const Shape &sh);
+size_t winograd_workspace_bytes(const Shape &sh);
+// ws: 256-byte aligned, winograd_workspace_bytes(sh) bytes (transformed weights and inputs).
+hipError_t launch_winograd_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                                void *ws, hipStream_t st);
 // db[oc] = sum of dout over images and positions (fixed order).
 hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *db, hipStream_t st);
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);

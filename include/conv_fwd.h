@@ -74,7 +74,11 @@ typedef enum {
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_MFMA = 1,      /* implicit GEMM on bf16 matrix cores, fp32 accumulate */
-    CONV_ALGO_VALU = 2       /* direct convolution, fp32 FMA on the vector ALUs       */
+    CONV_ALGO_VALU = 2,      /* direct convolution, fp32 FMA on the vector ALUs       */
+    CONV_ALGO_WINOGRAD = 3   /* Winograd F(2x2,3x3) ("Why use matrix multiplication for
+                                convolution", 5.1): conv_fwd_ex_bf16 only, with a
+                                workspace; 3x3, stride 1, dilation 1, groups 1, NCHW,
+                                C_in % 16 == 0.  Never chosen by AUTO. */
 } conv_algo_t;
 
 /* floor((in + 2*pad - K)/stride) + 1, or -1 if in < 1, K < 1, stride < 1,
@@ -286,17 +290,26 @@ typedef struct {
 } conv_options_t;
 
 /* Workspace conv_fwd_ex_bf16 can use (the packed weights of the 3x3 kernels,
- * which take NCHW with any epilogue); 0 when none, or on invalid arguments. */
+ * which take NCHW with any epilogue) or, with algo CONV_ALGO_WINOGRAD, needs
+ * (the fp16 transformed weights, 16 x C_out x C_in, and transformed input
+ * blocks, 16 x N*ceil(H_out/2)*ceil(W_out/2) x C_in); 0 when none, or on
+ * invalid arguments or a shape Winograd does not take. */
 CONV_API size_t conv_fwd_ex_workspace_bytes(const conv_params_t *params, const conv_options_t *opts, int algo);
 
 /* conv_fwd_bf16 with options.  y is float* (fp32) or uint16_t* (bf16 bits)
- * as out_dtype says.  workspace: NULL, or 16-byte aligned device memory of
- * at least conv_fwd_ex_workspace_bytes() bytes (overwritten).  Kernels that
+ * as out_dtype says.  workspace: NULL, or 16-byte aligned (256-byte aligned
+ * with Winograd) device memory of at least conv_fwd_ex_workspace_bytes()
+ * bytes (overwritten).  Kernels that
  * do not take an option step aside for the general ones: channels-last runs
  * on the general implicit GEMM and the direct VALU kernel; the 3x3, pointwise
  * and depthwise kernels apply ReLU and bf16 output in their own epilogue.
- * Extra errors: CONV_ERR_PARAM for an unknown layout, out_dtype or relu
- * value; CONV_ERR_WORKSPACE as for conv2d_fwd_bf16_ws. */
+ * algo CONV_ALGO_WINOGRAD computes U = G g G^T and V = B^T d B in fp16, the
+ * 16 transform-point GEMMs on the matrix cores with fp32 accumulation, and
+ * A^T M A per 2x2 block; its error scale is the transform-domain magnitude
+ * sum, up to ~4x the direct one on N(0,1) data (the page's low-precision
+ * caveat).  Extra errors: CONV_ERR_PARAM for an unknown layout, out_dtype or
+ * relu value; CONV_ERR_WORKSPACE as for conv2d_fwd_bf16_ws (required with
+ * Winograd); CONV_ERR_ALGO when Winograd does not take the shape. */
 CONV_API conv_status_t conv_fwd_ex_bf16(const conv_params_t *params, const conv_options_t *opts, const uint16_t *x,
                                         const uint16_t *w, const float *bias, void *y, void *workspace,
                                         size_t workspace_bytes, int algo, void *stream);
