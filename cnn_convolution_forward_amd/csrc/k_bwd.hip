@@ -22,7 +22,9 @@
 // positions per stage, contiguous along positions), B = X_col^T gathered from
 // x with bounds checks (32 positions x 128 columns (ic, kd, kh, kw)), both
 // staged in LDS with the reduction contiguous, v_mfma_f32_32x32x16_bf16.
-// Depthwise layers (one input channel per group) have their own VALU kernel.
+// Depthwise layers (one input channel per group) have their own VALU kernel,
+// and 3x3 stride-1 pad-1 layers a kernel that shares the dout operand across
+// the nine taps.
 #include "conv_internal.h"
 #include "mfma_common.h"
 
@@ -277,6 +279,120 @@ bool wgrad_dw_ok(const Shape &sh) {
            sh.out_plane() * 2 < (INT64_C(1) << 31);
 }
 
+// Weight gradient of a 3x3, stride-1, pad-1 layer (NCHW, W % 8 == 0, C_in and
+// C_out multiples of 64): the nine taps share one operand.  For tap (kh, kw),
+// dW[:, :, kh, kw] = dout_mat (C_out x positions) @ x_shift(kh, kw)^T, and
+// dout_mat does not depend on the tap, so each step of 16 positions loads
+// the dout operand once and builds the nine x operands from three input rows:
+// a lane's 8 positions lie in one row at an 8-aligned column ow0, so
+// x[ih][ow0 + kw - 1 .. +7] is the aligned 16-byte chunk at ow0 shifted by
+// kw - 1 elements, completed by the neighbouring chunks' edge elements
+// (v_alignbyte).  A workgroup: 64 output x 64 input channels x all 9 taps
+// over one range of positions; wave (wm, wn) holds a 32 x 32 block per tap
+// (9 accumulator tiles).  Partials are written as [split][tap][oc][ic].
+__global__ __launch_bounds__(256, 1)
+void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout, float *__restrict__ part,
+                     int C, int Co, int H, int W, int P, int chunk) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int ic0 = blockIdx.x * 64 + wn * 32, oc0 = blockIdx.y * 64 + wm * 32;
+    const int split = blockIdx.z;
+    const int k_begin = split * chunk;
+    const int k_end = k_begin + chunk < P ? k_begin + chunk : P;
+    const int r32 = lane & 31, half = lane >> 5;
+    const int plane = H * W;
+    const int oc = oc0 + r32, ic = ic0 + r32;
+    // buffer resources over one channel plane series: dout[n][oc], x[n][ic] for all n
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout, (uint32_t)((int64_t)(P / plane) * Co * plane * 2));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)(P / plane) * C * plane * 2));
+
+    f32x16_t acc[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+    // operands of one step: a (dout, 16 B), per kernel row the aligned chunk
+    // and the neighbouring chunks' edge dwords; two sets, the next step's
+    // loads in flight while the current step's MFMAs run
+    struct Ops {
+        uint4 a, cur[3];
+        uint32_t prv[3], nxt[3];
+    };
+    auto load = [&](int kk, Ops &o) {
+        const int pp = kk + 8 * half;                 // this lane's first position (8-aligned)
+        const bool ok = pp < k_end;
+        const int n = pp / plane, q = pp - n * plane;
+        const int oh = q / W, ow0 = q - oh * W;
+        o.a = bload16(dr, ok ? (uint32_t)(((n * Co + oc) * plane + q) * 2) : kOob, 0);
+        const int xb = (n * C + ic) * plane;
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int ih = oh + kh - 1;
+            const bool rok = ok && 0 <= ih && ih < H;
+            const uint32_t ro = (uint32_t)((xb + ih * W + ow0) * 2);
+            o.cur[kh] = bload16(xr, rok ? ro : kOob, 0);
+            o.prv[kh] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(rok && ow0 > 0 ? ro - 4 : kOob), 0, 0);
+            o.nxt[kh] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(rok && ow0 + 8 < W ? ro + 16 : kOob), 0, 0);
+        }
+    };
+    auto compute = [&](const Ops &o) {
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const uint32_t c0 = o.cur[kh].x, c1 = o.cur[kh].y, c2 = o.cur[kh].z, c3 = o.cur[kh].w;
+            // kw = 0: columns ow0-1 .. ow0+6; kw = 1: the chunk; kw = 2: ow0+1 .. ow0+8
+            const uint4 b0 = make_uint4(__builtin_amdgcn_alignbyte(c0, o.prv[kh], 2),
+                                        __builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
+                                        __builtin_amdgcn_alignbyte(c3, c2, 2));
+            const uint4 b2 = make_uint4(__builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
+                                        __builtin_amdgcn_alignbyte(c3, c2, 2),
+                                        __builtin_amdgcn_alignbyte(o.nxt[kh], c3, 2));
+            acc[3 * kh + 0] = mfma32x32x16(o.a, b0, acc[3 * kh + 0]);
+            acc[3 * kh + 1] = mfma32x32x16(o.a, o.cur[kh], acc[3 * kh + 1]);
+            acc[3 * kh + 2] = mfma32x32x16(o.a, b2, acc[3 * kh + 2]);
+        }
+    };
+
+    Ops o0, o1;
+    int kk = k_begin;
+    if (kk < k_end) load(kk, o0);
+    // two steps per iteration so that the operand sets keep fixed registers
+    for (; kk < k_end; kk += 32) {
+        if (kk + 16 < k_end) load(kk + 16, o1);
+        compute(o0);
+        if (kk + 16 >= k_end) break;
+        if (kk + 32 < k_end) load(kk + 32, o0);
+        compute(o1);
+    }
+
+    // part[split][tap][oc][ic]: 32 lanes on 32 consecutive input channels
+    float *pp = part + (int64_t)split * 9 * Co * C;
+#pragma unroll
+    for (int t = 0; t < 9; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pp[((int64_t)t * Co + oc0 + mfma32_row(r, lane)) * C + ic] = acc[t][r];
+}
+
+// dw[oc][ic][tap] = sum over splits, in order, of part[split][tap][oc][ic].
+__global__ __launch_bounds__(256)
+void sum_splits_tap_kernel(const float *__restrict__ part, float *__restrict__ dw, int Co, int C, int splits) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;      // (tap, oc, ic), ic fastest
+    const int64_t n = (int64_t)9 * Co * C;
+    if (e >= n) return;
+    float s = 0.f;
+    for (int i = 0; i < splits; ++i) s += part[(int64_t)i * n + e];
+    const int ic = (int)(e % C);
+    const int64_t r = e / C;
+    const int ocv = (int)(r % Co), tap = (int)(r / Co);
+    dw[((int64_t)ocv * C + ic) * 9 + tap] = s;
+}
+
+bool wgrad3x3_ok(const Shape &sh) {
+    return sh.ndim == 2 && sh.plain() && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.W % 8 == 0 && sh.C % 64 == 0 &&
+           sh.Co % 64 == 0 && sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
+}
+
 // dw[e] = sum over splits, in order, of part[split][e].
 __global__ __launch_bounds__(256)
 void sum_splits_kernel(const float *__restrict__ part, float *__restrict__ dw, int64_t n, int splits) {
@@ -316,6 +432,14 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
 }
 
 int wgrad_splits(const Shape &sh) {
+    if (wgrad3x3_ok(sh)) {
+        // about 512 workgroups (two rounds of one per CU) over (C/64) x (C_out/64) channel tiles
+        const int64_t tiles = (int64_t)(sh.C / 64) * (sh.Co / 64);
+        int64_t s = (512 + tiles - 1) / tiles;
+        const int64_t most = sh.pixels() / 256;               // at least 16 steps of 16 positions
+        if (s > most) s = most;
+        return (int)(s < 1 ? 1 : s);
+    }
     if (wgrad_dw_ok(sh)) {
         // about 1024 workgroups: output channels x ranges of images
         int s = (1024 + sh.Co - 1) / sh.Co;
@@ -338,6 +462,19 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     const int64_t P = sh.pixels();
     const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
     const int splits = wgrad_splits(sh);
+    if (wgrad3x3_ok(sh)) {
+        const int Pi = (int)P;
+        const int chunk = (int)(((P + splits - 1) / splits + 15) / 16 * 16);
+        const int used = (int)((P + chunk - 1) / chunk);
+        dim3 grid((unsigned)(sh.C / 64), (unsigned)(sh.Co / 64), (unsigned)used);
+        hipLaunchKernelGGL(wgrad3x3_kernel, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi, chunk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n = (int64_t)9 * sh.Co * sh.C;
+        hipLaunchKernelGGL(sum_splits_tap_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, sh.Co,
+                           sh.C, used);
+        return hipGetLastError();
+    }
     if (wgrad_dw_ok(sh)) {
         const int per = (sh.N + splits - 1) / splits;
         const int used = (sh.N + per - 1) / per;          // ranges that hold images

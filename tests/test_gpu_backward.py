@@ -59,6 +59,8 @@ SMALL = [
     (3, 1, 3, (6, 5, 7), 8, 3, 2, 2, 2, 1),       # 3D, stride 2, dilation 2
     (2, 2, 6, (13, 11), 12, 5, 2, 2, 2, 6),       # depthwise, multiplier 2, K 5, stride 2, dilation 2
     (2, 3, 5, (9, 10), 5, 3, 1, 1, 1, 5),         # depthwise 3x3 on the depthwise weight-gradient kernel
+    (2, 2, 64, (10, 16), 128, 3, 1, 1, 1, 1),     # dW on the 3x3 shared-dout kernel (W % 8, C % 64)
+    (2, 3, 128, (7, 24), 64, 3, 1, 1, 1, 1),      # same kernel, odd H, ragged split ranges
 ]
 
 
@@ -72,7 +74,7 @@ def test_backward_small(case):
     compare(db, rdb, Sdb, TAU, label="db %s" % (case,))
 
 
-@pytest.mark.parametrize("case", SMALL[:6] + SMALL[9:], ids=lambda c: "x".join(map(str, c[:3] + tuple(c[3]) + c[4:])))
+@pytest.mark.parametrize("case", SMALL[:6] + SMALL[9:11] + SMALL[13:], ids=lambda c: "x".join(map(str, c[:3] + tuple(c[3]) + c[4:])))
 def test_backward_integer_exact(case):
     wl, x, w, dout = _inputs(*case, seed=7, integer=True)
     dx, dw, db = _gpu(wl, x, w, dout)
