@@ -139,8 +139,10 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (
 }
 
 // OUT: 0 = fp32 output, 1 = bf16 output (rounded to nearest even); relu:
-// max(y, 0) before the store.
-template <int D, int OUT>
+// max(y, 0) before the store.  NHWC: x and y channels-last -- the loader
+// then copies each pixel's 8 channels as they are (no transpose) and the
+// epilogue writes each pixel's channels contiguously.
+template <int D, int OUT, int NHWC>
 __global__ __launch_bounds__(kThreads, 2)
 void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
                       const float *__restrict__ bias, float *__restrict__ y,
@@ -181,17 +183,28 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     const int rho = tid % kInRows, rest = tid / kInRows;
     const int pg = rest % (W / 8), g8 = in_active ? rest / (W / 8) : 0;
     const int ih = r0 - 1 + rho;
-    const uint32_t ivoff = (in_active && ih >= 0 && ih < H)
-                               ? (uint32_t)((g8 * 8 * HW + ih * W + pg * 8) * 2) : kOob;
+    const bool ivalid = in_active && ih >= 0 && ih < H;
+    // NCHW: channel g8*8 + e's 8 pixels are 16 contiguous bytes (e = channel);
+    // NHWC: pixel pg*8 + e's channels g8*8 .. +7 are (e = pixel)
+    const uint32_t ivoff = !ivalid ? kOob
+                           : NHWC ? (uint32_t)(((ih * W + pg * 8) * C + g8 * 8) * 2)
+                                  : (uint32_t)((g8 * 8 * HW + ih * W + pg * 8) * 2);
     const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + 1) * kPix + in_half(g8, rho) * 16);
-    const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = chan_bytes * kIc;
+    const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = NHWC ? (uint32_t)kIc * 2 : chan_bytes * kIc;
+    const uint32_t e_bytes = NHWC ? (uint32_t)C * 2 : chan_bytes;
     uint4 xin[8];
     auto load_x = [&](int s) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xin[e] = bload16(xr, ivoff, (uint32_t)s * stage_bytes + e * chan_bytes);
+        for (int e = 0; e < 8; ++e) xin[e] = bload16(xr, ivoff + e * e_bytes, (uint32_t)s * stage_bytes);
     };
     auto store_x = [&](int buf) {
         if (!in_active) return;
+        if (NHWC) {
+            uint8_t *dst = ibuf + buf * G::IN_BYTES + idst;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(dst + j * kPix) = xin[j];
+            return;
+        }
         const uint32_t *v = reinterpret_cast<const uint32_t *>(xin);   // v[e*4 + j/2]: channel e, pixels j, j+1
         uint8_t *dst = ibuf + buf * G::IN_BYTES + idst;
 #pragma unroll
@@ -293,8 +306,10 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     float *const epi = reinterpret_cast<float *>(smem);
     constexpr int kOutB = OUT ? 2 : 4;                   // bytes per output element
     constexpr int kPer = 16 / kOutB;                     // outputs per 16-byte store
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB,
-                                                (uint32_t)kOc * HW * kOutB);
+    // NCHW: this tile's 64 channel planes; NHWC: the image (pixel-major, C_out channels each)
+    const __amdgpu_buffer_rsrc_t yr =
+        NHWC ? make_rsrc((char *)y + (int64_t)n * HW * Co * kOutB, (uint32_t)HW * Co * kOutB)
+             : make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB, (uint32_t)kOc * HW * kOutB);
     constexpr int kChPitch = kRows * W + 4;
     constexpr int kChunks = kEpiOc * kRows * W / kPer;   // 16-byte chunks per pass
 #pragma unroll
@@ -315,15 +330,32 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
         for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
             const int cid = k * kThreads + tid;
             if (kChunks % kThreads == 0 || cid < kChunks) {
-                const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
-                const int row = (kPer * e) / W;
-                const bool ok = r0 + row < H;
-                const uint32_t vo =
-                    ok ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + kPer * e) * kOutB) : kOob;
-                const float *src = epi + ocl * kChPitch + kPer * e;
+                float f[8];
+                uint32_t vo;
+                if (NHWC) {
+                    // chunk = (pixel, group of kPer channels of this pass)
+                    constexpr int kq = kEpiOc / kPer;
+                    const int px = cid / kq, qd = cid - px * kq;
+                    const int row = px / W, col = px - row * W;
+                    vo = r0 + row < H ? (uint32_t)((((r0 + row) * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB)
+                                      : kOob;
+#pragma unroll
+                    for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * kChPitch + row * W + col];
+                } else {
+                    const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
+                    const int row = (kPer * e) / W;
+                    vo = r0 + row < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + kPer * e) * kOutB) : kOob;
+                    const float *src = epi + ocl * kChPitch + kPer * e;
+                    const float4 lo = *reinterpret_cast<const float4 *>(src);
+                    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+                    if (kPer == 8) {
+                        const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+                        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+                    }
+                }
                 u32x4_t va;
                 if (OUT == 0) {
-                    float4 a4 = *reinterpret_cast<const float4 *>(src);
+                    float4 a4 = make_float4(f[0], f[1], f[2], f[3]);
                     if (relu) {
                         a4.x = fmaxf(a4.x, 0.f); a4.y = fmaxf(a4.y, 0.f);
                         a4.z = fmaxf(a4.z, 0.f); a4.w = fmaxf(a4.w, 0.f);
@@ -331,9 +363,6 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
                     va = (u32x4_t){__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
                                    __float_as_uint(a4.w)};
                 } else {
-                    const float4 lo = *reinterpret_cast<const float4 *>(src);
-                    const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-                    const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                     uint32_t b[8];
 #pragma unroll
                     for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(relu ? fmaxf(f[u], 0.f) : f[u]);
@@ -351,10 +380,11 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
     (void)w;
     const int64_t HW = (int64_t)sh.H * sh.W;
-    return sh.plain() && !sh.nhwc && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
+    return sh.plain() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
            sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
            (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range
+           (!sh.nhwc || HW * sh.Co * 4 < (INT64_C(1) << 31)) &&           // channels-last: one output image
            (int64_t)kPackOcBlock * sh.C * 9 * 2 < (INT64_C(1) << 31) &&
            (int64_t)sh.N * ((sh.H + kRows - 1) / kRows) * 2 < (INT64_C(1) << 31) &&
            ((uintptr_t)x % 16) == 0;
@@ -366,13 +396,15 @@ hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint1
     const int64_t blocks = (int64_t)sh.N * rb * 2;       // tiles x two 64-channel halves
     const int remap = (blocks % 8 == 0) ? 1 : 0;
     dim3 grid((unsigned)blocks, (unsigned)(sh.Co / kPackOcBlock));
-#define CONV3X3CG_LAUNCH(DV)                                                                                   \
-    if (sh.out_bf16)                                                                                           \
-        hipLaunchKernelGGL((conv3x3cg_kernel<DV, 1>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
-                           sh.Co, rb, remap, sh.relu);                                                         \
-    else                                                                                                       \
-        hipLaunchKernelGGL((conv3x3cg_kernel<DV, 0>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
-                           sh.Co, rb, remap, sh.relu)
+#define CONV3X3CG_GO(DV, O, L)                                                                                  \
+    hipLaunchKernelGGL((conv3x3cg_kernel<DV, O, L>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
+                       sh.Co, rb, remap, sh.relu)
+#define CONV3X3CG_LAUNCH(DV)                                              \
+    if (sh.nhwc) {                                                        \
+        if (sh.out_bf16) CONV3X3CG_GO(DV, 1, 1); else CONV3X3CG_GO(DV, 0, 1); \
+    } else {                                                              \
+        if (sh.out_bf16) CONV3X3CG_GO(DV, 1, 0); else CONV3X3CG_GO(DV, 0, 0); \
+    }
     switch (sh.W / 4) {
         case 8: CONV3X3CG_LAUNCH(8); break;
         case 10: CONV3X3CG_LAUNCH(10); break;
@@ -382,6 +414,7 @@ hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint1
         default: return hipErrorInvalidValue;
     }
 #undef CONV3X3CG_LAUNCH
+#undef CONV3X3CG_GO
     return hipGetLastError();
 }
 

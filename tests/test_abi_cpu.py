@@ -249,9 +249,9 @@ def test_options_validation():
     assert B.conv_fwd_ex_f32(prm, B.ConvOptions(0, 0, 0), X, Wp, BIAS, None, 0, None) == 1
     assert B.conv_fwd_ex_f32(prm, B.ConvOptions(1, 1, 1), X, Wp, BIAS, Y, 1, None) == 7   # MFMA is bf16-only
     assert f(B.ConvOptions(0, 1, 0), y=X + 2) == 5   # bf16 output over x
-    # 3x3 NCHW layers offer the packed-weight workspace with any epilogue; NHWC does not
+    # 3x3 layers offer the packed-weight workspace with any epilogue and layout
     big = B.make_params((64, 128, 56, 56), (128, 128, 3, 3), 1, 1, 1, 1)
     assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(0, 1, 1), 0) == 128 * 128 * 9 * 2
     assert B.conv_fwd_ex_workspace_bytes(big, None, 0) == 128 * 128 * 9 * 2
-    assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(1, 0, 0), 0) == 0
+    assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(1, 0, 0), 0) == 128 * 128 * 9 * 2   # channels-last too
     assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(0, 0, 5), 0) == 0

@@ -92,7 +92,7 @@ def test_options(case, opts):
     wl = _wl(*shape)
     t = synth.make_inputs(wl, seed=sum(shape[3]) + shape[4])
     y_ref, S = _reference(wl, t, layout)
-    got = _run(wl, t, layout, out_dtype, relu, algo, use_ws and layout == "nchw")
+    got = _run(wl, t, layout, out_dtype, relu, algo, use_ws)
     _check(got, y_ref, S, relu, out_dtype, TAU["bf16"], False, "%s %s" % (name, opts))
 
 
@@ -103,7 +103,7 @@ def test_options_integer_exact(case, layout):
     wl = _wl(*shape)
     t = synth.make_inputs(wl, seed=3, integer=True)
     y_ref, _ = _reference(wl, t, layout)
-    got = _run(wl, t, layout, "bf16", True, algo, use_ws and layout == "nchw")
+    got = _run(wl, t, layout, "bf16", True, algo, use_ws)
     _check(got, y_ref, None, True, "bf16", 0, True, "%s %s" % (name, layout))
 
 
@@ -122,3 +122,13 @@ def test_full_3x3_layer_bf16_relu():
     y_ref, S = _reference(wl, t, "nchw")
     got = _run(wl, t, "nchw", "bf16", True, "auto", True)
     _check(got, y_ref, S, True, "bf16", TAU["bf16"], False, "full 3x3 bf16 relu")
+
+
+@pytest.mark.parametrize("layout,out_dtype,relu", [("nhwc", "f32", False), ("nhwc", "bf16", True)])
+def test_full_3x3_layer_channels_last(layout, out_dtype, relu):
+    """The 3x3 layer stored channels-last, on the column-group kernel."""
+    wl = synth.WORKLOADS["conv3x3_bf16"]
+    t = synth.make_inputs(wl)
+    y_ref, S = _reference(wl, t, layout)
+    got = _run(wl, t, layout, out_dtype, relu, "auto", True)
+    _check(got, y_ref, S, relu, out_dtype, TAU["bf16"], False, "full 3x3 %s %s" % (layout, out_dtype))
