@@ -181,11 +181,128 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
         }
 }
 
+// Channels-last pointwise layer: x is (pixels, C_in) and y (pixels, C_out),
+// so Y = X @ W_row^T with both operands contiguous along the reduction (C_in):
+// a tile of 128 pixels x 128 output channels, 32-channel stages, both
+// operands staged in LDS as [row][k] and read in 16-byte pieces (no
+// transposes).  The accumulator rows are pixels and its columns output
+// channels, so 32 lanes store 32 consecutive channels of one pixel.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 4)))
+void conv1x1_nhwc_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                         const float *__restrict__ bias, float *__restrict__ y,
+                         int C, int Co, int64_t P, int npt, int ncb, int remap, int out_bf16, int relu) {
+    constexpr int kLd = kBK + 8;          // 80-byte rows: 16-byte reads of 8 consecutive rows are conflict-free
+    __shared__ __align__(16) uint16_t As[2][kBN][kLd];      // pixels x k
+    __shared__ __align__(16) uint16_t Bs[2][kBM][kLd];      // output channels x k
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int T = npt * ncb;
+    int L = blockIdx.x;
+    if (remap) L = (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
+    const int pt = L / ncb, ob = L - pt * ncb;
+    const int m0 = ob * kBM;                   // first output channel
+    const int64_t j0 = (int64_t)pt * kBN;      // first pixel
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(P * C * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)Co * C * 2));
+    // loader units u -> (row u/4, k-quad u%4), two per thread for each operand
+    uint32_t a_off[2], b_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = tid + 256 * i;
+        const int row = u >> 2, kq = u & 3;
+        a_off[i] = (j0 + row < P) ? (uint32_t)(((j0 + row) * C + kq * 8) * 2) : kOob;
+        b_off[i] = (m0 + row < Co) ? (uint32_t)(((int64_t)(m0 + row) * C + kq * 8) * 2) : kOob;
+    }
+    uint4 a_reg[2], b_reg[2];
+    auto load = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            a_reg[i] = bload16(xr, a_off[i], (uint32_t)(kt * kBK * 2));
+            b_reg[i] = bload16(wr, b_off[i], (uint32_t)(kt * kBK * 2));
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = tid + 256 * i;
+            *reinterpret_cast<uint4 *>(&As[buf][u >> 2][(u & 3) * 8]) = a_reg[i];
+            *reinterpret_cast<uint4 *>(&Bs[buf][u >> 2][(u & 3) * 8]) = b_reg[i];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[i][0][r] = 0.f;
+            acc[i][1][r] = 0.f;
+        }
+
+    const int nk = C / kBK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int kof = kk * 16 + (lane >> 5) * 8;
+            uint4 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const uint4 *>(&As[buf][wm * 64 + i * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const uint4 *>(&Bs[buf][wn * 64 + j * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // y[pixel][oc] = acc + bias[oc] (then ReLU, bf16): lane column = output channel
+    const int ob_ = out_bf16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)(P * Co * ob_));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int oc = m0 + wn * 64 + j * 32 + (lane & 31);
+        const bool cok = oc < Co;
+        const float bv = (bias && cok) ? bias[oc] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t px = j0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+                const bool ok = cok && px < P;
+                const uint32_t vo = ok ? (uint32_t)((px * Co + oc) * ob_) : kOob;
+                float v = acc[i][j][r] + bv;
+                if (relu) v = fmaxf(v, 0.f);
+                if (out_bf16)
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(v), yr, (int)vo, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)vo, 0, 0);
+            }
+    }
+}
+
 }  // namespace
 
 bool conv1x1_supported(const Shape &sh, const void *x, const void *w) {
     const int64_t plane = sh.out_plane();
-    return sh.plain() && !sh.nhwc && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
+    if (sh.nhwc)   // channels-last: any pixel count; x and y below 2 GiB
+        return sh.plain() && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 &&
+               sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 4 < (INT64_C(1) << 31) &&
+               sh.w_elems() * 2 < (INT64_C(1) << 31) && ((uintptr_t)x % 16) == 0 && ((uintptr_t)w % 16) == 0;
+    return sh.plain() && sh.K == 1 && sh.s == 1 && sh.p == 0 && sh.C % kBK == 0 && plane % 8 == 0 &&
            plane < (INT64_C(1) << 31) && sh.x_elems() * 2 < (INT64_C(1) << 31) &&
            sh.y_elems() * 4 < (INT64_C(1) << 31) &&
            sh.w_elems() * 2 < (INT64_C(1) << 31) &&
@@ -200,6 +317,11 @@ hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_
     const int ncb = (sh.Co + kBM - 1) / kBM;
     const int64_t T = (int64_t)npt * ncb;
     const int remap = (T % 8 == 0) ? 1 : 0;
+    if (sh.nhwc) {
+        hipLaunchKernelGGL(conv1x1_nhwc_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co, P, npt,
+                           ncb, remap, sh.out_bf16, sh.relu);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co,
                        plane, P, npt, ncb, remap, sh.out_bf16, sh.relu);
     return hipGetLastError();
