@@ -71,7 +71,8 @@ hipError_t launch_igemm_upsampled_bf16(const Shape &sh, const uint16_t *x, const
 void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wflip, hipStream_t st);
 // Weight gradient: partial sums over `splits` pixel ranges into part
 // (splits x Co x C/G*taps fp32), then their fixed-order sum into dw.
-int wgrad_splits(const Shape &sh);
+int wgrad_splits(const Shape &sh, bool aligned);      // aligned: x and dout 16-byte aligned
+int64_t wgrad_workspace_floats(const Shape &sh);        // enough for either alignment
 hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
                              hipStream_t st);
 // Winograd F(2x2, 3x3): 2D, K=3, stride 1, dilation 1, groups 1, NCHW, C % 16 == 0.
@@ -81,7 +82,10 @@ size_t winograd_workspace_bytes(const Shape &sh);
 hipError_t launch_winograd_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
                                 void *ws, hipStream_t st);
 // db[oc] = sum of dout over images and positions (fixed order).
-hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *db, hipStream_t st);
+// db from dout; part holds (ranges x C_out) floats and may be the front of
+// the weight-gradient workspace
+int bias_grad_ranges(const Shape &sh);
+hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *part, float *db, hipStream_t st);
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w);
 // Workspace for the repacked weights of the 3x3 kernel (bytes).
 size_t conv3x3s1_workspace_bytes(const Shape &sh);

@@ -403,24 +403,46 @@ void sum_splits_kernel(const float *__restrict__ part, float *__restrict__ dw, i
     dw[e] = s;
 }
 
-// db[oc]: one workgroup per channel; each thread sums a strided subset in
-// order, then a fixed-shape tree in LDS.
+// Partial bias gradient: workgroup (oc, r) sums channel oc over images
+// [r*per, min(N, (r+1)*per)), reading the images' rows of dout as one flat
+// run of bf16 values (16 bytes a load when the base is 16-byte aligned and
+// rows are whole 16-byte units);
+// each thread adds its values in order, then a fixed-shape tree in LDS.
+// part[r][oc] receives the sum, so the result does not depend on timing.
 __global__ __launch_bounds__(256)
-void bias_grad_kernel(const uint16_t *__restrict__ dout, float *__restrict__ db, int N, int Co, int64_t plane) {
+void bias_grad_part_kernel(const uint16_t *__restrict__ dout, float *__restrict__ part, int N, int Co,
+                           int64_t plane, int per, int vec) {
     __shared__ float red[256];
-    const int oc = blockIdx.x, tid = threadIdx.x;
-    float s = 0.f;
-    for (int n = 0; n < N; ++n) {
-        const uint16_t *p = dout + ((int64_t)n * Co + oc) * plane;
-        for (int64_t q = tid; q < plane; q += 256) s += bf16_to_f32(p[q]);
+    const int oc = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int n0 = r * per, n1 = min(N, n0 + per);
+    float s0 = 0.f, s1 = 0.f;
+    if (vec) {
+        const int64_t units = plane >> 3;                 // 16-byte units per image row
+        const int64_t total = (int64_t)(n1 - n0) * units;
+        for (int64_t u = tid; u < total; u += 256) {
+            const int64_t n = n0 + u / units, q = u % units;
+            const uint4 v = *(const uint4 *)(dout + ((n * Co + oc) * plane + q * 8));
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s0 += __uint_as_float(wv[j] << 16);
+                s1 += __uint_as_float(wv[j] & 0xffff0000u);
+            }
+        }
+    } else {
+        const int64_t total = (int64_t)(n1 - n0) * plane;
+        for (int64_t u = tid; u < total; u += 256) {
+            const int64_t n = n0 + u / plane, q = u % plane;
+            s0 += bf16_to_f32(dout[(n * Co + oc) * plane + q]);
+        }
     }
-    red[tid] = s;
+    red[tid] = s0 + s1;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
         if (tid < h) red[tid] += red[tid + h];
         __syncthreads();
     }
-    if (tid == 0) db[oc] = red[0];
+    if (tid == 0) part[(int64_t)r * Co + oc] = red[0];
 }
 
 }  // namespace
@@ -431,8 +453,8 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
                        sh.Cg(), sh.Cog(), sh.G, (int)sh.taps(), total);
 }
 
-int wgrad_splits(const Shape &sh) {
-    if (wgrad3x3_ok(sh)) {
+int wgrad_splits(const Shape &sh, bool aligned) {
+    if (aligned && wgrad3x3_ok(sh)) {
         // about 512 workgroups (two rounds of one per CU) over (C/64) x (C_out/64) channel tiles
         const int64_t tiles = (int64_t)(sh.C / 64) * (sh.Co / 64);
         int64_t s = (512 + tiles - 1) / tiles;
@@ -457,12 +479,20 @@ int wgrad_splits(const Shape &sh) {
     return (int)s;
 }
 
+int64_t wgrad_workspace_floats(const Shape &sh) {
+    // the 3x3 kernel runs only on 16-byte aligned x and dout; size the
+    // workspace for whichever route the pointers select
+    const int a = wgrad_splits(sh, true), b = wgrad_splits(sh, false);
+    return (int64_t)(a > b ? a : b) * sh.w_elems();
+}
+
 hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
                              hipStream_t st) {
     const int64_t P = sh.pixels();
     const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
-    const int splits = wgrad_splits(sh);
-    if (wgrad3x3_ok(sh)) {
+    const bool aligned = (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0;
+    const int splits = wgrad_splits(sh, aligned);
+    if (aligned && wgrad3x3_ok(sh)) {
         const int Pi = (int)P;
         const int chunk = (int)(((P + splits - 1) / splits + 15) / 16 * 16);
         const int used = (int)((P + chunk - 1) / chunk);
@@ -515,9 +545,25 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     return hipGetLastError();
 }
 
-hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *db, hipStream_t st) {
-    hipLaunchKernelGGL(bias_grad_kernel, dim3((unsigned)sh.Co), dim3(256), 0, st, dout, db, sh.N, sh.Co,
-                       sh.out_plane());
+int bias_grad_ranges(const Shape &sh) {
+    // about 1024 workgroups, no more ranges than images, and the partials must
+    // fit in the front of the weight-gradient workspace (which they use before
+    // the weight kernels do)
+    int64_t r = (1024 + sh.Co - 1) / sh.Co;
+    if (r > sh.N) r = sh.N;
+    const int64_t room = wgrad_workspace_floats(sh) / sh.Co;
+    if (r > room) r = room;
+    return (int)(r < 1 ? 1 : r);
+}
+
+hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *part, float *db, hipStream_t st) {
+    const int r = bias_grad_ranges(sh), per = (sh.N + r - 1) / r;
+    const int ranges = (sh.N + per - 1) / per;
+    hipLaunchKernelGGL(bias_grad_part_kernel, dim3((unsigned)sh.Co, (unsigned)ranges), dim3(256), 0, st, dout, part,
+                       sh.N, sh.Co, sh.out_plane(), per,
+                       (int)(sh.out_plane() % 8 == 0 && (uintptr_t)dout % 16 == 0));
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((sh.Co + 255) / 256)), dim3(256), 0, st, part, db,
+                       (int64_t)sh.Co, ranges);
     return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ SMALL = [
     (2, 3, 5, (9, 10), 5, 3, 1, 1, 1, 5),         # depthwise 3x3 on the depthwise weight-gradient kernel
     (2, 2, 64, (10, 16), 128, 3, 1, 1, 1, 1),     # dW on the 3x3 shared-dout kernel (W % 8, C % 64)
     (2, 3, 128, (7, 24), 64, 3, 1, 1, 1, 1),      # same kernel, odd H, ragged split ranges
+    (2, 7, 16, (5, 6), 400, 1, 1, 0, 1, 1),       # db over image ranges of 3, 3, 1 (rows of 30: 2-byte loads)
+    (2, 7, 8, (4, 8), 300, 1, 1, 0, 1, 1),        # db over image ranges of 2, 2, 2, 1 (rows of 32: 16-byte loads)
 ]
 
 
@@ -105,6 +107,29 @@ def test_backward_full_3x3_layer_sampled(integer):
     d64 = synth.bf16_bits_to_f32(dout).astype(np.float64)
     rdb = d64.sum(axis=(0, 2, 3))
     compare(db, rdb, np.abs(d64).sum(axis=(0, 2, 3)), tau, exact=integer, label="db")
+
+
+def _misaligned(a):
+    """a device copy of bf16 bits `a` whose address is 2 bytes past a 16-byte boundary"""
+    buf = torch.empty(a.size + 8, dtype=torch.int16, device="cuda")
+    t = buf[1:1 + a.size].view(a.shape)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda())
+    assert t.data_ptr() % 16 == 2
+    return t
+
+
+def test_backward_misaligned_inputs():
+    """x and dout 2 bytes off a 16-byte boundary: the 3x3 weight-gradient
+    kernel and the 16-byte loads of the bias gradient are skipped for the
+    general routes, within the workspace the size query returns."""
+    wl, x, w, dout = _inputs(2, 2, 64, (10, 16), 128, 3, 1, 1, 1, 1, seed=11)
+    xt, dt, wt = _misaligned(x), _misaligned(dout), dev(w, None)
+    dx, dw, db = B.conv_backward(xt, wt, dt, 1, 1, 1, 1)
+    torch.cuda.synchronize()
+    (rdx, rdw, rdb), (Sdx, Sdw, Sdb) = oracle.conv_backward(x, w, dout, 1, 1, 1, 1)
+    compare(dx.cpu().numpy(), rdx, Sdx, TAU, label="dx")
+    compare(dw.cpu().numpy(), rdw, Sdw, TAU, label="dw")
+    compare(db.cpu().numpy(), rdb, Sdb, TAU, label="db")
 
 
 def test_backward_deterministic():
