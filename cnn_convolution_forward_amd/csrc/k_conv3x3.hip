@@ -452,10 +452,11 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 // Repack OIHW 3x3 weights for the PACKED kernel: for every 128-channel block
 // and 16-channel stage, the 36 KB image that stage occupies in LDS
 // ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  A workgroup
-// takes 16 output channels of one stage: it reads their 16 x 144 contiguous
-// source values with dword loads into LDS, then writes 288 16-byte units, 32
-// consecutive units (512 bytes) per tap.
-constexpr int kPackOc = 16;
+// takes 4 output channels of one stage (C_out / 4 x C_in / 16 workgroups, so
+// the few dependent memory trips of each overlap across the chip): it reads
+// their 4 x 144 contiguous source values with dword loads into LDS, then
+// writes 72 16-byte units, 8 consecutive units (128 bytes) per tap.
+constexpr int kPackOc = 4;
 
 __global__ __launch_bounds__(256)
 void pack_w3x3_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wp, int C, int Co) {

@@ -32,10 +32,12 @@
 //   input    [row 10][col RP][ic 16] at 32 bytes per pixel, an odd row pitch
 //            RP >= W + 2 and the two 16-byte halves swapped on bit 2 of the
 //            row, so the 8 rows of a fragment column hit 8 distinct 16-byte
-//            bank groups; double-buffered: the next stage is loaded into
-//            registers at the start of a stage and written transposed (NCHW
-//            keeps channels strided, the operand needs 8 consecutive) into
-//            the other buffer halfway through its MFMAs; one barrier a stage.
+//            bank groups; double-buffered: a stage's input is loaded into
+//            registers halfway through the stage before the previous one and
+//            written transposed (NCHW keeps channels strided, the operand
+//            needs 8 consecutive) into the other buffer halfway through the
+//            previous stage's MFMAs, so a whole stage of MFMA work covers the
+//            load; one barrier a stage.
 // Accumulator orientation D[px][oc]: lane l owns channel l % 32, and its 16
 // slots are pixels (rows 4*(l/32) .. +3) x (4 column groups); across its J
 // fragments a lane holds J consecutive columns of each (row, group).  The
@@ -255,6 +257,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     const float bv = bias ? bias[ocb + wm * 32 + l32] : 0.f;
     CONV3X3_WAIT_VMCNT(0);
     store_x(0);
+    if (S > 1) load_x(1);            // stored at the middle of stage 0
     __syncthreads();
 
     // accumulators start at this lane's channel bias
@@ -267,10 +270,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     for (int s = 0; s < S; ++s) {
         const int b = s & 1;
         const bool more = s + 1 < S;
-        if (more) {
-            dma_w(s + 1, b ^ 1);
-            load_x(s + 1);
-        }
+        if (more) dma_w(s + 1, b ^ 1);
         const uint8_t *wb = wbuf + b * kWStage + a_off;
         const uint8_t *ib = ibuf + b * G::IN_BYTES + b_base;
         const uint8_t *tb = ibuf + b * G::IN_BYTES + t_base;
@@ -282,16 +282,19 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
             T1[0] = *reinterpret_cast<const uint4 *>(tb + RP * kPix);
             T2[0] = *reinterpret_cast<const uint4 *>(tb + 2 * RP * kPix);
         }
-        // halfway through the stage the next stage's input (loaded at its
-        // start) goes into the other buffer, which nobody reads this stage
+        // halfway through the stage the next stage's input (loaded halfway
+        // through the previous stage, so a whole stage of MFMA work covers
+        // its latency) goes into the other buffer, which nobody reads this
+        // stage; the wait also covers the next stage's weights, copied since
+        // this stage's start.  Then the input of the stage after is loaded.
         auto mid = [&]() {
             if (more) {
                 CONV3X3_WAIT_VMCNT(0);
                 store_x(b ^ 1);
+                if (s + 2 < S) load_x(s + 2);
             }
         };
         cg_col<D, 0>(acc, A, B0, T1, T2, ib, tb, row7, mid);
-        CONV3X3_WAIT_VMCNT(0);      // next stage's weights in LDS
         __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
