@@ -32,12 +32,11 @@
 //   input    [row 10][col RP][ic 16] at 32 bytes per pixel, an odd row pitch
 //            RP >= W + 2 and the two 16-byte halves swapped on bit 2 of the
 //            row, so the 8 rows of a fragment column hit 8 distinct 16-byte
-//            bank groups; double-buffered: a stage's input is loaded into
-//            registers halfway through the stage before the previous one and
-//            written transposed (NCHW keeps channels strided, the operand
-//            needs 8 consecutive) into the other buffer halfway through the
-//            previous stage's MFMAs, so a whole stage of MFMA work covers the
-//            load; one barrier a stage.
+//            bank groups; double-buffered: stage s's input is loaded into
+//            registers halfway through stage s - 2 and written transposed
+//            (NCHW keeps channels strided, the operand needs 8 consecutive)
+//            into the other buffer halfway through stage s - 1, so a whole
+//            stage of MFMA work covers the load; one barrier a stage.
 // Accumulator orientation D[px][oc]: lane l owns channel l % 32, and its 16
 // slots are pixels (rows 4*(l/32) .. +3) x (4 column groups); across its J
 // fragments a lane holds J consecutive columns of each (row, group).  The
