@@ -12,12 +12,12 @@
 // lane n holds row n % 8, column c + D * (n / 8), with D = W / 4.  Moving one
 // column to the right maps fragment c onto fragment c + 1, so the horizontal
 // taps (kw = 0, 1, 2) of fragments c .. c + J - 1 all read the same J + 2
-// input fragments.  Moving one row down is a move by one lane inside each
-// 8-lane group (DPP), so kernel rows 1 and 2 reuse the row-0 fragments and
-// only the 8 lanes of the new bottom row read LDS.  Per 16-channel stage a
-// wave reads 9 weight fragments and J + 2 full input fragments (+ 2 (J + 2)
-// one-eighth reads) for 9 J MFMAs (20 KB for 63 MFMAs at J = 7, against
-// 126 KB when every tap reads both operands).
+// input fragments.  Kernel rows 1 and 2 read the same columns one and two
+// input rows further down (a plain LDS read each: moving the row-0 fragment
+// across lanes instead costs eight VALU operations per fragment between the
+// MFMAs, which measured slower).  Per 16-channel stage a wave reads 9
+// weight fragments and 3 (J + 2) input fragments for 9 J MFMAs (36 KB for
+// 63 MFMAs at J = 7, against 126 KB when every tap reads both operands).
 //
 // Tiling: a workgroup computes 64 output channels x 8 output rows x W (one
 // tile per workgroup), four waves in a 2 x 2 grid: 32 channels x J = D/2
@@ -82,22 +82,6 @@ struct Geo {
     static constexpr int UNITS = 2 * kInRows * (W / 8);   // input load units per stage
 };
 
-// Rows of a fragment one down: lane 8g + r takes lane 8g + r + 1 (DPP
-// row_shl:1 inside each 16-lane row).  Lanes 8g + 7 receive a wrong or zero
-// value and are overwritten by the caller.
-__device__ __forceinline__ uint4 rows_down(const uint4 &v) {
-    uint4 r;
-    r.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x101, 0xf, 0xf, true);
-    r.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x101, 0xf, 0xf, true);
-    r.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x101, 0xf, 0xf, true);
-    r.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x101, 0xf, 0xf, true);
-    return r;
-}
-
-__device__ __forceinline__ uint4 pick(bool c, const uint4 &a, const uint4 &b) {
-    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
-}
-
 // The MFMAs of input-fragment column q (column c0 - 1 + q of this wave's
 // range) and kernel row rr: the fragment serves output fragment j = q - kw
 // for the three horizontal taps kw.
@@ -111,32 +95,25 @@ __device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[Geo<D>::J], const uint4 
     }
 }
 
-// Column step q.  The kernel-row-0 fragment of column q comes from LDS; the
-// fragments of kernel rows 1 and 2 are the row-0 (row-1) fragment moved one
-// row down across lanes, plus one new row that only lanes 8g + 7 read from
-// LDS (8 of 64 lanes).  A step first issues the LDS reads of column q + 1,
-// then the 9 (or fewer) MFMAs of column q, so the reads have a column of
-// MFMA work to arrive.
+// Column step q.  The fragments of kernel rows 0, 1 and 2 of column q are
+// three LDS reads, one input row apart (ib, tb, ub).  A step first issues
+// the reads of column q + 1, then the 9 (or fewer) MFMAs of column q, so the
+// reads have a column of MFMA work to arrive.
 template <int D, int q, class Mid>
 __device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], uint4 (&B0)[2],
                                        uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, const uint8_t *tb,
-                                       bool row7, Mid &&mid) {
+                                       const uint8_t *ub, Mid &&mid) {
     constexpr int J = Geo<D>::J, RP = Geo<D>::RP, Q = J + 2;
     if constexpr (q + 1 < Q) {
         B0[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (q + 1) * kPix);
-        if (row7) {
-            T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (RP + q + 1) * kPix);
-            T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (2 * RP + q + 1) * kPix);
-        }
+        T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (q + 1) * kPix);
+        T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ub + (q + 1) * kPix);
     }
-    const uint4 b0 = B0[q & 1];
-    cg_mfma<D, 0>(acc, A, b0, q);
-    const uint4 b1 = pick(row7, T1[q & 1], rows_down(b0));
-    cg_mfma<D, 1>(acc, A, b1, q);
-    const uint4 b2 = pick(row7, T2[q & 1], rows_down(b1));
-    cg_mfma<D, 2>(acc, A, b2, q);
+    cg_mfma<D, 0>(acc, A, B0[q & 1], q);
+    cg_mfma<D, 1>(acc, A, T1[q & 1], q);
+    cg_mfma<D, 2>(acc, A, T2[q & 1], q);
     if constexpr (q == Q / 2) mid();
-    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, tb, row7, mid);
+    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, tb, ub, mid);
 }
 
 // OUT: 0 = fp32 output, 1 = bf16 output (rounded to nearest even); relu:
@@ -236,14 +213,17 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     // operand addresses: A (weights) row wm*32 + l32 of the tap, k half h
     // (swizzled on the row's bits 2-3, which the 64-row offset leaves alone);
     // B (input fragment) for fragment column c' = c0 - 1 + q at kernel row rr
-    // is b_base + (rr*RP + q) * 48
+    // is at (input row (l32 % 8) + rr, column c' + D*(l32 / 8)), with the
+    // 16-byte half swizzled on that input row: b_base, b1_base, b2_base for
+    // rr = 0, 1, 2, plus q * 32
     const uint32_t a_off = (uint32_t)((wm * 32 + l32) * 32 + ((h ^ wswz(l32)) * 16));
     const int c0 = wn * J;
     const uint32_t b_base = (uint32_t)((((l32 & 7) * RP) + D * (l32 >> 3) + c0) * kPix +
                                        in_half(h, l32 & 7) * 16);
-    const bool row7 = (l32 & 7) == 7;        // lanes that read the new row of kernel rows 1 and 2
-    // their rows 8 and 9 keep the unswapped halves
-    const uint32_t t_base = (uint32_t)(((7 * RP) + D * (l32 >> 3) + c0) * kPix + in_half(h, 8) * 16);
+    const uint32_t b1_base = (uint32_t)(((((l32 & 7) + 1) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                        in_half(h, (l32 & 7) + 1) * 16);
+    const uint32_t b2_base = (uint32_t)(((((l32 & 7) + 2) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                        in_half(h, (l32 & 7) + 2) * 16);
 
     // zero both input buffers: halo columns are never written again
     for (int i = tid; i < 2 * G::IN_BYTES / 16; i += kThreads)
@@ -272,15 +252,14 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
         if (more) dma_w(s + 1, b ^ 1);
         const uint8_t *wb = wbuf + b * kWStage + a_off;
         const uint8_t *ib = ibuf + b * G::IN_BYTES + b_base;
-        const uint8_t *tb = ibuf + b * G::IN_BYTES + t_base;
+        const uint8_t *tb = ibuf + b * G::IN_BYTES + b1_base;
+        const uint8_t *ub = ibuf + b * G::IN_BYTES + b2_base;
         uint4 A[9], B0[2], T1[2], T2[2];
 #pragma unroll
         for (int t = 0; t < 9; ++t) A[t] = *reinterpret_cast<const uint4 *>(wb + t * kTapBytes);
         B0[0] = *reinterpret_cast<const uint4 *>(ib);
-        if (row7) {
-            T1[0] = *reinterpret_cast<const uint4 *>(tb + RP * kPix);
-            T2[0] = *reinterpret_cast<const uint4 *>(tb + 2 * RP * kPix);
-        }
+        T1[0] = *reinterpret_cast<const uint4 *>(tb);
+        T2[0] = *reinterpret_cast<const uint4 *>(ub);
         // halfway through the stage the next stage's input (loaded halfway
         // through the previous stage, so a whole stage of MFMA work covers
         // its latency) goes into the other buffer, which nobody reads this
@@ -293,7 +272,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
                 if (s + 2 < S) load_x(s + 2);
             }
         };
-        cg_col<D, 0>(acc, A, B0, T1, T2, ib, tb, row7, mid);
+        cg_col<D, 0>(acc, A, B0, T1, T2, ib, tb, ub, mid);
         __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
