@@ -48,8 +48,9 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first: about 40 ms of continuous work brings the clocks to steady state")
     ap.add_argument("--workload", default="conv3x3_bf16")
     ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit", "winograd"])
     ap.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"], help="layout of x and y (forward)")
