@@ -451,39 +451,30 @@ void conv3x3s1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 
 // Repack OIHW 3x3 weights for the PACKED kernel: for every 128-channel block
 // and 16-channel stage, the 36 KB image that stage occupies in LDS
-// ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  A workgroup
-// takes 4 output channels of one stage (C_out / 4 x C_in / 16 workgroups, so
-// the few dependent memory trips of each overlap across the chip): it reads
-// their 4 x 144 contiguous source values with dword loads into LDS, then
-// writes 72 16-byte units, 8 consecutive units (128 bytes) per tap.
-constexpr int kPackOc = 4;
-
+// ([tap 9][oc 128][ic 16], 16-byte halves swizzled as in wswz).  One thread
+// per 16-byte unit of the packed array, in the array's order (so the stores
+// of a wave are 1 KB contiguous): it gathers the unit's 8 input channels of
+// one tap straight from the OIHW weights, a single memory round trip.
 __global__ __launch_bounds__(256)
 void pack_w3x3_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wp, int C, int Co) {
-    __shared__ uint32_t src[kPackOc * kIcStage * 9 / 2];
     const int S = C / kIcStage;
-    const int oc0 = blockIdx.x * kPackOc, st = blockIdx.y;
-    const int tid = threadIdx.x;
-    constexpr int kRowDw = kIcStage * 9 / 2;                  // 72 dwords per output channel
-    for (int i = tid; i < kPackOc * kRowDw; i += 256) {
-        const int r = i / kRowDw, c = i - r * kRowDw;
-        const uint32_t *row = reinterpret_cast<const uint32_t *>(w + ((int64_t)(oc0 + r) * C + st * kIcStage) * 9);
-        src[i] = row[c];
-    }
-    __syncthreads();
-    const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
-    const int ocb = oc0 / kOcTile;
-    uint16_t *chunk = wp + ((int64_t)ocb * S + st) * (9 * kOcTile * kIcStage);
-    for (int v = tid; v < 9 * kPackOc * 2; v += 256) {
-        const int t = v / (kPackOc * 2), r = v - t * (kPackOc * 2);
-        const int i = r >> 1, slot = r & 1;
-        const int ocl = (oc0 % kOcTile) + i;
-        const int h = slot ^ wswz(ocl);
-        uint16_t e8[8];
+    const int64_t total = (int64_t)Co * S * 18;
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= total) return;
+    // u = (((ocb * S + st) * 9 + t) * kOcTile + ocl) * 2 + slot
+    const int slot = (int)(u & 1);
+    int64_t r = u >> 1;
+    const int ocl = (int)(r % kOcTile);
+    r /= kOcTile;
+    const int t = (int)(r % 9);
+    r /= 9;
+    const int st = (int)(r % S), ocb = (int)(r / S);
+    const int h = slot ^ wswz(ocl);
+    const uint16_t *src = w + ((int64_t)(ocb * kOcTile + ocl) * C + st * kIcStage + h * 8) * 9 + t;
+    uint16_t e8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = s16[i * (kIcStage * 9) + (h * 8 + e) * 9 + t];
-        *reinterpret_cast<uint4 *>(chunk + ((int64_t)t * kOcTile * 2 + ocl * 2 + slot) * 8) = pack8(e8);
-    }
+    for (int e = 0; e < 8; ++e) e8[e] = src[e * 9];
+    reinterpret_cast<uint4 *>(wp)[u] = pack8(e8);
 }
 
 // MFMA column steps (32 pixels each) that the busier pixel-wave of a tile runs.
@@ -599,8 +590,9 @@ Plan make_plan(const Shape &sh, int slots) {
 }  // namespace
 
 void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st) {
-    hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)(sh.Co / kPackOc), (unsigned)(sh.C / kIcStage)),
-                       dim3(256), 0, st, w, wpack, sh.C, sh.Co);
+    const int64_t units = (int64_t)sh.Co * (sh.C / kIcStage) * 18;
+    hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, wpack, sh.C,
+                       sh.Co);
 }
 
 bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
