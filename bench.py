@@ -103,6 +103,11 @@ class Runner:
         self.options = None if options in (None, ("nchw", "f32", False)) else options
         if route == "winograd" and self.options is None:
             self.options = ("nchw", "f32", False)       # Winograd runs through the options entry point
+        if (self.options is None and not backward and not wl.plain and wl.dtype == "bf16" and
+                route in ("auto", "mfma")):
+            # dilation / groups: the workspace entry point (with its packed 3x3
+            # weights the column-group kernel takes dilation 1 or 2)
+            self.options = ("nchw", "f32", False)
         self.t = synth.make_inputs(wl, seed=seed)
         t = self.t
         if t.x.dtype == np.uint16:

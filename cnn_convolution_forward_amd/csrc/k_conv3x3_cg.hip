@@ -44,7 +44,13 @@
 // stores them back in 16-byte chunks as whole 8-row blocks of each channel,
 // contiguous in y (bias is the accumulators' initial value).
 //
-// Requirements (checked by the launcher): K = 3, s = 1, p = 1, C_in % 16 == 0,
+// Dilation d (1 or 2, with pad d): a tile's 8 output rows are r0 + d*i, one
+// row phase of a band of 8d rows, so kernel row kh of tile row i is again LDS
+// row i + kh (the input rows are loaded d apart); a horizontal tap moves d
+// fragment columns, so a pixel-wave steps through J + 2d input columns, and
+// the LDS rows carry d halo columns on each side.
+//
+// Requirements (checked by the launcher): K = 3, s = 1, p = d, groups 1, C_in % 16 == 0,
 // C_out % 128 == 0, W % 8 == 0, 32 <= W <= 64, packed weights, 16-byte
 // aligned x.
 #include "conv_internal.h"
@@ -72,11 +78,12 @@ constexpr int kEpiBytes = kEpiOc * (kRows * 64 + 4) * 4;   // largest pass image
 // bank groups.
 __device__ __forceinline__ int in_half(int h, int rho) { return h ^ ((rho >> 2) & 1); }
 
-template <int D>
+template <int D, int DL>
 struct Geo {
     static constexpr int W = 4 * D;
     static constexpr int J = D / 2;                       // fragments per pixel-wave
-    static constexpr int RP = (W + 2) | 1;                // odd input row pitch (pixels)
+    static constexpr int Q = J + 2 * DL;                  // input fragment columns per pixel-wave
+    static constexpr int RP = (W + 2 * DL) | 1;           // odd input row pitch (pixels), DL halo columns each side
     static constexpr int IN_BYTES = kInRows * RP * kPix;
     static constexpr int LDS = 2 * kWStage + 2 * IN_BYTES;
     static constexpr int UNITS = 2 * kInRows * (W / 8);   // input load units per stage
@@ -85,12 +92,12 @@ struct Geo {
 // The MFMAs of input-fragment column q (column c0 - 1 + q of this wave's
 // range) and kernel row rr: the fragment serves output fragment j = q - kw
 // for the three horizontal taps kw.
-template <int D, int RR>
-__device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], const uint4 &b, int q) {
-    constexpr int J = Geo<D>::J;
+template <int D, int DL, int RR>
+__device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[(Geo<D, DL>::J)], const uint4 (&A)[9], const uint4 &b, int q) {
+    constexpr int J = Geo<D, DL>::J;
 #pragma unroll
     for (int kw = 0; kw < 3; ++kw) {
-        const int j = q - kw;
+        const int j = q - DL * kw;
         if (j >= 0 && j < J) acc[j] = mfma32x32x16(b, A[RR * 3 + kw], acc[j]);
     }
 }
@@ -99,33 +106,33 @@ __device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[Geo<D>::J], const uint4 
 // three LDS reads, one input row apart (ib, tb, ub).  A step first issues
 // the reads of column q + 1, then the 9 (or fewer) MFMAs of column q, so the
 // reads have a column of MFMA work to arrive.
-template <int D, int q, class Mid>
-__device__ __forceinline__ void cg_col(f32x16_t (&acc)[Geo<D>::J], const uint4 (&A)[9], uint4 (&B0)[2],
+template <int D, int DL, int q, class Mid>
+__device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const uint4 (&A)[9], uint4 (&B0)[2],
                                        uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, const uint8_t *tb,
                                        const uint8_t *ub, Mid &&mid) {
-    constexpr int J = Geo<D>::J, RP = Geo<D>::RP, Q = J + 2;
+    constexpr int Q = Geo<D, DL>::Q;
     if constexpr (q + 1 < Q) {
         B0[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (q + 1) * kPix);
         T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (q + 1) * kPix);
         T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ub + (q + 1) * kPix);
     }
-    cg_mfma<D, 0>(acc, A, B0[q & 1], q);
-    cg_mfma<D, 1>(acc, A, T1[q & 1], q);
-    cg_mfma<D, 2>(acc, A, T2[q & 1], q);
+    cg_mfma<D, DL, 0>(acc, A, B0[q & 1], q);
+    cg_mfma<D, DL, 1>(acc, A, T1[q & 1], q);
+    cg_mfma<D, DL, 2>(acc, A, T2[q & 1], q);
     if constexpr (q == Q / 2) mid();
-    if constexpr (q + 1 < Q) cg_col<D, q + 1>(acc, A, B0, T1, T2, ib, tb, ub, mid);
+    if constexpr (q + 1 < Q) cg_col<D, DL, q + 1>(acc, A, B0, T1, T2, ib, tb, ub, mid);
 }
 
 // OUT: 0 = fp32 output, 1 = bf16 output (rounded to nearest even); relu:
 // max(y, 0) before the store.  NHWC: x and y channels-last -- the loader
 // then copies each pixel's 8 channels as they are (no transpose) and the
 // epilogue writes each pixel's channels contiguously.
-template <int D, int OUT, int NHWC>
+template <int D, int OUT, int NHWC, int DL>
 __global__ __launch_bounds__(kThreads, 2)
 void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
                       const float *__restrict__ bias, float *__restrict__ y,
                       int C, int H, int Co, int rb_per_img, int remap, int relu) {
-    using G = Geo<D>;
+    using G = Geo<D, DL>;
     constexpr int W = G::W, J = G::J, RP = G::RP;
     __shared__ __align__(16) uint8_t smem[G::LDS];
     static_assert(G::LDS >= kEpiBytes, "the epilogue image overlays the stage buffers");
@@ -144,8 +151,11 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     if (remap) t = (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
     const int half = t & 1;
     t >>= 1;
+    // image n; within it, band tr / DL of 8 * DL rows and its row phase tr % DL:
+    // output rows r0 + DL * i for i = 0 .. 7
     const int n = t / rb_per_img;
-    const int r0 = (t - n * rb_per_img) * kRows;
+    const int tr = t - n * rb_per_img, band = tr / DL;
+    const int r0 = band * kRows * DL + (tr - band * DL);
     const int ocb = (int)blockIdx.y * kPackOcBlock + half * kOc;
     const int HW = H * W;
     const int S = C / kIc;
@@ -160,14 +170,14 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     const bool in_active = tid < G::UNITS;
     const int rho = tid % kInRows, rest = tid / kInRows;
     const int pg = rest % (W / 8), g8 = in_active ? rest / (W / 8) : 0;
-    const int ih = r0 - 1 + rho;
+    const int ih = r0 - DL + DL * rho;        // LDS row rho holds input row r0 - DL + DL * rho
     const bool ivalid = in_active && ih >= 0 && ih < H;
     // NCHW: channel g8*8 + e's 8 pixels are 16 contiguous bytes (e = channel);
     // NHWC: pixel pg*8 + e's channels g8*8 .. +7 are (e = pixel)
     const uint32_t ivoff = !ivalid ? kOob
                            : NHWC ? (uint32_t)(((ih * W + pg * 8) * C + g8 * 8) * 2)
                                   : (uint32_t)((g8 * 8 * HW + ih * W + pg * 8) * 2);
-    const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + 1) * kPix + in_half(g8, rho) * 16);
+    const uint32_t idst = (uint32_t)((rho * RP + pg * 8 + DL) * kPix + in_half(g8, rho) * 16);
     const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = NHWC ? (uint32_t)kIc * 2 : chan_bytes * kIc;
     const uint32_t e_bytes = NHWC ? (uint32_t)C * 2 : chan_bytes;
     uint4 xin[8];
@@ -272,7 +282,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
                 if (s + 2 < S) load_x(s + 2);
             }
         };
-        cg_col<D, 0>(acc, A, B0, T1, T2, ib, tb, ub, mid);
+        cg_col<D, DL, 0>(acc, A, B0, T1, T2, ib, tb, ub, mid);
         __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
@@ -318,14 +328,15 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
                     constexpr int kq = kEpiOc / kPer;
                     const int px = cid / kq, qd = cid - px * kq;
                     const int row = px / W, col = px - row * W;
-                    vo = r0 + row < H ? (uint32_t)((((r0 + row) * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB)
-                                      : kOob;
+                    const int orow = r0 + DL * row;
+                    vo = orow < H ? (uint32_t)(((orow * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB) : kOob;
 #pragma unroll
                     for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * kChPitch + row * W + col];
                 } else {
                     const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
-                    const int row = (kPer * e) / W;
-                    vo = r0 + row < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + r0 * W + kPer * e) * kOutB) : kOob;
+                    const int row = (kPer * e) / W, orow = r0 + DL * row;
+                    vo = orow < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + orow * W + kPer * e - row * W) * kOutB)
+                                  : kOob;
                     const float *src = epi + ocl * kChPitch + kPer * e;
                     const float4 lo = *reinterpret_cast<const float4 *>(src);
                     f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
@@ -361,25 +372,32 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
 bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
     (void)w;
     const int64_t HW = (int64_t)sh.H * sh.W;
-    return sh.plain() && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.C % kIc == 0 &&
+    const int dl = sh.dil;
+    return sh.G == 1 && (dl == 1 || dl == 2) && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == dl &&
+           sh.C % kIc == 0 &&
            sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
            (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range
            (!sh.nhwc || HW * sh.Co * 4 < (INT64_C(1) << 31)) &&           // channels-last: one output image
            (int64_t)kPackOcBlock * sh.C * 9 * 2 < (INT64_C(1) << 31) &&
-           (int64_t)sh.N * ((sh.H + kRows - 1) / kRows) * 2 < (INT64_C(1) << 31) &&
+           (int64_t)sh.N * dl * ((sh.H + kRows * dl - 1) / (kRows * dl)) * 2 < (INT64_C(1) << 31) &&
            ((uintptr_t)x % 16) == 0;
 }
 
 hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack, const float *bias,
                                  float *y, hipStream_t st) {
-    const int rb = (sh.H + kRows - 1) / kRows;
+    const int dl = sh.dil;                               // 1 or 2 (conv3x3cg_supported)
+    const int rb = dl * ((sh.H + kRows * dl - 1) / (kRows * dl));   // tiles per image: bands x row phases
     const int64_t blocks = (int64_t)sh.N * rb * 2;       // tiles x two 64-channel halves
     const int remap = (blocks % 8 == 0) ? 1 : 0;
     dim3 grid((unsigned)blocks, (unsigned)(sh.Co / kPackOcBlock));
-#define CONV3X3CG_GO(DV, O, L)                                                                                  \
-    hipLaunchKernelGGL((conv3x3cg_kernel<DV, O, L>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, sh.H, \
-                       sh.Co, rb, remap, sh.relu)
+#define CONV3X3CG_GO(DV, O, L)                                                                                 \
+    if (dl == 1)                                                                                                \
+        hipLaunchKernelGGL((conv3x3cg_kernel<DV, O, L, 1>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C,  \
+                           sh.H, sh.Co, rb, remap, sh.relu);                                                    \
+    else                                                                                                        \
+        hipLaunchKernelGGL((conv3x3cg_kernel<DV, O, L, 2>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C,  \
+                           sh.H, sh.Co, rb, remap, sh.relu)
 #define CONV3X3CG_LAUNCH(DV)                                              \
     if (sh.nhwc) {                                                        \
         if (sh.out_bf16) CONV3X3CG_GO(DV, 1, 1); else CONV3X3CG_GO(DV, 0, 1); \

@@ -255,3 +255,10 @@ def test_options_validation():
     assert B.conv_fwd_ex_workspace_bytes(big, None, 0) == 128 * 128 * 9 * 2
     assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(1, 0, 0), 0) == 128 * 128 * 9 * 2   # channels-last too
     assert B.conv_fwd_ex_workspace_bytes(big, B.ConvOptions(0, 0, 5), 0) == 0
+    # dilation 2 with pad 2 takes the column-group kernel (packed weights) too; other pads or
+    # dilations, and groups, do not
+    dil = lambda p, d, g=1: B.make_params((2, 32, 19, 40), (128, 32 // g, 3, 3), 1, p, d, g)
+    assert B.conv_fwd_ex_workspace_bytes(dil(2, 2), None, 0) == 128 * 32 * 9 * 2
+    assert B.conv_fwd_ex_workspace_bytes(dil(1, 2), None, 0) == 0
+    assert B.conv_fwd_ex_workspace_bytes(dil(3, 3), None, 0) == 0
+    assert B.conv_fwd_ex_workspace_bytes(dil(2, 2, 2), None, 0) == 0

@@ -124,6 +124,32 @@ def test_general_f32_direct():
         compare(_go(wl, t, "valu"), y_ref, S, TAU["f32"], label=str(shape))
 
 
+# ---- dilation 2 on the column-group kernel (workspace entry point) ---------------
+
+DILATED_CG = [
+    # (N, C, H, W, C_out): K 3, stride 1, pad 2, dilation 2
+    (2, 32, 19, 40, 128),      # two bands of 16 rows, the last one ragged; both row phases
+    (1, 16, 5, 32, 128),       # one 16-channel stage, fewer rows than a tile, W = 32
+    (1, 48, 33, 64, 256),      # W = 64 (the widest tile), two 128-channel blocks
+    (2, 64, 12, 48, 128),
+]
+
+
+@pytest.mark.parametrize("shape", DILATED_CG, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("integer", [False, True])
+def test_dilated_column_group(shape, integer):
+    N, C, H, W, Co = shape
+    wl = _wl("dilcg", 2, N, C, (H, W), Co, 3, 1, 2, 2, 1)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    y_ref, S = reference_general(wl, t)
+    ws = B.workspace_ex(wl.x_shape, wl.w_shape, 1, 2, 2, 1, "nchw", "f32", False, "auto")
+    assert ws is not None and ws.numel() == Co * C * 9 * 2     # packed weights: the column-group route
+    y = B.conv_ex(dev(t.x, None), dev(t.w, None), dev(t.b, np.float32), 1, 2, 2, 1, "nchw", "f32", False, "auto",
+                  ws, out=poisoned(wl.y_shape))
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), y_ref, S, 0 if integer else TAU["bf16"], exact=integer, label=str(shape))
+
+
 # ---- full-size layers ----------------------------------------------------------
 
 @pytest.mark.parametrize("name", GENERAL_FULL)
