@@ -279,7 +279,7 @@ bool wgrad_dw_ok(const Shape &sh) {
            sh.out_plane() * 2 < (INT64_C(1) << 31);
 }
 
-// Weight gradient of a 3x3, stride-1, pad-1 layer (NCHW, W % 8 == 0, C_in and
+// Weight gradient of a 3x3, stride-1, pad-1 (or dilation-2, pad-2) layer (NCHW, W % 8 == 0, C_in and
 // C_out multiples of 64): the nine taps share one operand.  For tap (kh, kw),
 // dW[:, :, kh, kw] = dout_mat (C_out x positions) @ x_shift(kh, kw)^T, and
 // dout_mat does not depend on the tap, so each step of 16 positions loads
@@ -287,9 +287,13 @@ bool wgrad_dw_ok(const Shape &sh) {
 // a lane's 8 positions lie in one row at an 8-aligned column ow0, so
 // x[ih][ow0 + kw - 1 .. +7] is the aligned 16-byte chunk at ow0 shifted by
 // kw - 1 elements, completed by the neighbouring chunks' edge elements
-// (v_alignbyte).  A workgroup: 64 output x 64 input channels x all 9 taps
-// over one range of positions; wave (wm, wn) holds a 32 x 32 block per tap
-// (9 accumulator tiles).  Partials are written as [split][tap][oc][ic].
+// (v_alignbyte).  With dilation 2 (pad 2) the kernel rows are two input rows
+// apart and a horizontal tap moves two elements, a whole dword: the shifted
+// operands are dword selections of the same three loads.  A workgroup: 64
+// output x 64 input channels x all 9 taps over one range of positions; wave
+// (wm, wn) holds a 32 x 32 block per tap (9 accumulator tiles).  Partials
+// are written as [split][tap][oc][ic].
+template <int DL>
 __global__ __launch_bounds__(256, 1)
 void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout, float *__restrict__ part,
                      int C, int Co, int H, int W, int P, int chunk) {
@@ -328,7 +332,7 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
         const int xb = (n * C + ic) * plane;
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh) {
-            const int ih = oh + kh - 1;
+            const int ih = oh + DL * (kh - 1);
             const bool rok = ok && 0 <= ih && ih < H;
             const uint32_t ro = (uint32_t)((xb + ih * W + ow0) * 2);
             o.cur[kh] = bload16(xr, rok ? ro : kOob, 0);
@@ -340,13 +344,20 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh) {
             const uint32_t c0 = o.cur[kh].x, c1 = o.cur[kh].y, c2 = o.cur[kh].z, c3 = o.cur[kh].w;
-            // kw = 0: columns ow0-1 .. ow0+6; kw = 1: the chunk; kw = 2: ow0+1 .. ow0+8
-            const uint4 b0 = make_uint4(__builtin_amdgcn_alignbyte(c0, o.prv[kh], 2),
-                                        __builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
-                                        __builtin_amdgcn_alignbyte(c3, c2, 2));
-            const uint4 b2 = make_uint4(__builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
-                                        __builtin_amdgcn_alignbyte(c3, c2, 2),
-                                        __builtin_amdgcn_alignbyte(o.nxt[kh], c3, 2));
+            // kw = 0: columns ow0-DL .. ow0+7-DL; kw = 1: the chunk; kw = 2: ow0+DL .. ow0+7+DL
+            uint4 b0, b2;
+            if constexpr (DL == 1) {
+                b0 = make_uint4(__builtin_amdgcn_alignbyte(c0, o.prv[kh], 2), __builtin_amdgcn_alignbyte(c1, c0, 2),
+                                __builtin_amdgcn_alignbyte(c2, c1, 2), __builtin_amdgcn_alignbyte(c3, c2, 2));
+                b2 = make_uint4(__builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
+                                __builtin_amdgcn_alignbyte(c3, c2, 2), __builtin_amdgcn_alignbyte(o.nxt[kh], c3, 2));
+            } else {
+                // whole-dword shifts; each component is a fresh VALU result so the
+                // operand quads are built in registers
+                auto cp = [](uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020100u); };
+                b0 = make_uint4(cp(o.prv[kh]), cp(c0), cp(c1), cp(c2));
+                b2 = make_uint4(cp(c1), cp(c2), cp(c3), cp(o.nxt[kh]));
+            }
             acc[3 * kh + 0] = mfma32x32x16(o.a, b0, acc[3 * kh + 0]);
             acc[3 * kh + 1] = mfma32x32x16(o.a, o.cur[kh], acc[3 * kh + 1]);
             acc[3 * kh + 2] = mfma32x32x16(o.a, b2, acc[3 * kh + 2]);
@@ -389,7 +400,8 @@ void sum_splits_tap_kernel(const float *__restrict__ part, float *__restrict__ d
 }
 
 bool wgrad3x3_ok(const Shape &sh) {
-    return sh.ndim == 2 && sh.plain() && sh.K == 3 && sh.s == 1 && sh.p == 1 && sh.W % 8 == 0 && sh.C % 64 == 0 &&
+    return sh.ndim == 2 && sh.G == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil && sh.K == 3 && sh.s == 1 &&
+           sh.W % 8 == 0 && sh.C % 64 == 0 &&
            sh.Co % 64 == 0 && sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
 }
 
@@ -497,7 +509,12 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
         const int chunk = (int)(((P + splits - 1) / splits + 15) / 16 * 16);
         const int used = (int)((P + chunk - 1) / chunk);
         dim3 grid((unsigned)(sh.C / 64), (unsigned)(sh.Co / 64), (unsigned)used);
-        hipLaunchKernelGGL(wgrad3x3_kernel, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi, chunk);
+        if (sh.dil == 2)
+            hipLaunchKernelGGL(wgrad3x3_kernel<2>, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi,
+                               chunk);
+        else
+            hipLaunchKernelGGL(wgrad3x3_kernel<1>, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi,
+                               chunk);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = (int64_t)9 * sh.Co * sh.C;

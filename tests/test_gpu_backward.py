@@ -87,11 +87,12 @@ def test_backward_integer_exact(case):
     compare(db, rdb, None, 0, exact=True, label="db %s" % (case,))
 
 
+@pytest.mark.parametrize("name", ["conv3x3_bf16", "dilated3x3_bf16"])
 @pytest.mark.parametrize("integer", [False, True])
-def test_backward_full_3x3_layer_sampled(integer):
-    """x (64,128,56,56), w (128,128,3,3), s1 p1: every db entry, 256 dw entries
-    (each a sum over 200704 positions) and 4000 dx entries."""
-    wl = synth.WORKLOADS["conv3x3_bf16"]
+def test_backward_full_3x3_layer_sampled(name, integer):
+    """x (64,128,56,56), w (128,128,3,3), s1 p1 (and dilation 2, p2): every db
+    entry, 256 dw entries (each a sum over 200704 positions) and 4000 dx entries."""
+    wl = synth.ALL_WORKLOADS[name]
     t = synth.make_inputs(wl, integer=integer)
     rng = np.random.default_rng(99)
     if integer:
@@ -101,7 +102,8 @@ def test_backward_full_3x3_layer_sampled(integer):
     dx, dw, db = _gpu(wl, t.x, t.w, dout)
     iw = rng.choice(dw.size, size=256, replace=False)
     ix = rng.choice(dx.size, size=4000, replace=False)
-    (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(t.x, t.w, dout, 1, 1, 1, 1, iw, ix)
+    (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(t.x, t.w, dout, wl.stride, wl.pad, wl.dilation,
+                                                           wl.groups, iw, ix)
     tau = 0 if integer else TAU
     compare(dw.reshape(-1)[iw], pdw, pSdw, tau, exact=integer, label="dw")
     compare(dx.reshape(-1)[ix], pdx, pSdx, tau, exact=integer, label="dx")
