@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass instead (data + weight + bias gradients of the layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass (50 steps, caches evicted "
+                                                            "before each)")
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--report", action="store_true", help="also time every workload/route (stderr)")
@@ -278,6 +280,31 @@ def time_steps(runner, steps, warmup):
     return wall, gpu, per
 
 
+def time_cold(runner, steps, flush_bytes=512 << 20):
+    """Cold caches: before each step a reduction reads `flush_bytes` of a scratch
+    buffer (outside the events), which evicts the L2s and the 256 MB memory-side
+    cache and leaves them holding clean lines (a write would leave dirty lines
+    for the step to write back); events around the step and its measured
+    launch."""
+    import torch
+    stream = torch.cuda.current_stream()
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps):
+        scratch.max()
+        a, b, c = ev[i]
+        a.record(stream)
+        runner.pre()
+        b.record(stream)
+        runner.main()
+        c.record(stream)
+    torch.cuda.synchronize()
+    step = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e-3
+    main = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    del scratch
+    return step, main
+
+
 # HBM traffic of the main kernel from rocprofv3 counters (profiles/counters_*.json):
 # FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what they read for a plain
 # copy of known size.  Used only while the kernel sources still hash to the
@@ -473,6 +500,18 @@ def main():
                                "second pass of the same steps (the weight repack before it is in the step, "
                                "not in this figure)"},
     }
+    if not args.no_cold:
+        n_cold = min(args.steps, 50)
+        c_step, c_main = time_cold(runner, n_cold)
+        out["cold_cache"] = {
+            "steps": n_cold, "flush_bytes_between_steps": 512 << 20,
+            "step_median_us": round(float(np.median(c_step)) * 1e6, 3),
+            "step_min_us": round(float(np.min(c_step)) * 1e6, 3),
+            "kernel_median_us": round(float(np.median(c_main)) * 1e6, 3),
+            "kernel_min_us": round(float(np.min(c_main)) * 1e6, 3),
+            "value": round(flops / float(np.median(c_step)) / 1e12, 3),
+            "note": "the same steps, each after a 512 MiB scratch buffer is read outside the events "
+                    "(L2s and the memory-side cache evicted, clean); value from the median step"}
     if args.backward:
         out["roofline"]["timing"] = ("HIP events on the library's stream around each call of a second pass of "
                                      "the same steps; per call (us): %s; the longer call is the roofline's "

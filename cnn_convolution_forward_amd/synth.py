@@ -109,7 +109,13 @@ WORKLOADS_GENERAL = {
     "grouped3x3_bf16": Workload("grouped3x3_bf16", 2, 64, 128, (56, 56), 128, 3, 1, 1, "bf16", "normal", 8,
                                 groups=4, note="x (64,128,56,56), w (128,32,3,3), groups 4 -> (64,128,56,56)"),
 }
-ALL_WORKLOADS = {**WORKLOADS, **WORKLOADS_GENERAL}
+# The 3x3 layer at one GPU's share of an 8-way batch shard (N = 8): the same
+# per-image work, 112 tiles of the column-group kernel for 256 compute units.
+WORKLOADS_SHARD = {
+    "conv3x3_bf16_n8": Workload("conv3x3_bf16_n8", 2, 8, 128, (56, 56), 128, 3, 1, 1, "bf16", "normal", 9,
+                                note="x (8,128,56,56), w (128,128,3,3), s1 p1 -> (8,128,56,56)"),
+}
+ALL_WORKLOADS = {**WORKLOADS, **WORKLOADS_GENERAL, **WORKLOADS_SHARD}
 
 
 @dataclass

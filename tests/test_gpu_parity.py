@@ -17,7 +17,8 @@ from parity import TAU, compare, dev, poisoned, reference, run
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["tiny_f32", "stem_bf16", "conv3x3_bf16", "conv1x1_bf16", "conv3d_bf16"]
+FULL = ["tiny_f32", "stem_bf16", "conv3x3_bf16", "conv1x1_bf16", "conv3d_bf16",
+        "conv3x3_bf16_n8"]          # the 3x3 layer at one GPU's share of an 8-way batch shard
 
 
 def _routes(wl):
@@ -88,11 +89,11 @@ def test_small_f32(shape):
     compare(_go(wl3, t3, "valu"), y_ref, S, TAU["f32"], label="3d " + str(shape))
 
 
-# ---- the five workloads at full size ------------------------------------------
+# ---- the five workloads (and the sharded 3x3 layer) at full size ---------------
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_workload(name):
-    wl = synth.WORKLOADS[name]
+    wl = synth.ALL_WORKLOADS[name]
     t = synth.make_inputs(wl)
     y_ref, S = reference(wl, t)
     for route in _routes(wl):
@@ -112,7 +113,7 @@ def test_full_workload_integer_exact(name):
     """x, w in {-2..2}, b in {-3..3}: every partial sum is an exact integer, so
     every route must reproduce the oracle bit for bit (catches any missing or
     misplaced tap)."""
-    wl = synth.WORKLOADS[name]
+    wl = synth.ALL_WORKLOADS[name]
     t = synth.make_inputs(wl, integer=True)
     y_ref, S = reference(wl, t)
     for route in _routes(wl):
