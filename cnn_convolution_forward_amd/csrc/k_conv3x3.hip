@@ -590,8 +590,9 @@ Plan make_plan(const Shape &sh, int slots) {
 }  // namespace
 
 void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st) {
-    const int64_t units = (int64_t)sh.Co * (sh.C / kIcStage) * 18;
-    hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, wpack, sh.C,
+    // a grouped layer packs as a layer of C_in / groups input channels
+    const int64_t units = (int64_t)sh.Co * (sh.Cg() / kIcStage) * 18;
+    hipLaunchKernelGGL(pack_w3x3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, wpack, sh.Cg(),
                        sh.Co);
 }
 
@@ -607,7 +608,7 @@ bool conv3x3s1_supported(const Shape &sh, const void *x, const void *w) {
 }
 
 size_t conv3x3s1_workspace_bytes(const Shape &sh) {
-    return (size_t)sh.Co * sh.C * 9 * 2;
+    return (size_t)sh.Co * sh.Cg() * 9 * 2;          // packed weights (C_in / groups per output channel)
 }
 
 hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, uint16_t *wpack,

@@ -123,6 +123,100 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const u
     if constexpr (q + 1 < Q) cg_col<D, DL, q + 1>(acc, A, B0, T1, T2, ib, tb, ub, mid);
 }
 
+// Epilogue of a column-group tile (64 output channels x 8 output rows r0 +
+// DL*i x W of image n, channels ocb ..).
+template <int D, int OUT, int NHWC, int DL>
+__device__ __forceinline__ void cg_epilogue(uint8_t *smem, const f32x16_t (&acc)[(Geo<D, DL>::J)], float *y, int n,
+                                            int Co, int ocb, int H, int r0, int relu) {
+    using G = Geo<D, DL>;
+    constexpr int W = G::W, J = G::J;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int c0 = wn * J;
+    const int HW = H * W;
+    // ---- epilogue: 4 passes of 16 channels through LDS, then whole rows out.
+    // Pass p: channels 16p .. 16p+15 = wave row wm = p/2, lanes with
+    // l32 / 16 == p % 2.  The pass image is [channel 16][row 8][column W]
+    // fp32 with a channel pitch of 8W + 4 dwords; a writer lane puts slot r
+    // (row 4h + r%4, group r/4) of fragment j at column c0 + j + D*(r/4).
+    // Readback: 16-byte chunks, consecutive threads on consecutive chunks of
+    // one channel's 8 rows -- a contiguous 32*W-byte block of y -- so every
+    // store instruction writes 1 KB of consecutive output.
+    float *const epi = reinterpret_cast<float *>(smem);
+    constexpr int kOutB = OUT ? 2 : 4;                   // bytes per output element
+    constexpr int kPer = 16 / kOutB;                     // outputs per 16-byte store
+    // NCHW: this tile's 64 channel planes; NHWC: the image (pixel-major, C_out channels each)
+    const __amdgpu_buffer_rsrc_t yr =
+        NHWC ? make_rsrc((char *)y + (int64_t)n * HW * Co * kOutB, (uint32_t)HW * Co * kOutB)
+             : make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB, (uint32_t)kOc * HW * kOutB);
+    constexpr int kChPitch = kRows * W + 4;
+    constexpr int kChunks = kEpiOc * kRows * W / kPer;   // 16-byte chunks per pass
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (wm == (p >> 1) && (l32 >> 4) == (p & 1)) {
+            float *dst = epi + (l32 & 15) * kChPitch + c0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 4 * h + (r & 3), grp = r >> 2;
+#pragma unroll
+                for (int j = 0; j < J; ++j) dst[row * W + grp * D + j] = acc[j][r];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
+            const int cid = k * kThreads + tid;
+            if (kChunks % kThreads == 0 || cid < kChunks) {
+                float f[8];
+                uint32_t vo;
+                if (NHWC) {
+                    // chunk = (pixel, group of kPer channels of this pass)
+                    constexpr int kq = kEpiOc / kPer;
+                    const int px = cid / kq, qd = cid - px * kq;
+                    const int row = px / W, col = px - row * W;
+                    const int orow = r0 + DL * row;
+                    vo = orow < H ? (uint32_t)(((orow * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB) : kOob;
+#pragma unroll
+                    for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * kChPitch + row * W + col];
+                } else {
+                    const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
+                    const int row = (kPer * e) / W, orow = r0 + DL * row;
+                    vo = orow < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + orow * W + kPer * e - row * W) * kOutB)
+                                  : kOob;
+                    const float *src = epi + ocl * kChPitch + kPer * e;
+                    const float4 lo = *reinterpret_cast<const float4 *>(src);
+                    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+                    if (kPer == 8) {
+                        const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+                        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+                    }
+                }
+                u32x4_t va;
+                if (OUT == 0) {
+                    float4 a4 = make_float4(f[0], f[1], f[2], f[3]);
+                    if (relu) {
+                        a4.x = fmaxf(a4.x, 0.f); a4.y = fmaxf(a4.y, 0.f);
+                        a4.z = fmaxf(a4.z, 0.f); a4.w = fmaxf(a4.w, 0.f);
+                    }
+                    va = (u32x4_t){__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
+                                   __float_as_uint(a4.w)};
+                } else {
+                    uint32_t b[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(relu ? fmaxf(f[u], 0.f) : f[u]);
+                    va = (u32x4_t){b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
+            }
+        }
+        if (p < 3) __syncthreads();
+    }
+}
+
 // OUT: 0 = fp32 output, 1 = bf16 output (rounded to nearest even); relu:
 // max(y, 0) before the store.  NHWC: x and y channels-last -- the loader
 // then copies each pixel's 8 channels as they are (no transpose) and the
@@ -286,85 +380,151 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
         __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
-    // ---- epilogue: 4 passes of 16 channels through LDS, then whole rows out.
-    // Pass p: channels 16p .. 16p+15 = wave row wm = p/2, lanes with
-    // l32 / 16 == p % 2.  The pass image is [channel 16][row 8][column W]
-    // fp32 with a channel pitch of 8W + 4 dwords; a writer lane puts slot r
-    // (row 4h + r%4, group r/4) of fragment j at column c0 + j + D*(r/4).
-    // Readback: 16-byte chunks, consecutive threads on consecutive chunks of
-    // one channel's 8 rows -- a contiguous 32*W-byte block of y -- so every
-    // store instruction writes 1 KB of consecutive output.
-    float *const epi = reinterpret_cast<float *>(smem);
-    constexpr int kOutB = OUT ? 2 : 4;                   // bytes per output element
-    constexpr int kPer = 16 / kOutB;                     // outputs per 16-byte store
-    // NCHW: this tile's 64 channel planes; NHWC: the image (pixel-major, C_out channels each)
-    const __amdgpu_buffer_rsrc_t yr =
-        NHWC ? make_rsrc((char *)y + (int64_t)n * HW * Co * kOutB, (uint32_t)HW * Co * kOutB)
-             : make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB, (uint32_t)kOc * HW * kOutB);
-    constexpr int kChPitch = kRows * W + 4;
-    constexpr int kChunks = kEpiOc * kRows * W / kPer;   // 16-byte chunks per pass
+    cg_epilogue<D, OUT, NHWC, DL>(smem, acc, y, n, Co, ocb, H, r0, relu);
+}
+
+// Grouped layers with 32 output channels per group (C_in/G a multiple of
+// 16): a workgroup's 64 output channels are two whole groups, and wave row
+// wm works on group gA + wm with an input plane of its own (the same pixel
+// layout as above, one plane per group).  Weights are packed as for a layer
+// of C_in/G input channels, so stage s of an output channel holds its own
+// group's channels 16s .. 16s+15.  Both planes and the weights of a stage are
+// single-buffered (56 KB at W = 56): load, barrier, MFMAs, barrier.  Groups
+// of 32 channels make short K loops (C_in/G / 16 stages), so the other
+// workgroup on the CU, not a pipeline inside this one, covers the loads.
+template <int D, int OUT>
+__global__ __launch_bounds__(kThreads, 2)
+void conv3x3cg_gp_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
+                         const float *__restrict__ bias, float *__restrict__ y,
+                         int C, int H, int Co, int Cg, int rb_per_img, int remap, int relu) {
+    using G = Geo<D, 1>;
+    constexpr int W = G::W, J = G::J, RP = G::RP;
+    constexpr int kLds = kWStage + 2 * G::IN_BYTES;
+    __shared__ __align__(16) uint8_t smem[kLds > kEpiBytes ? kLds : kEpiBytes];
+    static_assert(kLds <= 80 * 1024, "two workgroups per CU");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const int T = gridDim.x;
+    int t = blockIdx.x;
+    if (remap) t = (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
+    const int half = t & 1;
+    t >>= 1;
+    const int n = t / rb_per_img;
+    const int r0 = (t - n * rb_per_img) * kRows;
+    const int ocb = (int)blockIdx.y * kPackOcBlock + half * kOc;
+    const int gA = ocb / 32;                  // group of wave row 0; wave row 1 takes gA + 1
+    const int HW = H * W;
+    const int S = Cg / kIc;
+
+    uint8_t *const wbuf = smem;
+    uint8_t *const ibuf = smem + kWStage;
+    lds_u8 *const wlds = (lds_u8 *)smem;
+
+    // ---- input loader: unit u < 2 * UNITS -> plane u / UNITS, then (row,
+    // 8-pixel group, channel half) as in the dense kernel; thread tid takes
+    // units tid and tid + 256
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)n * C * HW, (uint32_t)C * HW * 2);
+    constexpr int kUnits = 2 * G::UNITS;
+    uint32_t ivoff[2], idst[2];
+    bool act[2];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (wm == (p >> 1) && (l32 >> 4) == (p & 1)) {
-            float *dst = epi + (l32 & 15) * kChPitch + c0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 4 * h + (r & 3), grp = r >> 2;
-#pragma unroll
-                for (int j = 0; j < J; ++j) dst[row * W + grp * D + j] = acc[j][r];
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
-            const int cid = k * kThreads + tid;
-            if (kChunks % kThreads == 0 || cid < kChunks) {
-                float f[8];
-                uint32_t vo;
-                if (NHWC) {
-                    // chunk = (pixel, group of kPer channels of this pass)
-                    constexpr int kq = kEpiOc / kPer;
-                    const int px = cid / kq, qd = cid - px * kq;
-                    const int row = px / W, col = px - row * W;
-                    const int orow = r0 + DL * row;
-                    vo = orow < H ? (uint32_t)(((orow * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB) : kOob;
-#pragma unroll
-                    for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * kChPitch + row * W + col];
-                } else {
-                    const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
-                    const int row = (kPer * e) / W, orow = r0 + DL * row;
-                    vo = orow < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + orow * W + kPer * e - row * W) * kOutB)
-                                  : kOob;
-                    const float *src = epi + ocl * kChPitch + kPer * e;
-                    const float4 lo = *reinterpret_cast<const float4 *>(src);
-                    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-                    if (kPer == 8) {
-                        const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-                        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-                    }
-                }
-                u32x4_t va;
-                if (OUT == 0) {
-                    float4 a4 = make_float4(f[0], f[1], f[2], f[3]);
-                    if (relu) {
-                        a4.x = fmaxf(a4.x, 0.f); a4.y = fmaxf(a4.y, 0.f);
-                        a4.z = fmaxf(a4.z, 0.f); a4.w = fmaxf(a4.w, 0.f);
-                    }
-                    va = (u32x4_t){__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
-                                   __float_as_uint(a4.w)};
-                } else {
-                    uint32_t b[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(relu ? fmaxf(f[u], 0.f) : f[u]);
-                    va = (u32x4_t){b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
-            }
-        }
-        if (p < 3) __syncthreads();
+    for (int k = 0; k < 2; ++k) {
+        const int u = tid + kThreads * k;
+        act[k] = u < kUnits;
+        const int pl = act[k] ? u / G::UNITS : 0, v = act[k] ? u - pl * G::UNITS : 0;
+        const int rho = v % kInRows, rest = v / kInRows;
+        const int pg = rest % (W / 8), g8 = rest / (W / 8);
+        const int ih = r0 - 1 + rho;
+        const bool ok = act[k] && ih >= 0 && ih < H;
+        ivoff[k] = ok ? (uint32_t)((((gA + pl) * Cg + g8 * 8) * HW + ih * W + pg * 8) * 2) : kOob;
+        idst[k] = (uint32_t)(pl * G::IN_BYTES + (rho * RP + pg * 8 + 1) * kPix + in_half(g8, rho) * 16);
     }
+    const uint32_t chan_bytes = (uint32_t)HW * 2, stage_bytes = chan_bytes * kIc;
+    uint4 xin[2][8];
+    auto load_x = [&](int s) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (k == 1 && kUnits <= kThreads) break;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xin[k][e] = bload16(xr, ivoff[k] + e * chan_bytes, (uint32_t)s * stage_bytes);
+        }
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (k == 1 && kUnits <= kThreads) break;
+            if (!act[k]) continue;
+            const uint32_t *v = reinterpret_cast<const uint32_t *>(xin[k]);   // v[e*4 + j/2]: channel e, pixels j, j+1
+            uint8_t *dst = ibuf + idst[k];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int dj = j >> 1, hj = j & 1;
+                uint4 o;
+                o.x = pack_halves(v[0 * 4 + dj], hj, v[1 * 4 + dj], hj);
+                o.y = pack_halves(v[2 * 4 + dj], hj, v[3 * 4 + dj], hj);
+                o.z = pack_halves(v[4 * 4 + dj], hj, v[5 * 4 + dj], hj);
+                o.w = pack_halves(v[6 * 4 + dj], hj, v[7 * 4 + dj], hj);
+                *reinterpret_cast<uint4 *>(dst + j * kPix) = o;
+            }
+        }
+    };
+    // ---- weights: packed as a layer of Cg input channels
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp + (int64_t)blockIdx.y * kPackOcBlock * Cg * 9,
+                                                (uint32_t)kPackOcBlock * Cg * 9 * 2);
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    auto dma_w = [&](int s) {
+        for (int blk = wave; blk < 18; blk += 4) {
+            const int tap = blk >> 1, u = blk & 1;
+            dma_1k(wlds + tap * kTapBytes + u * 1024, wr, lane16,
+                   s * kPackStage + tap * (kPackOcBlock * 32) + half * kTapBytes + u * 1024);
+        }
+    };
+
+    // operands: A as in the dense kernel; B from this wave row's plane
+    const uint32_t a_off = (uint32_t)((wm * 32 + l32) * 32 + ((h ^ wswz(l32)) * 16));
+    const int c0 = wn * J;
+    const uint32_t pl_off = (uint32_t)(wm * G::IN_BYTES);
+    const uint32_t b_base = pl_off + (uint32_t)((((l32 & 7) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                                in_half(h, l32 & 7) * 16);
+    const uint32_t b1_base = pl_off + (uint32_t)(((((l32 & 7) + 1) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                                 in_half(h, (l32 & 7) + 1) * 16);
+    const uint32_t b2_base = pl_off + (uint32_t)(((((l32 & 7) + 2) * RP) + D * (l32 >> 3) + c0) * kPix +
+                                                 in_half(h, (l32 & 7) + 2) * 16);
+
+    // zero both planes: halo columns are never written again
+    for (int i = tid; i < 2 * G::IN_BYTES / 16; i += kThreads)
+        reinterpret_cast<uint4 *>(ibuf)[i] = make_uint4(0, 0, 0, 0);
+    const float bv = bias ? bias[ocb + wm * 32 + l32] : 0.f;
+    f32x16_t acc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = bv;
+    __syncthreads();
+
+    for (int s = 0; s < S; ++s) {
+        dma_w(s);
+        load_x(s);
+        CONV3X3_WAIT_VMCNT(0);
+        store_x();
+        __syncthreads();            // this stage's weights and planes visible
+        const uint8_t *wb = wbuf + a_off;
+        const uint8_t *ib = ibuf + b_base, *tb = ibuf + b1_base, *ub = ibuf + b2_base;
+        uint4 A[9], B0[2], T1[2], T2[2];
+#pragma unroll
+        for (int tp = 0; tp < 9; ++tp) A[tp] = *reinterpret_cast<const uint4 *>(wb + tp * kTapBytes);
+        B0[0] = *reinterpret_cast<const uint4 *>(ib);
+        T1[0] = *reinterpret_cast<const uint4 *>(tb);
+        T2[0] = *reinterpret_cast<const uint4 *>(ub);
+        cg_col<D, 1, 0>(acc, A, B0, T1, T2, ib, tb, ub, []() {});
+        __syncthreads();            // buffers free for the next stage
+    }
+
+    cg_epilogue<D, OUT, 0, 1>(smem, acc, y, n, Co, ocb, H, r0, relu);
 }
 
 }  // namespace
@@ -373,13 +533,14 @@ bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w) {
     (void)w;
     const int64_t HW = (int64_t)sh.H * sh.W;
     const int dl = sh.dil;
-    return sh.G == 1 && (dl == 1 || dl == 2) && sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.p == dl &&
-           sh.C % kIc == 0 &&
+    const bool grouped_pair = sh.G > 1 && sh.Cog() == 32 && sh.Cg() % kIc == 0 && dl == 1 && !sh.nhwc;
+    return (sh.G == 1 || grouped_pair) && (dl == 1 || dl == 2) && sh.ndim == 2 && sh.K == 3 && sh.s == 1 &&
+           sh.p == dl && sh.Cg() % kIc == 0 &&
            sh.Co % kPackOcBlock == 0 && sh.W % 8 == 0 && sh.W >= 32 && sh.W <= 64 &&
            (int64_t)sh.C * HW * 2 < (INT64_C(1) << 31) &&                 // one image within a buffer range
            (int64_t)kOc * HW * 4 < (INT64_C(1) << 31) &&                  // one output block within a buffer range
            (!sh.nhwc || HW * sh.Co * 4 < (INT64_C(1) << 31)) &&           // channels-last: one output image
-           (int64_t)kPackOcBlock * sh.C * 9 * 2 < (INT64_C(1) << 31) &&
+           (int64_t)kPackOcBlock * sh.Cg() * 9 * 2 < (INT64_C(1) << 31) &&
            (int64_t)sh.N * dl * ((sh.H + kRows * dl - 1) / (kRows * dl)) * 2 < (INT64_C(1) << 31) &&
            ((uintptr_t)x % 16) == 0;
 }
@@ -403,6 +564,25 @@ hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint1
         if (sh.out_bf16) CONV3X3CG_GO(DV, 1, 1); else CONV3X3CG_GO(DV, 0, 1); \
     } else {                                                              \
         if (sh.out_bf16) CONV3X3CG_GO(DV, 1, 0); else CONV3X3CG_GO(DV, 0, 0); \
+    }
+    if (sh.G > 1) {
+#define CONV3X3CG_GP(DV)                                                                                    \
+    if (sh.out_bf16)                                                                                        \
+        hipLaunchKernelGGL((conv3x3cg_gp_kernel<DV, 1>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, \
+                           sh.H, sh.Co, sh.Cg(), rb, remap, sh.relu);                                      \
+    else                                                                                                    \
+        hipLaunchKernelGGL((conv3x3cg_gp_kernel<DV, 0>), grid, dim3(kThreads), 0, st, x, wpack, bias, y, sh.C, \
+                           sh.H, sh.Co, sh.Cg(), rb, remap, sh.relu)
+        switch (sh.W / 4) {
+            case 8: CONV3X3CG_GP(8); break;
+            case 10: CONV3X3CG_GP(10); break;
+            case 12: CONV3X3CG_GP(12); break;
+            case 14: CONV3X3CG_GP(14); break;
+            case 16: CONV3X3CG_GP(16); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef CONV3X3CG_GP
+        return hipGetLastError();
     }
     switch (sh.W / 4) {
         case 8: CONV3X3CG_LAUNCH(8); break;

@@ -262,3 +262,9 @@ def test_options_validation():
     assert B.conv_fwd_ex_workspace_bytes(dil(1, 2), None, 0) == 0
     assert B.conv_fwd_ex_workspace_bytes(dil(3, 3), None, 0) == 0
     assert B.conv_fwd_ex_workspace_bytes(dil(2, 2, 2), None, 0) == 0
+    # groups of 32 output channels take the grouped column-group kernel (weights packed per group)
+    grp = lambda g, co=128, c=128: B.make_params((2, c, 19, 40), (co, c // g, 3, 3), 1, 1, 1, g)
+    assert B.conv_fwd_ex_workspace_bytes(grp(4), None, 0) == 128 * 32 * 9 * 2
+    assert B.conv_fwd_ex_workspace_bytes(grp(2), None, 0) == 0              # 64 per group: general kernel
+    assert B.conv_fwd_ex_workspace_bytes(grp(8, 256, 256), None, 0) == 256 * 32 * 9 * 2
+    assert B.conv_fwd_ex_workspace_bytes(grp(4), B.ConvOptions(1, 0, 0), 0) == 0   # channels-last: general

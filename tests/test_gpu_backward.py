@@ -64,6 +64,7 @@ SMALL = [
     (2, 7, 16, (5, 6), 400, 1, 1, 0, 1, 1),       # db over image ranges of 3, 3, 1 (rows of 30: 2-byte loads)
     (2, 7, 8, (4, 8), 300, 1, 1, 0, 1, 1),        # db over image ranges of 2, 2, 2, 1 (rows of 32: 16-byte loads)
     (2, 2, 128, (13, 32), 128, 3, 1, 2, 2, 1),    # dilation 2: dx on the column-group kernel (pad 2d - 2 = 2)
+    (2, 2, 128, (13, 32), 128, 3, 1, 1, 1, 4),    # groups of 32: dx on the grouped column-group kernel
 ]
 
 

@@ -150,6 +150,46 @@ def test_dilated_column_group(shape, integer):
     compare(y.cpu().numpy(), y_ref, S, 0 if integer else TAU["bf16"], exact=integer, label=str(shape))
 
 
+# ---- groups of 32 output channels on the column-group kernel (workspace entry point)
+
+GROUPED_CG = [
+    # (N, C, H, W, C_out, G): K 3, stride 1, pad 1; C_out / G = 32
+    (2, 128, 19, 40, 128, 4),    # two input stages per group, ragged last row tile
+    (1, 64, 9, 56, 128, 4),      # 16 input channels per group: one stage; two loader passes (W = 56)
+    (1, 256, 10, 32, 256, 8),    # two 128-channel blocks, W = 32
+    (2, 128, 8, 48, 128, 4),
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED_CG, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("integer", [False, True])
+def test_grouped_column_group(shape, integer):
+    N, C, H, W, Co, g = shape
+    wl = _wl("grpcg", 2, N, C, (H, W), Co, 3, 1, 1, 1, g)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    y_ref, S = reference_general(wl, t)
+    ws = B.workspace_ex(wl.x_shape, wl.w_shape, 1, 1, 1, g, "nchw", "f32", False, "auto")
+    assert ws is not None and ws.numel() == Co * (C // g) * 9 * 2     # packed weights: the column-group route
+    y = B.conv_ex(dev(t.x, None), dev(t.w, None), dev(t.b, np.float32), 1, 1, 1, g, "nchw", "f32", False, "auto",
+                  ws, out=poisoned(wl.y_shape))
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), y_ref, S, 0 if integer else TAU["bf16"], exact=integer, label=str(shape))
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_grouped_full_layer_column_group(integer):
+    """The G = 4 layer (64,128,56,56) through the workspace entry point, whole output."""
+    wl = synth.ALL_WORKLOADS["grouped3x3_bf16"]
+    t = synth.make_inputs(wl, integer=integer)
+    y_ref, S = reference_general(wl, t)
+    ws = B.workspace_ex(wl.x_shape, wl.w_shape, 1, 1, 1, wl.groups, "nchw", "f32", False, "auto")
+    assert ws is not None and ws.numel() == 128 * 32 * 9 * 2
+    y = B.conv_ex(dev(t.x, None), dev(t.w, None), dev(t.b, np.float32), 1, 1, 1, wl.groups, "nchw", "f32", False,
+                  "auto", ws, out=poisoned(wl.y_shape))
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), y_ref, S, 0 if integer else TAU["bf16"], exact=integer, label="grouped full")
+
+
 # ---- full-size layers ----------------------------------------------------------
 
 @pytest.mark.parametrize("name", GENERAL_FULL)

@@ -74,6 +74,7 @@ CASES = [
     ("3x3 column-group", (2, 2, 128, (56, 56), 128, 3, 1, 1, 1, 1), "auto", True),
     ("3x3 W=40 column-group", (2, 1, 32, (13, 40), 256, 3, 1, 1, 1, 1), "auto", True),
     ("3x3 dilation 2 column-group", (2, 2, 32, (19, 40), 128, 3, 1, 2, 2, 1), "auto", True),
+    ("3x3 groups of 32 column-group", (2, 2, 128, (11, 40), 128, 3, 1, 1, 1, 4), "auto", True),
     ("pointwise", (2, 3, 64, (14, 16), 192, 1, 1, 0, 1, 1), "auto", False),
     ("depthwise", (2, 2, 24, (30, 40), 48, 3, 2, 1, 1, 24), "auto", False),
     ("stem (direct VALU)", (2, 2, 3, (33, 35), 64, 3, 2, 1, 1, 1), "auto", False),
