@@ -244,7 +244,9 @@ CONV_API int64_t conv_out_dim_dilated(int64_t in, int64_t K, int64_t stride, int
  * depthwise VALU kernel, which reads each input once and writes each output
  * once; a per-group reduction (C_in/G * K^ndim) <= 32 -> the direct VALU
  * kernel; otherwise the MFMA implicit GEMM, one GEMM of C_out/G x
- * (C_in/G * K^ndim) per group. */
+ * (C_in/G * K^ndim) per group.  It takes no workspace: the 3x3 kernels that
+ * read packed weights (dilation 1 or 2 with pad = dilation, or groups of 32
+ * output channels) are reached through conv_fwd_ex_bf16 with a workspace. */
 CONV_API conv_status_t conv_fwd_bf16(const conv_params_t *params, const uint16_t *x, const uint16_t *w,
                                      const float *bias, float *y, int algo, void *stream);
 
@@ -289,8 +291,11 @@ typedef struct {
     int relu;        /* 0 or 1                                       */
 } conv_options_t;
 
-/* Workspace conv_fwd_ex_bf16 can use (the packed weights of the 3x3 kernels,
- * which take NCHW with any epilogue) or, with algo CONV_ALGO_WINOGRAD, needs
+/* Workspace conv_fwd_ex_bf16 can use (C_out x C_in/G x 9 bf16: the packed
+ * weights of the 3x3 column-group kernels, for 3x3 stride-1 layers with
+ * dilation 1 or 2 and pad = dilation, or with groups of 32 output channels
+ * (NCHW, dilation 1); any epilogue, and channels-last for groups 1) or, with
+ * algo CONV_ALGO_WINOGRAD, needs
  * (the fp16 transformed weights, 16 x C_out x C_in, and transformed input
  * blocks, 16 x N*ceil(H_out/2)*ceil(W_out/2) x C_in); 0 when none, or on
  * invalid arguments or a shape Winograd does not take. */
@@ -301,8 +306,10 @@ CONV_API size_t conv_fwd_ex_workspace_bytes(const conv_params_t *params, const c
  * with Winograd) device memory of at least conv_fwd_ex_workspace_bytes()
  * bytes (overwritten).  Kernels that
  * do not take an option step aside for the general ones: channels-last runs
- * on the general implicit GEMM and the direct VALU kernel; the 3x3, pointwise
- * and depthwise kernels apply ReLU and bf16 output in their own epilogue.
+ * on the 3x3 column-group kernel (groups 1), a channels-last pointwise
+ * kernel, and otherwise the general implicit GEMM and the direct VALU kernel;
+ * the 3x3, pointwise and depthwise kernels apply ReLU and bf16 output in
+ * their own epilogue.
  * algo CONV_ALGO_WINOGRAD computes U = G g G^T and V = B^T d B in fp16, the
  * 16 transform-point GEMMs on the matrix cores with fp32 accumulation, and
  * A^T M A per 2x2 block; its error scale is the transform-domain magnitude
