@@ -364,25 +364,36 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
         }
     };
 
-    Ops o0, o1;
+    // three operand sets: the loads of a step are issued two steps ahead of
+    // its MFMAs; three steps per iteration so that each set keeps fixed registers
+    Ops o0, o1, o2;
     int kk = k_begin;
     if (kk < k_end) load(kk, o0);
-    // two steps per iteration so that the operand sets keep fixed registers
-    for (; kk < k_end; kk += 32) {
-        if (kk + 16 < k_end) load(kk + 16, o1);
+    if (kk + 16 < k_end) load(kk + 16, o1);
+    for (; kk < k_end; kk += 48) {
+        if (kk + 32 < k_end) load(kk + 32, o2);
         compute(o0);
         if (kk + 16 >= k_end) break;
-        if (kk + 32 < k_end) load(kk + 32, o0);
+        if (kk + 48 < k_end) load(kk + 48, o0);
         compute(o1);
+        if (kk + 32 >= k_end) break;
+        if (kk + 64 < k_end) load(kk + 64, o1);
+        compute(o2);
     }
 
-    // part[split][tap][oc][ic]: 32 lanes on 32 consecutive input channels
-    float *pp = part + (int64_t)split * 9 * Co * C;
+    // part[split][tap][oc][ic]: 32 lanes on 32 consecutive input channels.
+    // Through a buffer resource: the lane's part of the offset (its input
+    // channel, the rows of its half) in one VGPR, the (tap, slot) part
+    // uniform, so the 144 stores need no address registers of their own
+    // (64-bit addresses computed ahead of the loop held ~100 VGPRs through it).
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(part + (int64_t)split * 9 * Co * C, (uint32_t)(9 * Co * C * 4));
+    const int voff = ((oc0 + 4 * (lane >> 5)) * C + ic) * 4;
 #pragma unroll
     for (int t = 0; t < 9; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            pp[((int64_t)t * Co + oc0 + mfma32_row(r, lane)) * C + ic] = acc[t][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[t][r]), pr, voff,
+                                                  ((t * Co + 8 * (r >> 2) + (r & 3)) * C) * 4, 0);
 }
 
 // dw[oc][ic][tap] = sum over splits, in order, of part[split][tap][oc][ic].
@@ -401,7 +412,7 @@ void sum_splits_tap_kernel(const float *__restrict__ part, float *__restrict__ d
 
 bool wgrad3x3_ok(const Shape &sh) {
     return sh.ndim == 2 && sh.G == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil && sh.K == 3 && sh.s == 1 &&
-           sh.W % 8 == 0 && sh.C % 64 == 0 &&
+           sh.W % 8 == 0 && sh.C % 64 == 0 && (int64_t)9 * sh.Co * sh.C * 4 < (INT64_C(1) << 31) &&
            sh.Co % 64 == 0 && sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
 }
 
