@@ -365,19 +365,20 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
     };
 
     // three operand sets: the loads of a step are issued two steps ahead of
-    // its MFMAs; three steps per iteration so that each set keeps fixed registers
+    // its MFMAs; three steps per iteration so that each set keeps fixed
+    // registers.  Loads and MFMAs are unconditional: a step past the range
+    // loads zeros (out-of-range offsets) and adds zero, and with no branch
+    // around the loads the compiler's waits leave the two later steps in flight.
     Ops o0, o1, o2;
     int kk = k_begin;
-    if (kk < k_end) load(kk, o0);
-    if (kk + 16 < k_end) load(kk + 16, o1);
+    load(kk, o0);
+    load(kk + 16, o1);
     for (; kk < k_end; kk += 48) {
-        if (kk + 32 < k_end) load(kk + 32, o2);
+        load(kk + 32, o2);
         compute(o0);
-        if (kk + 16 >= k_end) break;
-        if (kk + 48 < k_end) load(kk + 48, o0);
+        load(kk + 48, o0);
         compute(o1);
-        if (kk + 32 >= k_end) break;
-        if (kk + 64 < k_end) load(kk + 64, o1);
+        load(kk + 64, o1);
         compute(o2);
     }
 
