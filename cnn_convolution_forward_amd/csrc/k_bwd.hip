@@ -27,6 +27,7 @@
 // the nine taps.
 #include "conv_internal.h"
 #include "mfma_common.h"
+#include "conv3x3_common.h"
 
 namespace convfwd {
 namespace {
@@ -279,36 +280,99 @@ bool wgrad_dw_ok(const Shape &sh) {
            sh.out_plane() * 2 < (INT64_C(1) << 31);
 }
 
-// Weight gradient of a 3x3, stride-1, pad-1 (or dilation-2, pad-2) layer (NCHW, W % 8 == 0, C_in and
-// C_out multiples of 64): the nine taps share one operand.  For tap (kh, kw),
-// dW[:, :, kh, kw] = dout_mat (C_out x positions) @ x_shift(kh, kw)^T, and
-// dout_mat does not depend on the tap, so each step of 16 positions loads
-// the dout operand once and builds the nine x operands from three input rows:
-// a lane's 8 positions lie in one row at an 8-aligned column ow0, so
-// x[ih][ow0 + kw - 1 .. +7] is the aligned 16-byte chunk at ow0 shifted by
-// kw - 1 elements, completed by the neighbouring chunks' edge elements
-// (v_alignbyte).  With dilation 2 (pad 2) the kernel rows are two input rows
-// apart and a horizontal tap moves two elements, a whole dword: the shifted
-// operands are dword selections of the same three loads.  A workgroup: 64
-// output x 64 input channels x all 9 taps over one range of positions; wave
-// (wm, wn) holds a 32 x 32 block per tap (9 accumulator tiles).  Partials
-// are written as [split][tap][oc][ic].
-template <int DL>
+// Weight gradient of a 3x3, stride-1 layer with pad = dilation (1 or 2):
+// NCHW, W % 8 == 0, W <= 64, C_in and C_out multiples of 64.  The nine taps
+// share one operand: for tap (kh, kw), dW[:, :, kh, kw] = dout_mat (C_out x
+// positions) @ x_shift(kh, kw)^T.  A workgroup (64 output x 64 input
+// channels; four waves (wm, wn) of 32 x 32 per tap, 9 accumulator tiles)
+// runs over a range of output rows, one row (n, oh) a stage.  The stage's
+// operands are copied into LDS by coalesced direct-to-LDS loads of 16-byte
+// units of contiguous rows (read straight from global memory, with 32
+// channel planes per load instruction, they kept the vector-memory pipeline
+// busy with cache-line lookups at ~11% of the MFMA peak):
+//   dout [oc 64][DU units]: the row's W/8 units, then zeros up to 16 x
+//        ceil(W/16) positions (DU odd, so 8 rows hit 8 bank groups);
+//   x    [ic 64][kh 3][XU units]: a zero unit, input row oh + d(kh - 1)'s
+//        W/8 units, a zero unit (XU odd).
+// Rows outside the image and the zero units come from out-of-range offsets
+// (the copy writes zeros).  Per 16-position step a lane reads its dout unit
+// and, per kernel row, the x unit under its 8 positions and the neighbouring
+// dwords; the horizontal shifts are v_alignbyte (dilation 1) or whole-dword
+// selections (dilation 2).  Three LDS buffers, copies two stages ahead, one
+// barrier a stage.  Partials are written as [split][tap][oc][ic].
+template <int W, int DL>
+struct WgGeo {
+    static constexpr int KS = (W + 15) / 16;          // 16-position steps per row
+    static constexpr int DU = (2 * KS) | 1;           // dout units per channel row
+    static constexpr int XU = (W / 8 + 2) | 1;        // x units per (channel, kernel row)
+    static constexpr int D_BYTES = 64 * DU * 16;
+    static constexpr int STAGE = D_BYTES + 64 * 3 * XU * 16;
+    static constexpr int INSTS = DU + 3 * XU;         // 1 KB copy instructions per stage
+    static constexpr int PER_WAVE = (INSTS + 3) / 4;  // instructions of waves 0 .. INSTS % 4 - 1
+};
+
+template <int W, int DL>
 __global__ __launch_bounds__(256, 1)
 void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout, float *__restrict__ part,
-                     int C, int Co, int H, int W, int P, int chunk) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                     int N, int C, int Co, int H, int rows_per) {
+    using G = WgGeo<W, DL>;
+    static_assert(3 * G::STAGE <= 160 * 1024, "three stages in LDS");
+    __shared__ __align__(16) uint8_t smem[3 * G::STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int ic0 = blockIdx.x * 64 + wn * 32, oc0 = blockIdx.y * 64 + wm * 32;
-    const int split = blockIdx.z;
-    const int k_begin = split * chunk;
-    const int k_end = k_begin + chunk < P ? k_begin + chunk : P;
-    const int r32 = lane & 31, half = lane >> 5;
-    const int plane = H * W;
-    const int oc = oc0 + r32, ic = ic0 + r32;
-    // buffer resources over one channel plane series: dout[n][oc], x[n][ic] for all n
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout, (uint32_t)((int64_t)(P / plane) * Co * plane * 2));
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)(P / plane) * C * plane * 2));
+    const int ic0 = blockIdx.x * 64, oc0 = blockIdx.y * 64, split = blockIdx.z;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int NH = N * H;
+    const int row_begin = split * rows_per;
+    const int row_end = row_begin + rows_per < NH ? row_begin + rows_per : NH;
+    const int plane_b = H * W * 2;                    // bytes per channel plane
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout, (uint32_t)((int64_t)N * Co * H * W * 2));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)N * C * H * W * 2));
+
+    // copy instructions of this wave: i = wave + 4 j; lane -> unit i * 64 + lane
+    int n_mine = 0;
+    uint32_t st_off[G::PER_WAVE];
+    int st_kh[G::PER_WAVE];                           // -1: dout unit; 0..2: x kernel row; 3: zero unit
+#pragma unroll
+    for (int j = 0; j < G::PER_WAVE; ++j) {
+        const int i = wave + 4 * j;
+        st_off[j] = 0;
+        st_kh[j] = 3;
+        if (i >= G::INSTS) continue;
+        ++n_mine;
+        const int u = i * 64 + lane;
+        if (i < G::DU) {
+            const int oc = u / G::DU, uu = u - oc * G::DU;
+            st_kh[j] = uu < W / 8 ? -1 : 3;
+            st_off[j] = (uint32_t)(oc * plane_b + uu * 16);
+        } else {
+            const int ux = u - 64 * G::DU;
+            const int ic = ux / (3 * G::XU), rem = ux - ic * (3 * G::XU);
+            const int kh = rem / G::XU, uc = rem - kh * G::XU;
+            st_kh[j] = (uc >= 1 && uc <= W / 8) ? kh : 3;
+            st_off[j] = (uint32_t)(ic * plane_b + (uc - 1) * 16);
+        }
+    }
+    auto issue = [&](int row, int buf) {
+        const int n = row / H, oh = row - n * H;
+        const uint32_t row_d = (uint32_t)(((n * Co + oc0) * H + oh) * W * 2);
+        const uint32_t row_x = (uint32_t)(((n * C + ic0) * H + oh) * W * 2);
+        lds_u8 *const base = (lds_u8 *)smem + buf * G::STAGE;
+#pragma unroll
+        for (int j = 0; j < G::PER_WAVE; ++j) {
+            const int i = wave + 4 * j;
+            if (i >= G::INSTS) break;
+            const int kh = st_kh[j];
+            if (i < G::DU) {
+                dma_1k(base + i * 1024, dr, kh == -1 ? row_d + st_off[j] : kOob, 0);
+            } else {
+                const int ih = oh + DL * (kh - 1);
+                const bool ok = kh < 3 && ih >= 0 && ih < H;
+                dma_1k(base + i * 1024, xr, ok ? row_x + (uint32_t)(DL * (kh - 1) * W * 2) + st_off[j] : kOob, 0);
+            }
+        }
+    };
 
     f32x16_t acc[9];
 #pragma unroll
@@ -316,79 +380,71 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
-    // operands of one step: a (dout, 16 B), per kernel row the aligned chunk
-    // and the neighbouring chunks' edge dwords; two sets, the next step's
-    // loads in flight while the current step's MFMAs run
-    struct Ops {
-        uint4 a, cur[3];
-        uint32_t prv[3], nxt[3];
-    };
-    auto load = [&](int kk, Ops &o) {
-        const int pp = kk + 8 * half;                 // this lane's first position (8-aligned)
-        const bool ok = pp < k_end;
-        const int n = pp / plane, q = pp - n * plane;
-        const int oh = q / W, ow0 = q - oh * W;
-        o.a = bload16(dr, ok ? (uint32_t)(((n * Co + oc) * plane + q) * 2) : kOob, 0);
-        const int xb = (n * C + ic) * plane;
+    // operand offsets in a stage: A row wm*32 + r32 of dout, B row wn*32 + r32 of x
+    const uint32_t a_off = (uint32_t)(((wm * 32 + r32) * G::DU + h) * 16);
+    const uint32_t b_off = (uint32_t)(G::D_BYTES + ((wn * 32 + r32) * 3 * G::XU + 1 + h) * 16);
+    auto compute = [&](int buf) {
+        const uint8_t *sb = smem + buf * G::STAGE;
 #pragma unroll
-        for (int kh = 0; kh < 3; ++kh) {
-            const int ih = oh + DL * (kh - 1);
-            const bool rok = ok && 0 <= ih && ih < H;
-            const uint32_t ro = (uint32_t)((xb + ih * W + ow0) * 2);
-            o.cur[kh] = bload16(xr, rok ? ro : kOob, 0);
-            o.prv[kh] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(rok && ow0 > 0 ? ro - 4 : kOob), 0, 0);
-            o.nxt[kh] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(rok && ow0 + 8 < W ? ro + 16 : kOob), 0, 0);
+        for (int ks = 0; ks < G::KS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(sb + a_off + ks * 32);
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+                const uint8_t *xb = sb + b_off + (kh * G::XU + 2 * ks) * 16;
+                const uint4 cur = *reinterpret_cast<const uint4 *>(xb);
+                const uint32_t prv = *reinterpret_cast<const uint32_t *>(xb - 4);
+                const uint32_t nxt = *reinterpret_cast<const uint32_t *>(xb + 16);
+                const uint32_t c0 = cur.x, c1 = cur.y, c2 = cur.z, c3 = cur.w;
+                // kw = 0: columns ow0-DL .. ow0+7-DL; kw = 1: the unit; kw = 2: ow0+DL .. ow0+7+DL
+                uint4 b0, b2;
+                if constexpr (DL == 1) {
+                    b0 = make_uint4(__builtin_amdgcn_alignbyte(c0, prv, 2), __builtin_amdgcn_alignbyte(c1, c0, 2),
+                                    __builtin_amdgcn_alignbyte(c2, c1, 2), __builtin_amdgcn_alignbyte(c3, c2, 2));
+                    b2 = make_uint4(__builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
+                                    __builtin_amdgcn_alignbyte(c3, c2, 2), __builtin_amdgcn_alignbyte(nxt, c3, 2));
+                } else {
+                    // whole-dword shifts; fresh VALU results so the operand quads are built in registers
+                    auto cp = [](uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020100u); };
+                    b0 = make_uint4(cp(prv), cp(c0), cp(c1), cp(c2));
+                    b2 = make_uint4(cp(c1), cp(c2), cp(c3), cp(nxt));
+                }
+                acc[3 * kh + 0] = mfma32x32x16(a, b0, acc[3 * kh + 0]);
+                acc[3 * kh + 1] = mfma32x32x16(a, cur, acc[3 * kh + 1]);
+                acc[3 * kh + 2] = mfma32x32x16(a, b2, acc[3 * kh + 2]);
+            }
         }
     };
-    auto compute = [&](const Ops &o) {
-#pragma unroll
-        for (int kh = 0; kh < 3; ++kh) {
-            const uint32_t c0 = o.cur[kh].x, c1 = o.cur[kh].y, c2 = o.cur[kh].z, c3 = o.cur[kh].w;
-            // kw = 0: columns ow0-DL .. ow0+7-DL; kw = 1: the chunk; kw = 2: ow0+DL .. ow0+7+DL
-            uint4 b0, b2;
-            if constexpr (DL == 1) {
-                b0 = make_uint4(__builtin_amdgcn_alignbyte(c0, o.prv[kh], 2), __builtin_amdgcn_alignbyte(c1, c0, 2),
-                                __builtin_amdgcn_alignbyte(c2, c1, 2), __builtin_amdgcn_alignbyte(c3, c2, 2));
-                b2 = make_uint4(__builtin_amdgcn_alignbyte(c1, c0, 2), __builtin_amdgcn_alignbyte(c2, c1, 2),
-                                __builtin_amdgcn_alignbyte(c3, c2, 2), __builtin_amdgcn_alignbyte(o.nxt[kh], c3, 2));
-            } else {
-                // whole-dword shifts; each component is a fresh VALU result so the
-                // operand quads are built in registers
-                auto cp = [](uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020100u); };
-                b0 = make_uint4(cp(o.prv[kh]), cp(c0), cp(c1), cp(c2));
-                b2 = make_uint4(cp(c1), cp(c2), cp(c3), cp(o.nxt[kh]));
-            }
-            acc[3 * kh + 0] = mfma32x32x16(o.a, b0, acc[3 * kh + 0]);
-            acc[3 * kh + 1] = mfma32x32x16(o.a, o.cur[kh], acc[3 * kh + 1]);
-            acc[3 * kh + 2] = mfma32x32x16(o.a, b2, acc[3 * kh + 2]);
+    // wait until this wave's copies of all but the last `later` issued stages are done
+    // (copies complete in order; the count is an immediate, so one branch per case)
+    auto wait_all_but = [&](bool later) {
+        if (!later) {
+            CONV3X3_WAIT_VMCNT(0);
+        } else if (n_mine == G::PER_WAVE) {
+            CONV3X3_WAIT_VMCNT(G::PER_WAVE);
+        } else {
+            CONV3X3_WAIT_VMCNT(G::PER_WAVE - 1);
         }
     };
 
-    // three operand sets: the loads of a step are issued two steps ahead of
-    // its MFMAs; three steps per iteration so that each set keeps fixed
-    // registers.  Loads and MFMAs are unconditional: a step past the range
-    // loads zeros (out-of-range offsets) and adds zero, and with no branch
-    // around the loads the compiler's waits leave the two later steps in flight.
-    Ops o0, o1, o2;
-    int kk = k_begin;
-    load(kk, o0);
-    load(kk + 16, o1);
-    for (; kk < k_end; kk += 48) {
-        load(kk + 32, o2);
-        compute(o0);
-        load(kk + 48, o0);
-        compute(o1);
-        load(kk + 64, o1);
-        compute(o2);
+    const int rows = row_end > row_begin ? row_end - row_begin : 0;
+    if (rows > 0) issue(row_begin, 0);
+    if (rows > 1) issue(row_begin + 1, 1);
+    wait_all_but(rows > 1);
+    __syncthreads();
+    for (int s = 0; s < rows; ++s) {
+        const bool ahead = s + 2 < rows;
+        if (ahead) issue(row_begin + s + 2, (s + 2) % 3);
+        compute(s % 3);
+        wait_all_but(ahead);                          // stage s + 1 copied
+        __syncthreads();                              // stage s's buffer free, stage s + 1's visible
     }
 
     // part[split][tap][oc][ic]: 32 lanes on 32 consecutive input channels.
     // Through a buffer resource: the lane's part of the offset (its input
     // channel, the rows of its half) in one VGPR, the (tap, slot) part
-    // uniform, so the 144 stores need no address registers of their own
-    // (64-bit addresses computed ahead of the loop held ~100 VGPRs through it).
+    // uniform, so the 144 stores need no address registers of their own.
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(part + (int64_t)split * 9 * Co * C, (uint32_t)(9 * Co * C * 4));
-    const int voff = ((oc0 + 4 * (lane >> 5)) * C + ic) * 4;
+    const int voff = ((oc0 + wm * 32 + 4 * h) * C + ic0 + wn * 32 + r32) * 4;
 #pragma unroll
     for (int t = 0; t < 9; ++t)
 #pragma unroll
@@ -413,7 +469,7 @@ void sum_splits_tap_kernel(const float *__restrict__ part, float *__restrict__ d
 
 bool wgrad3x3_ok(const Shape &sh) {
     return sh.ndim == 2 && sh.G == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil && sh.K == 3 && sh.s == 1 &&
-           sh.W % 8 == 0 && sh.C % 64 == 0 && (int64_t)9 * sh.Co * sh.C * 4 < (INT64_C(1) << 31) &&
+           sh.W % 8 == 0 && sh.W <= 64 && sh.C % 64 == 0 && (int64_t)9 * sh.Co * sh.C * 4 < (INT64_C(1) << 31) &&
            sh.Co % 64 == 0 && sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
 }
 
@@ -480,12 +536,12 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
 int wgrad_splits(const Shape &sh, bool aligned) {
     if (aligned && wgrad3x3_ok(sh)) {
         // about 256 workgroups (one round of one per CU) over (C/64) x (C_out/64)
-        // channel tiles: two rounds of shorter ranges measured 8% slower on the
-        // 3x3 layer (twice the partials to write and add)
+        // channel tiles, each a range of output rows: two rounds of shorter
+        // ranges measured 8% slower on the 3x3 layer (twice the partials)
         const int64_t tiles = (int64_t)(sh.C / 64) * (sh.Co / 64);
         int64_t s = (256 + tiles - 1) / tiles;
-        const int64_t most = sh.pixels() / 256;               // at least 16 steps of 16 positions
-        if (s > most) s = most;
+        const int64_t rows = (int64_t)sh.N * sh.H;
+        if (s > rows) s = rows;
         return (int)(s < 1 ? 1 : s);
     }
     if (wgrad_dw_ok(sh)) {
@@ -519,16 +575,28 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     const bool aligned = (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0;
     const int splits = wgrad_splits(sh, aligned);
     if (aligned && wgrad3x3_ok(sh)) {
-        const int Pi = (int)P;
-        const int chunk = (int)(((P + splits - 1) / splits + 15) / 16 * 16);
-        const int used = (int)((P + chunk - 1) / chunk);
+        const int NH = sh.N * sh.H;
+        const int per = (NH + splits - 1) / splits;
+        const int used = (NH + per - 1) / per;             // ranges that hold rows
         dim3 grid((unsigned)(sh.C / 64), (unsigned)(sh.Co / 64), (unsigned)used);
-        if (sh.dil == 2)
-            hipLaunchKernelGGL(wgrad3x3_kernel<2>, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi,
-                               chunk);
-        else
-            hipLaunchKernelGGL(wgrad3x3_kernel<1>, grid, dim3(256), 0, st, x, dout, part, sh.C, sh.Co, sh.H, sh.W, Pi,
-                               chunk);
+#define WGRAD3X3_GO(WV)                                                                                           \
+    if (sh.dil == 2)                                                                                              \
+        hipLaunchKernelGGL((wgrad3x3_kernel<WV, 2>), grid, dim3(256), 0, st, x, dout, part, sh.N, sh.C, sh.Co, sh.H, \
+                           per);                                                                                  \
+    else                                                                                                          \
+        hipLaunchKernelGGL((wgrad3x3_kernel<WV, 1>), grid, dim3(256), 0, st, x, dout, part, sh.N, sh.C, sh.Co, sh.H, \
+                           per)
+        switch (sh.W / 8) {
+            case 1: WGRAD3X3_GO(8); break;
+            case 2: WGRAD3X3_GO(16); break;
+            case 3: WGRAD3X3_GO(24); break;
+            case 4: WGRAD3X3_GO(32); break;
+            case 5: WGRAD3X3_GO(40); break;
+            case 6: WGRAD3X3_GO(48); break;
+            case 7: WGRAD3X3_GO(56); break;
+            default: WGRAD3X3_GO(64); break;
+        }
+#undef WGRAD3X3_GO
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = (int64_t)9 * sh.Co * sh.C;

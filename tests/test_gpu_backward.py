@@ -65,6 +65,8 @@ SMALL = [
     (2, 7, 8, (4, 8), 300, 1, 1, 0, 1, 1),        # db over image ranges of 2, 2, 2, 1 (rows of 32: 16-byte loads)
     (2, 2, 128, (13, 32), 128, 3, 1, 2, 2, 1),    # dilation 2: dx on the column-group kernel (pad 2d - 2 = 2)
     (2, 2, 128, (13, 32), 128, 3, 1, 1, 1, 4),    # groups of 32: dx on the grouped column-group kernel
+    (2, 1, 64, (9, 64), 64, 3, 1, 1, 1, 1),       # 3x3 dW, W = 64: copy instructions spread unevenly over waves
+    (2, 1, 64, (5, 40), 128, 3, 1, 2, 2, 1),      # 3x3 dW, dilation 2, W = 40 (padded 16-position steps)
 ]
 
 
