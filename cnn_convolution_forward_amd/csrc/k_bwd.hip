@@ -453,18 +453,44 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
                                                   ((t * Co + 8 * (r >> 2) + (r & 3)) * C) * 4, 0);
 }
 
-// dw[oc][ic][tap] = sum over splits, in order, of part[split][tap][oc][ic].
+// dw[oc][ic][tap] = sum over splits of part[split][tap][oc][ic], in a fixed
+// order.  A workgroup takes 32 groups of 4 consecutive elements; thread
+// (group, k) adds splits k*per .. k*per+per-1 in order with independent
+// 16-byte loads (all in flight at once), then the 8 partial sums of a group
+// are added in order k = 0 .. 7.  Each thread walking all splits by itself
+// was latency-bound (17.5 us for 38 MB on the 3x3 layer).
 __global__ __launch_bounds__(256)
 void sum_splits_tap_kernel(const float *__restrict__ part, float *__restrict__ dw, int Co, int C, int splits) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;      // (tap, oc, ic), ic fastest
-    const int64_t n = (int64_t)9 * Co * C;
-    if (e >= n) return;
-    float s = 0.f;
-    for (int i = 0; i < splits; ++i) s += part[(int64_t)i * n + e];
+    __shared__ float4 red[8][32];
+    const int g = threadIdx.x & 31, k = threadIdx.x >> 5;
+    const int64_t n4 = (int64_t)9 * Co * C / 4;              // float4 groups (C % 64 == 0)
+    const int64_t e4 = (int64_t)blockIdx.x * 32 + g;
+    const int per = (splits + 7) / 8;
+    const int i0 = k * per, i1 = i0 + per < splits ? i0 + per : splits;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e4 < n4) {
+        const float4 *p = reinterpret_cast<const float4 *>(part) + e4;
+#pragma unroll 8
+        for (int i = i0; i < i1; ++i) {
+            const float4 v = p[(int64_t)i * n4];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+    }
+    red[k][g] = acc;
+    __syncthreads();
+    if (k != 0 || e4 >= n4) return;
+    float4 sum = red[0][g];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+        const float4 v = red[j][g];
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    const int64_t e = e4 * 4;                                  // (tap, oc, ic), ic fastest
     const int ic = (int)(e % C);
     const int64_t r = e / C;
     const int ocv = (int)(r % Co), tap = (int)(r / Co);
-    dw[((int64_t)ocv * C + ic) * 9 + tap] = s;
+    float *d = dw + ((int64_t)ocv * C + ic) * 9 + tap;
+    d[0] = sum.x; d[9] = sum.y; d[18] = sum.z; d[27] = sum.w;
 }
 
 bool wgrad3x3_ok(const Shape &sh) {
@@ -599,8 +625,8 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
 #undef WGRAD3X3_GO
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t n = (int64_t)9 * sh.Co * sh.C;
-        hipLaunchKernelGGL(sum_splits_tap_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, sh.Co,
+        const int64_t n4 = (int64_t)9 * sh.Co * sh.C / 4;
+        hipLaunchKernelGGL(sum_splits_tap_kernel, dim3((unsigned)((n4 + 31) / 32)), dim3(256), 0, st, part, dw, sh.Co,
                            sh.C, used);
         return hipGetLastError();
     }
