@@ -523,8 +523,7 @@ conv_status_t conv_bwd_weight_bf16(const conv_params_t *prm, const uint16_t *x, 
     if (overlaps(dw, dwb, db, dbb) || overlaps(workspace, wsb, x, xb) || overlaps(workspace, wsb, dout, dob))
         return CONV_ERR_ALIAS;
     hipStream_t hs = (hipStream_t)stream;
-    if (db && convfwd::launch_bias_grad_bf16(sh, dout, (float *)workspace, db, hs) != hipSuccess) return CONV_ERR_HIP;
-    return to_status(convfwd::launch_wgrad_bf16(sh, x, dout, (float *)workspace, dw, hs));
+    return to_status(convfwd::launch_wgrad_bf16(sh, x, dout, (float *)workspace, dw, db, hs));
 }
 
 // ---- options: channels-last layout, ReLU, bf16 output ----

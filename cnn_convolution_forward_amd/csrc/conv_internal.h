@@ -74,7 +74,7 @@ void launch_flip_weights_bf16(const Shape &sh, const uint16_t *w, uint16_t *wfli
 int wgrad_splits(const Shape &sh, bool aligned);      // aligned: x and dout 16-byte aligned
 int64_t wgrad_workspace_floats(const Shape &sh);        // enough for either alignment
 hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
-                             hipStream_t st);
+                             float *db, hipStream_t st);   // db: NULL or the bias gradient, computed too
 // Winograd F(2x2, 3x3): 2D, K=3, stride 1, dilation 1, groups 1, NCHW, C % 16 == 0.
 bool winograd_supported(const Shape &sh);
 size_t winograd_workspace_bytes(const Shape &sh);

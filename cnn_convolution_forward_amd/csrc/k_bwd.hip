@@ -590,14 +590,23 @@ int wgrad_splits(const Shape &sh, bool aligned) {
 int64_t wgrad_workspace_floats(const Shape &sh) {
     // the 3x3 kernel runs only on 16-byte aligned x and dout; size the
     // workspace for whichever route the pointers select
-    const int a = wgrad_splits(sh, true), b = wgrad_splits(sh, false);
-    return (int64_t)(a > b ? a : b) * sh.w_elems();
+    const int64_t a = (int64_t)wgrad_splits(sh, true) * sh.w_elems();
+    const int64_t b = (int64_t)wgrad_splits(sh, false) * sh.w_elems();
+    return a > b ? a : b;
 }
 
 hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t *dout, float *part, float *dw,
-                             hipStream_t st) {
+                             float *db, hipStream_t st) {
     const int64_t P = sh.pixels();
     const int Kg = (int)sh.kgemm(), Cog = sh.Cog();
+    // the bias gradient first, its partials in the front of the workspace
+    // (the weight partials overwrite them afterwards, in stream order).  Folding
+    // it into the 3x3 weight kernel measured slower (its channel-tile-0
+    // workgroups, which set the makespan, took the extra LDS reads).
+    if (db) {
+        const hipError_t e = launch_bias_grad_bf16(sh, dout, part, db, st);
+        if (e != hipSuccess) return e;
+    }
     const bool aligned = (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0;
     const int splits = wgrad_splits(sh, aligned);
     if (aligned && wgrad3x3_ok(sh)) {
