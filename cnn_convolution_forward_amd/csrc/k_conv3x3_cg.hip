@@ -69,8 +69,7 @@ constexpr int kPix = 32;                 // LDS bytes per input pixel: 16 bf16, 
 constexpr int kTapBytes = kOc * 32;      // one tap's weights in LDS (2 KB)
 constexpr int kWStage = 9 * kTapBytes;   // 18432 bytes of weights per stage
 constexpr int kPackStage = 9 * kPackOcBlock * 32;   // 36864: one stage of a packed 128-channel block
-constexpr int kEpiOc = 16;               // channels per epilogue pass
-constexpr int kEpiBytes = kEpiOc * (kRows * 64 + 4) * 4;   // largest pass image (W = 64)
+constexpr int kEpiOc = 32;               // channels per epilogue pass
 
 // 16-byte half of an input pixel that holds channels 8h .. 8h+7 in LDS
 // input row rho: the halves swap on bit 2 of the row, so the 8 rows of a
@@ -124,96 +123,157 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const u
 }
 
 // Epilogue of a column-group tile (64 output channels x 8 output rows r0 +
-// DL*i x W of image n, channels ocb ..).
+// DL*i x W of image n, channels ocb ..).  Two passes of 32 channels through
+// LDS: in pass p wave row p writes its accumulators into the pass image
+// [channel 32][row 8][column W] (fp32, channel pitch 8W + 2 dwords), then all
+// four waves read it back and store it.
+//   Writes: a lane holds J consecutive columns c0 .. c0+J-1 of each (row,
+//   column group); they go out as 4-byte writes at immediate offsets from one
+//   lane base (paired by the compiler).  The pitch 8W + 2 puts 32 channels on
+//   16 banks: a 2-way conflict, against 4-way with half the lanes idle for a
+//   pitch of 8W + 4 and 16 channels a pass.  (An odd pitch would make the
+//   writes conflict-free but misalign the 8-byte readback; 8-byte writes need
+//   register pairs the accumulator layout does not give.)
+//   Readback (NCHW): a wave reads one channel at a time, lane i on the 8-byte
+//   units i, i+64, ... of that channel's 8 rows (consecutive in LDS), and
+//   stores each unit's 2 fp32 (or 4 bf16) outputs with one 8-byte store: the
+//   lane's output offsets are fixed for the whole epilogue and the channel
+//   comes in as the scalar offset, so no address is computed per chunk.
+//   Readback (NHWC): 16-byte chunks of one pixel's channels.
+template <int W>
+struct EpiGeo {
+    static constexpr int P = kRows * W + 2;        // channel pitch (dwords), 2 x odd
+    // a lane's last readback unit may lie past the last channel's 8 rows
+    // (units are read in steps of 64): 64 units of 8 (fp32 out) or 16 (bf16
+    // out) bytes per step
+    static constexpr int T2 = 64 * ((4 * W + 63) / 64) * 8, T4 = 64 * ((2 * W + 63) / 64) * 16;
+    static constexpr int TAIL = P * 4 > (T2 > T4 ? T2 : T4) ? P * 4 : (T2 > T4 ? T2 : T4);
+    static constexpr int BYTES = (kEpiOc - 1) * P * 4 + TAIL;
+};
+
+template <bool V>
+struct BoolC {
+    static constexpr bool value = V;
+};
+
 template <int D, int OUT, int NHWC, int DL>
 __device__ __forceinline__ void cg_epilogue(uint8_t *smem, const f32x16_t (&acc)[(Geo<D, DL>::J)], float *y, int n,
                                             int Co, int ocb, int H, int r0, int relu) {
     using G = Geo<D, DL>;
     constexpr int W = G::W, J = G::J;
+    constexpr int P = EpiGeo<W>::P;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int c0 = wn * J;
     const int HW = H * W;
-    // ---- epilogue: 4 passes of 16 channels through LDS, then whole rows out.
-    // Pass p: channels 16p .. 16p+15 = wave row wm = p/2, lanes with
-    // l32 / 16 == p % 2.  The pass image is [channel 16][row 8][column W]
-    // fp32 with a channel pitch of 8W + 4 dwords; a writer lane puts slot r
-    // (row 4h + r%4, group r/4) of fragment j at column c0 + j + D*(r/4).
-    // Readback: 16-byte chunks, consecutive threads on consecutive chunks of
-    // one channel's 8 rows -- a contiguous 32*W-byte block of y -- so every
-    // store instruction writes 1 KB of consecutive output.
     float *const epi = reinterpret_cast<float *>(smem);
     constexpr int kOutB = OUT ? 2 : 4;                   // bytes per output element
-    constexpr int kPer = 16 / kOutB;                     // outputs per 16-byte store
     // NCHW: this tile's 64 channel planes; NHWC: the image (pixel-major, C_out channels each)
     const __amdgpu_buffer_rsrc_t yr =
         NHWC ? make_rsrc((char *)y + (int64_t)n * HW * Co * kOutB, (uint32_t)HW * Co * kOutB)
              : make_rsrc((char *)y + ((int64_t)n * Co + ocb) * HW * kOutB, (uint32_t)kOc * HW * kOutB);
-    constexpr int kChPitch = kRows * W + 4;
-    constexpr int kChunks = kEpiOc * kRows * W / kPer;   // 16-byte chunks per pass
+    // writer lane: channel l32 of the pass, rows 4h .. 4h+3; slot r of
+    // fragment j is (row 4h + r%4, column c0 + j + D*(r/4))
+    float *const wdst = epi + l32 * P + 4 * h * W + c0;
+
+    // NCHW readback: 8-byte units of fp32 (2 values, or 4 for bf16 output),
+    // kU per channel, lane on units lane + 64*it
+    constexpr int kF = OUT ? 4 : 2;                      // fp32 values read per store
+    constexpr int kU = kRows * W / kF;
+    constexpr int kIt = (kU + 63) / 64;
+    uint32_t voff[kIt];
+    if (!NHWC) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+        for (int it = 0; it < kIt; ++it) {
+            const int u = lane + 64 * it, e = u * kF;
+            const int row = e / W, col = e - row * W, orow = r0 + DL * row;
+            voff[it] = (u < kU && orow < H) ? (uint32_t)((orow * W + col) * kOutB) : kOob;
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
         __builtin_amdgcn_sched_barrier(0);
-        if (wm == (p >> 1) && (l32 >> 4) == (p & 1)) {
-            float *dst = epi + (l32 & 15) * kChPitch + c0;
+        if (wm == p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = 4 * h + (r & 3), grp = r >> 2;
+                float *base = wdst + (r & 3) * W + (r >> 2) * D;
 #pragma unroll
-                for (int j = 0; j < J; ++j) dst[row * W + grp * D + j] = acc[j][r];
+                for (int j = 0; j < J; ++j) base[j] = acc[j][r];
             }
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-#pragma unroll
-        for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
-            const int cid = k * kThreads + tid;
-            if (kChunks % kThreads == 0 || cid < kChunks) {
-                float f[8];
-                uint32_t vo;
-                if (NHWC) {
-                    // chunk = (pixel, group of kPer channels of this pass)
-                    constexpr int kq = kEpiOc / kPer;
-                    const int px = cid / kq, qd = cid - px * kq;
-                    const int row = px / W, col = px - row * W;
-                    const int orow = r0 + DL * row;
-                    vo = orow < H ? (uint32_t)(((orow * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB) : kOob;
-#pragma unroll
-                    for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * kChPitch + row * W + col];
-                } else {
-                    const int ocl = cid / (kRows * W / kPer), e = cid - ocl * (kRows * W / kPer);   // e: chunk in the 8 rows
-                    const int row = (kPer * e) / W, orow = r0 + DL * row;
-                    vo = orow < H ? (uint32_t)(((p * kEpiOc + ocl) * HW + orow * W + kPer * e - row * W) * kOutB)
-                                  : kOob;
-                    const float *src = epi + ocl * kChPitch + kPer * e;
-                    const float4 lo = *reinterpret_cast<const float4 *>(src);
-                    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-                    if (kPer == 8) {
-                        const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-                        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+        // the ReLU choice is one uniform branch around the whole readback
+        auto readback = [&](auto rc) {
+            constexpr bool R = decltype(rc)::value;
+            if (NHWC) {
+                // chunk = (pixel, group of kPer channels of this pass)
+                constexpr int kPer = 16 / kOutB;
+                constexpr int kq = kEpiOc / kPer;
+                constexpr int kChunks = kRows * W * kq;
+    #pragma unroll
+                for (int k = 0; k < (kChunks + kThreads - 1) / kThreads; ++k) {
+                    const int cid = k * kThreads + tid;
+                    if (kChunks % kThreads == 0 || cid < kChunks) {
+                        const int px = cid / kq, qd = cid - px * kq;
+                        const int row = px / W, col = px - row * W;
+                        const int orow = r0 + DL * row;
+                        const uint32_t vo =
+                            orow < H ? (uint32_t)(((orow * W + col) * Co + ocb + p * kEpiOc + qd * kPer) * kOutB) : kOob;
+                        float f[8];
+    #pragma unroll
+                        for (int u = 0; u < kPer; ++u) f[u] = epi[(qd * kPer + u) * P + row * W + col];
+                        u32x4_t va;
+                        if (OUT == 0) {
+    #pragma unroll
+                            for (int u = 0; u < 4; ++u) va[u] = __float_as_uint(R ? fmaxf(f[u], 0.f) : f[u]);
+                        } else {
+                            uint32_t b[8];
+    #pragma unroll
+                            for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(R ? fmaxf(f[u], 0.f) : f[u]);
+                            va = (u32x4_t){b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                                           b[6] | (b[7] << 16)};
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
                     }
                 }
-                u32x4_t va;
-                if (OUT == 0) {
-                    float4 a4 = make_float4(f[0], f[1], f[2], f[3]);
-                    if (relu) {
-                        a4.x = fmaxf(a4.x, 0.f); a4.y = fmaxf(a4.y, 0.f);
-                        a4.z = fmaxf(a4.z, 0.f); a4.w = fmaxf(a4.w, 0.f);
+            } else {
+                // wave w: channels 8w .. 8w+7 of the pass
+    #pragma unroll
+                for (int i = 0; i < kEpiOc / 4; ++i) {
+                    const int c = wave * (kEpiOc / 4) + i;
+                    const float *src = epi + c * P + lane * kF;
+                    const uint32_t soff = (uint32_t)((p * kEpiOc + c) * HW * kOutB);
+    #pragma unroll
+                    for (int it = 0; it < kIt; ++it) {
+                        float f[4];
+                        const float2 a = *reinterpret_cast<const float2 *>(src + it * 64 * kF);
+                        f[0] = a.x; f[1] = a.y;
+                        if (OUT) {
+                            const float2 b = *reinterpret_cast<const float2 *>(src + it * 64 * kF + 2);
+                            f[2] = b.x; f[3] = b.y;
+                        }
+                        u32x2_t va;
+                        if (OUT == 0) {
+                            va[0] = __float_as_uint(R ? fmaxf(f[0], 0.f) : f[0]);
+                            va[1] = __float_as_uint(R ? fmaxf(f[1], 0.f) : f[1]);
+                        } else {
+                            uint32_t b[4];
+    #pragma unroll
+                            for (int u = 0; u < 4; ++u) b[u] = f32_to_bf16_rne(R ? fmaxf(f[u], 0.f) : f[u]);
+                            va[0] = b[0] | (b[1] << 16);
+                            va[1] = b[2] | (b[3] << 16);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b64(va, yr, (int)voff[it], (int)soff, 0);
                     }
-                    va = (u32x4_t){__float_as_uint(a4.x), __float_as_uint(a4.y), __float_as_uint(a4.z),
-                                   __float_as_uint(a4.w)};
-                } else {
-                    uint32_t b[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) b[u] = f32_to_bf16_rne(relu ? fmaxf(f[u], 0.f) : f[u]);
-                    va = (u32x4_t){b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
                 }
-                __builtin_amdgcn_raw_buffer_store_b128(va, yr, (int)vo, 0, 0);
             }
-        }
-        if (p < 3) __syncthreads();
+        };
+        if (relu) readback(BoolC<true>{}); else readback(BoolC<false>{});
+        if (p < 1) __syncthreads();
     }
 }
 
@@ -229,7 +289,7 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     using G = Geo<D, DL>;
     constexpr int W = G::W, J = G::J, RP = G::RP;
     __shared__ __align__(16) uint8_t smem[G::LDS];
-    static_assert(G::LDS >= kEpiBytes, "the epilogue image overlays the stage buffers");
+    static_assert(G::LDS >= EpiGeo<W>::BYTES, "the epilogue image overlays the stage buffers");
     static_assert(G::LDS <= 80 * 1024, "two workgroups per CU");
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -400,7 +460,8 @@ void conv3x3cg_gp_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
     using G = Geo<D, 1>;
     constexpr int W = G::W, J = G::J, RP = G::RP;
     constexpr int kLds = kWStage + 2 * G::IN_BYTES;
-    __shared__ __align__(16) uint8_t smem[kLds > kEpiBytes ? kLds : kEpiBytes];
+    constexpr int kEpiB = EpiGeo<W>::BYTES;
+    __shared__ __align__(16) uint8_t smem[kLds > kEpiB ? kLds : kEpiB];
     static_assert(kLds <= 80 * 1024, "two workgroups per CU");
 
     const int tid = threadIdx.x, lane = tid & 63;
