@@ -6,6 +6,7 @@
 namespace convfwd {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte halves of a 32-byte weight row (one output channel, 16 input
 // channels) are swapped on bit 2 xor bit 3 of the row, so 16-byte accesses of

@@ -37,7 +37,6 @@ __device__ __forceinline__ uint4 pack8(const uint16_t (&v)[8]) {
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Buffer resource over `bytes` bytes at p (raw buffer, 32-bit offsets).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
