@@ -1,4 +1,5 @@
-// conv3x3_common.h -- device helpers shared by the two 3x3 stride-1 kernels.
+// conv3x3_common.h -- device helpers shared by the 3x3 stride-1 kernels and
+// the streaming pointwise kernel (LDS copies, waits, operand packing).
 #pragma once
 
 #include "mfma_common.h"

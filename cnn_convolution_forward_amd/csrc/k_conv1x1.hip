@@ -8,6 +8,11 @@
 // of x.  No gather and no padding: the kernel is a plain GEMM whose B operand
 // is read in NCHW order.
 //
+// Two kernels.  NCHW layers with C_in in {64, 128, 256} and C_out a
+// multiple of 128 take the streaming kernel at the end of this file
+// (persistent workgroups, weights held in registers, the stores of one tile
+// overlapping the MFMAs of the next); the tiled kernel below takes the rest.
+//
 // Tiling: a workgroup computes 128 output channels x 128 output pixels (the
 // pixel axis runs over N * plane, so a tile may straddle two images); four
 // waves in a 2 x 2 grid, each 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K loop in
