@@ -88,6 +88,19 @@ struct Geo {
     static constexpr int UNITS = 2 * kInRows * (W / 8);   // input load units per stage
 };
 
+// Zero the halo columns (the DL left and RP - W - DL right ones, 32 bytes per
+// pixel) of nb consecutive input images [row 10][col RP] at dst.
+template <int W, int RP, int DL>
+__device__ __forceinline__ void zero_halo(uint8_t *dst, int nb, int tid) {
+    constexpr int HC = RP - W;
+    for (int i = tid; i < nb * kInRows * HC * 2; i += kThreads) {
+        const int hh = i & 1, rest = i >> 1;
+        const int c = rest % HC, rb = rest / HC;            // rb = image * 10 + row
+        const int col = c < DL ? c : W + c;
+        reinterpret_cast<uint4 *>(dst + (rb * RP + col) * kPix)[hh] = make_uint4(0, 0, 0, 0);
+    }
+}
+
 // The MFMAs of input-fragment column q (column c0 - 1 + q of this wave's
 // range) and kernel row rr: the fragment serves output fragment j = q - kw
 // for the three horizontal taps kw.
@@ -389,10 +402,10 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     const uint32_t b2_base = (uint32_t)(((((l32 & 7) + 2) * RP) + D * (l32 >> 3) + c0) * kPix +
                                         in_half(h, (l32 & 7) + 2) * 16);
 
-    // zero both input buffers: halo columns are never written again
-    for (int i = tid; i < 2 * G::IN_BYTES / 16; i += kThreads)
-        reinterpret_cast<uint4 *>(ibuf)[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
+    // zero the halo columns of both input buffers (DL on the left, RP - W -
+    // DL on the right): the loader writes every other column of all 10 rows
+    // each stage (rows outside the image as zeros) and never these
+    zero_halo<W, RP, DL>(ibuf, 2, tid);
 
     // ---- prologue: stage 0
     dma_w(0, 0);
@@ -556,9 +569,8 @@ void conv3x3cg_gp_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
     const uint32_t b2_base = pl_off + (uint32_t)(((((l32 & 7) + 2) * RP) + D * (l32 >> 3) + c0) * kPix +
                                                  in_half(h, (l32 & 7) + 2) * 16);
 
-    // zero both planes: halo columns are never written again
-    for (int i = tid; i < 2 * G::IN_BYTES / 16; i += kThreads)
-        reinterpret_cast<uint4 *>(ibuf)[i] = make_uint4(0, 0, 0, 0);
+    // zero the halo columns of both planes (never written by the loader)
+    zero_halo<W, RP, 1>(ibuf, 2, tid);
     const float bv = bias ? bias[ocb + wm * 32 + l32] : 0.f;
     f32x16_t acc[J];
 #pragma unroll

@@ -9,8 +9,11 @@
 //
 // Three kernels:
 //  1. U[xi][k][c] = (G g[k][c] G^T)[xi], fp16, once per call;
-//  2. V[xi][t][c] = (B^T d[c][t] B)[xi], fp16, for every 2x2 output block t
-//     (its 4x4 input block d, zero outside the image);
+//  2. V[xi][c/32][t][c%32] = (B^T d[c][t] B)[xi], fp16, for every 2x2 output
+//     block t (channels in tiles of 32, so a tile's blocks are contiguous)
+//     (its 4x4 input block d, zero outside the image) -- from LDS tiles of
+//     32 channels x 32 blocks when C_in % 32 == 0 and W % 8 == 0, else one
+//     thread per (block, 8 channels) straight from global memory;
 //  3. for each of the 16 transform points xi the GEMM M[xi] = U[xi] @ V[xi]^T
 //     (C_out x blocks, reduction over C_in) on v_mfma_f32_32x32x16_f16 with
 //     fp32 accumulation, then, in the same workgroup, Y = A^T M A per block,
@@ -126,33 +129,121 @@ void wino_input_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ V,
     }
 #pragma unroll
     for (int xi = 0; xi < 16; ++xi)
-        *reinterpret_cast<uint4 *>(V + ((int64_t)xi * T + t) * C + c0) =
+        *reinterpret_cast<uint4 *>(V + (((int64_t)xi * ((C + 31) / 32) + c0 / 32) * T + t) * 32 + (c0 & 31)) =
             make_uint4(out[xi][0], out[xi][1], out[xi][2], out[xi][3]);
+}
+
+// 2'. V for C_in % 32 == 0 and W % 8 == 0: a workgroup takes 32 channels x
+// 32 consecutive blocks of one block row (input rows 2bh - p .. +3).
+//   Copy: the 4 input rows of the 32 channels go to LDS in aligned 16-byte
+//   units (8 pixels, wholly inside or outside the image since W % 8 == 0;
+//   outside ones, and rows outside the image, read as zeros): [c][row][80 px].
+//   Transform: lane b on block b, four channels per thread; the 4 x 4 input
+//   block of block b starts 2b pixels into the copied rows.
+//   Store: each thread writes its 4 channels (8 bytes) of every xi; the 8
+//   threads of a block fill its 64-byte row of the channel tile, and a tile's
+//   blocks are consecutive rows.
+constexpr int kWiC = 32, kWiB = 32;       // channels, blocks per workgroup
+constexpr int kWiRow = 80;                // pixels per copied row (10 units)
+
+__global__ __launch_bounds__(256)
+void wino_input_tile_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ V, int C, int H, int W, int p,
+                            int TH, int TW, int64_t T, int nbw) {
+    __shared__ __align__(16) uint16_t Xs[kWiC * 4 * kWiRow];
+    const int tid = threadIdx.x;
+    const int c0 = blockIdx.x * kWiC;
+    int r = blockIdx.y;
+    const int bwg = r % nbw;
+    r /= nbw;
+    const int bh = r % TH;
+    const int n = r / TH;
+    const int bw0 = bwg * kWiB;
+    const int cs = 2 * bw0 - p;                            // first input column of the tile
+    const int a0 = (cs >= 0 ? cs / 8 : -((7 - cs) / 8)) * 8;   // aligned start (floor)
+    const int64_t HW = (int64_t)H * W;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + ((int64_t)n * C + c0) * HW, (uint32_t)(kWiC * HW * 2));
+    // copy: unit u -> (channel, row, 8-pixel unit k), k fastest
+    for (int u = tid; u < kWiC * 4 * (kWiRow / 8); u += 256) {
+        const int k = u % (kWiRow / 8), cr = u / (kWiRow / 8);
+        const int i = cr & 3, c = cr >> 2;
+        const int ih = 2 * bh - p + i, iw = a0 + 8 * k;
+        const bool in = 0 <= ih && ih < H && 0 <= iw && iw < W;
+        const uint4 v = bload16(xr, in ? (uint32_t)((c * HW + (int64_t)ih * W + iw) * 2) : kOob, 0);
+        *reinterpret_cast<uint4 *>(&Xs[(c * 4 + i) * kWiRow + 8 * k]) = v;
+    }
+    __syncthreads();
+    // transform: thread (block b, channels 4q .. 4q+3)
+    {
+        const int b = tid & 31, q = tid >> 5;
+        const int col0 = cs - a0 + 2 * b;
+        uint32_t out[16][2];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int c = 4 * q + cc;
+            float d[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[i][j] = bf16_to_f32(Xs[(c * 4 + i) * kWiRow + col0 + j]);
+            float s4[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s4[0][j] = d[0][j] - d[2][j];
+                s4[1][j] = d[1][j] + d[2][j];
+                s4[2][j] = d[2][j] - d[1][j];
+                s4[3][j] = d[1][j] - d[3][j];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v[4] = {s4[i][0] - s4[i][2], s4[i][1] + s4[i][2], s4[i][2] - s4[i][1], s4[i][1] - s4[i][3]};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t h = f16_bits(v[j]);
+                    uint32_t &slot = out[4 * i + j][cc >> 1];
+                    slot = (cc & 1) ? (slot | (h << 16)) : h;
+                }
+            }
+        }
+        if (bw0 + b < TW) {
+            const int64_t CT = C / 32;
+            const int64_t t = ((int64_t)n * TH + bh) * TW + bw0 + b;
+            uint16_t *dst = V + ((int64_t)blockIdx.x * T + t) * 32 + 4 * q;    // xi = 0, channel tile c0 / 32
+#pragma unroll
+            for (int xi = 0; xi < 16; ++xi)
+                *reinterpret_cast<uint2 *>(dst + (int64_t)xi * CT * T * 32) = make_uint2(out[xi][0], out[xi][1]);
+        }
+    }
 }
 
 // 3. 16 GEMMs + output transform.  LDS holds the 16 x 32 x 32 fp32 results
 // (64 KB; reads run along blocks, conflict-free).
 __global__ __launch_bounds__(256)
 void wino_gemm_kernel(const uint16_t *__restrict__ U, const uint16_t *__restrict__ V, const float *__restrict__ bias,
-                      float *__restrict__ y, Shape sh, int TH, int TW, int64_t T) {
+                      float *__restrict__ y, Shape sh, int TH, int TW, int64_t T, int nkt, int remap) {
     __shared__ float Ms[16][32][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = sh.C, Co = sh.Co;
-    const int k0 = blockIdx.x * 32;
-    const int64_t t0 = (int64_t)blockIdx.y * 32;
+    // block -> (channel tile, block tile): the channel tiles of one block tile
+    // are consecutive logical tiles, and with remap each XCD (block % 8) runs a
+    // contiguous range of them, so V's rows for a block tile come from one L2
+    int64_t L = blockIdx.x;
+    if (remap) L = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int k0 = (int)(L % nkt) * 32;
+    const int64_t t0 = (L / nkt) * 32;
     const int64_t plane = (int64_t)Co * C;
-    // A: U[xi][k0 + lane%32][c + 8*(lane/32)], B: V[xi][t0 + lane%32][c + 8*(lane/32)]
+    // A: U[xi][k0 + lane%32][c + 8*(lane/32)], B: V[xi][c/32][t0 + lane%32][c%32 + 8*(lane/32)]
     const int kr = k0 + (lane & 31);
     const int64_t tr = t0 + (lane & 31);
     const int coff = 8 * (lane >> 5);
     const __amdgpu_buffer_rsrc_t ur = make_rsrc(U, (uint32_t)(16 * plane * 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, (uint32_t)(16 * T * C * 2));
+    const int CT = (C + 31) / 32;
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, (uint32_t)(16 * CT * T * 64));
     uint32_t ao[4], bo[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int xi = 4 * wave + q;
         ao[q] = kr < Co ? (uint32_t)(((int64_t)xi * plane + (int64_t)kr * C + coff) * 2) : kOob;
-        bo[q] = tr < T ? (uint32_t)((((int64_t)xi * T + tr) * C + coff) * 2) : kOob;
+        bo[q] = tr < T ? (uint32_t)((((int64_t)xi * CT * T + tr) * 32 + coff) * 2) : kOob;
     }
     f32x16_t acc[4];
 #pragma unroll
@@ -169,11 +260,12 @@ void wino_gemm_kernel(const uint16_t *__restrict__ U, const uint16_t *__restrict
     const int nst = C / 16;
     for (int st = 0; st < nst; ++st) {
         if (st + 1 < nst) {
-            const uint32_t so = (uint32_t)(st + 1) * 32u;   // 16 channels = 32 bytes
+            const uint32_t so = (uint32_t)(st + 1) * 32u;   // U: 16 channels = 32 bytes
+            const uint32_t vso = (uint32_t)(((st + 1) >> 1) * T * 64 + ((st + 1) & 1) * 32);   // V: tile, half
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 an[q] = bload16(ur, ao[q] == kOob ? kOob : ao[q] + so, 0);
-                bn[q] = bload16(vr, bo[q] == kOob ? kOob : bo[q] + so, 0);
+                bn[q] = bload16(vr, bo[q] == kOob ? kOob : bo[q] + vso, 0);
             }
         }
 #pragma unroll
@@ -241,7 +333,7 @@ WinoGeom wino_geom(const Shape &sh) {
     g.TW = (sh.Wo + 1) / 2;
     g.T = (int64_t)sh.N * g.TH * g.TW;
     g.u_bytes = ((size_t)16 * sh.Co * sh.C * 2 + 255) / 256 * 256;
-    g.v_bytes = (size_t)16 * g.T * sh.C * 2;
+    g.v_bytes = (size_t)16 * g.T * ((sh.C + 31) / 32) * 64;
     return g;
 }
 
@@ -251,8 +343,10 @@ bool winograd_supported(const Shape &sh) {
     if (!(sh.ndim == 2 && sh.K == 3 && sh.s == 1 && sh.dil == 1 && sh.G == 1 && !sh.nhwc && sh.C % 16 == 0))
         return false;
     const WinoGeom g = wino_geom(sh);
-    // 32-bit buffer offsets into U and V; grid y below 2^31
-    return (int64_t)16 * sh.Co * sh.C * 2 < (INT64_C(1) << 31) && (int64_t)16 * g.T * sh.C * 2 < (INT64_C(1) << 31);
+    // 32-bit buffer offsets into U and V; the GEMM grid (256 threads a block) below 2^32 threads
+    return (int64_t)16 * sh.Co * sh.C * 2 < (INT64_C(1) << 31) &&
+           (int64_t)16 * g.T * ((sh.C + 31) / 32) * 64 < (INT64_C(1) << 31) &&
+           (int64_t)((sh.Co + 31) / 32) * ((g.T + 31) / 32) < (INT64_C(1) << 24);
 }
 
 size_t winograd_workspace_bytes(const Shape &sh) {
@@ -267,11 +361,20 @@ hipError_t launch_winograd_bf16(const Shape &sh, const uint16_t *x, const uint16
     uint16_t *V = (uint16_t *)((char *)ws + g.u_bytes);
     const int64_t nu = (int64_t)sh.Co * sh.C;
     hipLaunchKernelGGL(wino_weight_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, w, U, sh.Co, sh.C);
-    const int64_t nv = g.T * (sh.C / 8);
-    hipLaunchKernelGGL(wino_input_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, x, V, sh.C, sh.H, sh.W,
-                       sh.p, g.TH, g.TW, g.T);
-    dim3 grid((unsigned)((sh.Co + 31) / 32), (unsigned)((g.T + 31) / 32));
-    hipLaunchKernelGGL(wino_gemm_kernel, grid, dim3(256), 0, st, U, V, bias, y, sh, g.TH, g.TW, g.T);
+    if (sh.C % kWiC == 0 && sh.W % 8 == 0) {
+        const int nbw = (g.TW + kWiB - 1) / kWiB;
+        dim3 gi((unsigned)(sh.C / kWiC), (unsigned)((int64_t)sh.N * g.TH * nbw));
+        hipLaunchKernelGGL(wino_input_tile_kernel, gi, dim3(256), 0, st, x, V, sh.C, sh.H, sh.W, sh.p, g.TH, g.TW, g.T,
+                           nbw);
+    } else {
+        const int64_t nv = g.T * (sh.C / 8);
+        hipLaunchKernelGGL(wino_input_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, x, V, sh.C, sh.H,
+                           sh.W, sh.p, g.TH, g.TW, g.T);
+    }
+    const int nkt = (sh.Co + 31) / 32;
+    const int64_t nblk = (int64_t)nkt * ((g.T + 31) / 32);
+    hipLaunchKernelGGL(wino_gemm_kernel, dim3((unsigned)nblk), dim3(256), 0, st, U, V, bias, y, sh, g.TH, g.TW, g.T, nkt,
+                       nblk % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 

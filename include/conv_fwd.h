@@ -297,7 +297,8 @@ typedef struct {
  * (NCHW, dilation 1); any epilogue, and channels-last for groups 1) or, with
  * algo CONV_ALGO_WINOGRAD, needs
  * (the fp16 transformed weights, 16 x C_out x C_in, and transformed input
- * blocks, 16 x N*ceil(H_out/2)*ceil(W_out/2) x C_in); 0 when none, or on
+ * blocks, 16 x N*ceil(H_out/2)*ceil(W_out/2) x C_in rounded up to a multiple
+ * of 32); 0 when none, or on
  * invalid arguments or a shape Winograd does not take. */
 CONV_API size_t conv_fwd_ex_workspace_bytes(const conv_params_t *params, const conv_options_t *opts, int algo);
 

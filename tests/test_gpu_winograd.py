@@ -49,6 +49,12 @@ SHAPES = [
     (2, 16, 7, 13, 130, 2),      # C_out past four 32-row tiles, pad 2
     (3, 48, 12, 10, 40, 1),      # several block tiles of 32
     (1, 16, 1, 1, 8, 1),         # one input pixel: only the centre tap
+    # C_in % 32 == 0 and W % 8 == 0: the input transform from LDS tiles of 32 channels x 32 blocks
+    (2, 64, 10, 16, 40, 1),      # pad 1: the tile starts one pixel left of the image
+    (1, 32, 9, 40, 16, 2),       # pad 2, odd height
+    (2, 96, 6, 72, 32, 1),       # 37 blocks a row: a second, ragged block tile
+    (1, 32, 16, 8, 8, 3),        # pad 3
+    (1, 64, 5, 64, 24, 0),       # pad 0, 31 blocks a row
 ]
 
 
