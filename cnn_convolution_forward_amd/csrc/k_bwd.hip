@@ -51,7 +51,10 @@ void flip_weights_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ 
     wf[(((int64_t)g * Cg + j) * Cog + ocl) * taps + (taps - 1 - t)] = w[e];
 }
 
-template <int BM>
+// BVEC: a pointwise layer (K = 1, stride 1, pad 0, plane % 8 == 0, 16-byte
+// aligned x): X_col^T is x itself, so B loads like A -- 16 bytes of 8
+// consecutive positions, four lanes on one column's 32 positions.
+template <int BM, int BVEC>
 __global__ __launch_bounds__(256)
 void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
                   float *__restrict__ part, int64_t P, int Kg, int64_t chunk, int splits, int g0, int a_vec) {
@@ -114,6 +117,23 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
                 a_reg[i] = pack8(v);
             }
         }
+        if (BVEC) {
+            // unit u -> (column u / 4, positions 8 (u % 4) ..): ranges are
+            // multiples of 32 and P of 8, so a unit is all in or all out
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int u = tid + 256 * i;
+                const int jc = n0 + (u >> 2);
+                const int64_t kk = k0 + (u & 3) * 8;
+                if (jc < Kg && kk < k_end) {
+                    const int n = (int)kk / (int)plane, q = (int)kk - n * (int)plane;
+                    b_reg[i] = *reinterpret_cast<const uint4 *>(x + ((int64_t)n * sh.C + grp * Cg + jc) * plane + q);
+                } else {
+                    b_reg[i] = make_uint4(0, 0, 0, 0);
+                }
+            }
+            return;
+        }
         // B: x at the tap of column jcol for 8 consecutive positions
         // (32-bit position arithmetic: P = N * output positions < 2^31)
 #pragma unroll
@@ -146,8 +166,13 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
             *reinterpret_cast<uint4 *>(&As[buf][u >> 2][(u & 3) * 8]) = a_reg[i];
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<uint4 *>(&Bs[buf][bj][(bkq + 2 * i) * 8]) = b_reg[i];
+        for (int i = 0; i < 2; ++i) {
+            const int u = tid + 256 * i;
+            if (BVEC)
+                *reinterpret_cast<uint4 *>(&Bs[buf][u >> 2][(u & 3) * 8]) = b_reg[i];
+            else
+                *reinterpret_cast<uint4 *>(&Bs[buf][bj][(bkq + 2 * i) * 8]) = b_reg[i];
+        }
     };
 
     f32x16_t acc[MI][2];
@@ -509,6 +534,49 @@ void sum_splits_kernel(const float *__restrict__ part, float *__restrict__ dw, i
     dw[e] = s;
 }
 
+// The same sum for n % 4 == 0 and 16-byte aligned part and dw, with the
+// order of sum_splits_tap_kernel: thread (group g of 4 elements, k) adds
+// splits k*per .. k*per+per-1 in order with independent 16-byte loads, then
+// the 8 partial sums of a group are added in order k = 0 .. 7.
+__global__ __launch_bounds__(256)
+void sum_splits_vec_kernel(const float *__restrict__ part, float *__restrict__ dw, int64_t n4, int splits) {
+    __shared__ float4 red[8][32];
+    const int g = threadIdx.x & 31, k = threadIdx.x >> 5;
+    const int64_t e4 = (int64_t)blockIdx.x * 32 + g;
+    const int per = (splits + 7) / 8;
+    const int i0 = k * per, i1 = i0 + per < splits ? i0 + per : splits;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e4 < n4) {
+        const float4 *p = reinterpret_cast<const float4 *>(part) + e4;
+#pragma unroll 8
+        for (int i = i0; i < i1; ++i) {
+            const float4 v = p[(int64_t)i * n4];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+    }
+    red[k][g] = acc;
+    __syncthreads();
+    if (k != 0 || e4 >= n4) return;
+    float4 sum = red[0][g];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+        const float4 v = red[j][g];
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    reinterpret_cast<float4 *>(dw)[e4] = sum;
+}
+
+hipError_t launch_sum_splits(const float *part, float *out, int64_t n, int splits, hipStream_t st) {
+    if (n % 4 == 0 && (uintptr_t)part % 16 == 0 && (uintptr_t)out % 16 == 0) {
+        const int64_t n4 = n / 4;
+        hipLaunchKernelGGL(sum_splits_vec_kernel, dim3((unsigned)((n4 + 31) / 32)), dim3(256), 0, st, part, out, n4,
+                           splits);
+    } else {
+        hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, out, n, splits);
+    }
+    return hipGetLastError();
+}
+
 // Partial bias gradient: workgroup (oc, r) sums channel oc over images
 // [r*per, min(N, (r+1)*per)), reading the images' rows of dout as one flat
 // run of bf16 values (16 bytes a load when the base is 16-byte aligned and
@@ -651,32 +719,33 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = sh.w_elems();
-        hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, n,
-                           used);
+        const hipError_t e2 = launch_sum_splits(part, dw, n, used, st);
+        if (e2 != hipSuccess) return e2;
         return hipGetLastError();
     }
     const int64_t chunk = ((P + splits - 1) / splits + kBK - 1) / kBK * kBK;
     const int64_t plane = sh.out_plane();
     const int a_vec = (plane % 8 == 0) && ((uintptr_t)dout % 16 == 0);
+    const bool b_vec = a_vec && sh.K == 1 && sh.Kd == 1 && sh.s == 1 && sh.sd == 1 && sh.p == 0 && sh.pd == 0 &&
+                       ((uintptr_t)x % 16 == 0);
     const unsigned gx = (unsigned)((Kg + kBN - 1) / kBN);
     const int gmax = 65535 / splits;                    // groups per launch (grid z = splits * groups)
     for (int g0 = 0; g0 < sh.G; g0 += gmax) {
         const int ng = sh.G - g0 < gmax ? sh.G - g0 : gmax;
+#define WGRAD_GO(BMV, BV)                                                                                    \
+    hipLaunchKernelGGL((wgrad_kernel<BMV, BV>), dim3(gx, (unsigned)((Cog + BMV - 1) / BMV), (unsigned)(splits * ng)), \
+                       dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits, g0, a_vec)
         if (Cog > 64) {
-            dim3 grid(gx, (unsigned)((Cog + 127) / 128), (unsigned)(splits * ng));
-            hipLaunchKernelGGL((wgrad_kernel<128>), grid, dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits,
-                               g0, a_vec);
+            if (b_vec) WGRAD_GO(128, 1); else WGRAD_GO(128, 0);
         } else {
-            dim3 grid(gx, (unsigned)((Cog + 63) / 64), (unsigned)(splits * ng));
-            hipLaunchKernelGGL((wgrad_kernel<64>), grid, dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits,
-                               g0, a_vec);
+            if (b_vec) WGRAD_GO(64, 1); else WGRAD_GO(64, 0);
         }
+#undef WGRAD_GO
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t n = sh.w_elems();
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, dw, n, splits);
-    return hipGetLastError();
+    return launch_sum_splits(part, dw, n, splits, st);
 }
 
 int bias_grad_ranges(const Shape &sh) {
@@ -696,9 +765,7 @@ hipError_t launch_bias_grad_bf16(const Shape &sh, const uint16_t *dout, float *p
     hipLaunchKernelGGL(bias_grad_part_kernel, dim3((unsigned)sh.Co, (unsigned)ranges), dim3(256), 0, st, dout, part,
                        sh.N, sh.Co, sh.out_plane(), per,
                        (int)(sh.out_plane() % 8 == 0 && (uintptr_t)dout % 16 == 0));
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((sh.Co + 255) / 256)), dim3(256), 0, st, part, db,
-                       (int64_t)sh.Co, ranges);
-    return hipGetLastError();
+    return launch_sum_splits(part, db, (int64_t)sh.Co, ranges, st);
 }
 
 }  // namespace convfwd

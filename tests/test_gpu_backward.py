@@ -67,6 +67,11 @@ SMALL = [
     (2, 2, 128, (13, 32), 128, 3, 1, 1, 1, 4),    # groups of 32: dx on the grouped column-group kernel
     (2, 1, 64, (9, 64), 64, 3, 1, 1, 1, 1),       # 3x3 dW, W = 64: copy instructions spread unevenly over waves
     (2, 1, 64, (5, 40), 128, 3, 1, 2, 2, 1),      # 3x3 dW, dilation 2, W = 40 (padded 16-position steps)
+    # pointwise with plane % 8 == 0: dW's x operand read in 16-byte pieces like dout
+    (2, 3, 64, (8, 12), 96, 1, 1, 0, 1, 1),       # 3 images, ragged column and channel tiles
+    (2, 4, 256, (16, 16), 512, 1, 1, 0, 1, 1),    # two 128-column tiles, four channel tiles
+    (2, 2, 64, (4, 8), 128, 1, 1, 0, 1, 4),       # groups of 16 input channels
+    (3, 2, 32, (2, 4, 8), 48, 1, 1, 0, 1, 1),     # 3D pointwise
 ]
 
 
@@ -90,11 +95,12 @@ def test_backward_integer_exact(case):
     compare(db, rdb, None, 0, exact=True, label="db %s" % (case,))
 
 
-@pytest.mark.parametrize("name", ["conv3x3_bf16", "dilated3x3_bf16"])
+@pytest.mark.parametrize("name", ["conv3x3_bf16", "dilated3x3_bf16", "conv1x1_bf16"])
 @pytest.mark.parametrize("integer", [False, True])
 def test_backward_full_3x3_layer_sampled(name, integer):
-    """x (64,128,56,56), w (128,128,3,3), s1 p1 (and dilation 2, p2): every db
-    entry, 256 dw entries (each a sum over 200704 positions) and 4000 dx entries."""
+    """x (64,128,56,56), w (128,128,3,3), s1 p1 (and dilation 2, p2), and the
+    pointwise layer x (32,256,28,28), w (1024,256,1,1): every db entry, 256 dw
+    entries (each a sum over all N * H * W positions) and 4000 dx entries."""
     wl = synth.ALL_WORKLOADS[name]
     t = synth.make_inputs(wl, integer=integer)
     rng = np.random.default_rng(99)
