@@ -22,6 +22,8 @@
 // is stored at once -- 32 lanes on 32 consecutive pixels of one channel -- so
 // the output, which dominates the traffic (4 * C_out bytes per pixel against
 // 2 * C_in * s^dims read), leaves as a continuous stream of full lines.
+#include <atomic>
+
 #include "conv_internal.h"
 #include "mfma_common.h"
 
@@ -31,7 +33,6 @@ namespace {
 constexpr int kOcBlock = 64;            // output channels per workgroup
 constexpr int kMaxK = 128;              // C_in * K^dims, padded to 16
 constexpr int kPatchElems = 16384;      // LDS patch budget (32 KB)
-constexpr int kTargetPx = 512;
 
 struct SmallKPlan {
     int TR;          // output rows per tile
@@ -244,18 +245,81 @@ bool vec_ok(const Shape &sh, const void *x) {
     return sh.W % 8 == 0 && ((uintptr_t)x % 16) == 0 && sh.p <= 8;
 }
 
+size_t smem_bytes_for(int kpad, int64_t E) {
+    return (size_t)kOcBlock * 4 + kMaxK * 2 + (size_t)kOcBlock * kpad * 2 + (size_t)E * 2;
+}
+
+// Workgroups of smallk_kernel<KS> one CU holds by registers (the occupancy
+// query with no LDS; cached per KS), and the device's CUs and LDS per CU.
+struct SmallKDevice {
+    int cus, lds_per_cu, reg_wgs;
+};
+
+SmallKDevice smallk_device(int KS) {
+    static std::atomic<int> reg_cache[9];
+    SmallKDevice d{256, 160 * 1024, 1};
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) d.cus = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && v > 0)
+            d.lds_per_cu = v;
+    }
+    int r = reg_cache[KS].load(std::memory_order_relaxed);
+    if (r <= 0) {
+        int n = 0;
+        hipError_t e = hipErrorInvalidValue;
+        switch (KS) {
+            case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<1>, 256, 0); break;
+            case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<2>, 256, 0); break;
+            case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<3>, 256, 0); break;
+            case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<4>, 256, 0); break;
+            case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<5>, 256, 0); break;
+            case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<6>, 256, 0); break;
+            case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<7>, 256, 0); break;
+            default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<8>, 256, 0); break;
+        }
+        r = (e == hipSuccess && n > 0) ? n : 1;
+        reg_cache[KS].store(r, std::memory_order_relaxed);
+    }
+    d.reg_wgs = r;
+    return d;
+}
+
+// Row tiles: the workgroups of a round run at once, each copying its patch
+// (about one output row's worth of time, measured on the stem) and then
+// storing its rows, so a launch takes about rounds x (rows per tile + 1)
+// row-times.  Among the even splits of a plane whose patch fits the LDS
+// budget, take the cheapest (ties: fewer rounds, then more tiles).  A round
+// holds CUs x min(register-limited, LDS-limited) workgroups.
 SmallKPlan make_smallk_plan(const Shape &sh, bool vec) {
     SmallKPlan pl{};
     pl.kg = (int)sh.kgemm();
     pl.kpad = (pl.kg + 15) / 16 * 16;
     pl.vec = vec ? 1 : 0;
-    int TR = kTargetPx / sh.Wo;
-    if (TR < 1) TR = 1;
-    if (TR > sh.Ho) TR = sh.Ho;
-    while (TR > 1 && patch_elems(sh, TR, vec) > kPatchElems) --TR;
-    // even out the row tiles of a plane
+    const SmallKDevice dv = smallk_device(pl.kpad / 16);
+    const int64_t planes = (int64_t)sh.N * sh.Do * ((sh.Co + kOcBlock - 1) / kOcBlock);
+    int TR = 0;
+    int64_t best = -1, best_rounds = 0;
+    for (int TRc = sh.Ho; TRc >= 1; --TRc) {
+        const int tiles = (sh.Ho + TRc - 1) / TRc;
+        if ((sh.Ho + tiles - 1) / tiles != TRc) continue;           // an even split of the plane only
+        const int64_t E = patch_elems(sh, TRc, vec);
+        if (E > kPatchElems) continue;
+        int64_t per_cu = dv.lds_per_cu / (int64_t)smem_bytes_for(pl.kpad, E);
+        if (per_cu > dv.reg_wgs) per_cu = dv.reg_wgs;
+        if (per_cu < 1) per_cu = 1;
+        const int64_t slots = per_cu * dv.cus;
+        const int64_t rounds = (planes * tiles + slots - 1) / slots;
+        const int64_t cost = rounds * (TRc + 1);
+        if (best < 0 || cost < best || (cost == best && rounds <= best_rounds)) {
+            best = cost;
+            best_rounds = rounds;
+            TR = TRc;
+        }
+    }
+    if (TR == 0) TR = 1;                                              // patch_elems(TR = 1) fits (smallk_supported)
     const int tiles = (sh.Ho + TR - 1) / TR;
-    TR = (sh.Ho + tiles - 1) / tiles;
     pl.TR = TR;
     pl.Rt = (TR - 1) * sh.s + sh.K;
     patch_geom(sh, vec, pl.X0, pl.Wt);
@@ -264,9 +328,7 @@ SmallKPlan make_smallk_plan(const Shape &sh, bool vec) {
     return pl;
 }
 
-size_t smem_bytes(const SmallKPlan &pl) {
-    return (size_t)kOcBlock * 4 + kMaxK * 2 + (size_t)kOcBlock * pl.kpad * 2 + (size_t)pl.E * 2;
-}
+size_t smem_bytes(const SmallKPlan &pl) { return smem_bytes_for(pl.kpad, pl.E); }
 
 }  // namespace
 
