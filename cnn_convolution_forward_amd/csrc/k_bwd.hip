@@ -298,6 +298,92 @@ void wgrad_dw_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *_
     }
 }
 
+// The same for 3x3, stride 1, pad = dilation DL (1 or 2), W % 8 == 0, with
+// 16-byte loads: a thread task is (image, output row, 8-column group); it
+// reads the 8 dout values with one load and, per kernel row, the 8-pixel
+// unit under them and the units on either side (3 loads: the DL halo
+// columns of either side fall in the neighbours; units and rows outside the
+// image read zeros), then does the 72 FMAs of 9 taps x 8 positions.  One
+// resource spans all of x (and of dout), below 2 GiB, so lanes of one wave
+// may sit in different images.  The 9 tap sums of the 256 threads meet in
+// one fixed tree in LDS.
+template <int DL>
+__global__ __launch_bounds__(256)
+void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
+                      float *__restrict__ part, int imgs_per_split) {
+    __shared__ float red[9][256];
+    const int oc = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+    const int M = sh.Co / sh.C, ic = oc / M;
+    const int H = sh.H, W = sh.W, G8 = W / 8;
+    const uint32_t HW = (uint32_t)H * (uint32_t)W;
+    const int n0 = split * imgs_per_split;
+    const int n1 = n0 + imgs_per_split < sh.N ? n0 + imgs_per_split : sh.N;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)sh.N * sh.C * HW * 2));
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout, (uint32_t)((int64_t)sh.N * sh.Co * HW * 2));
+    float acc[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) acc[t] = 0.f;
+    const int per_img = H * G8;
+    const int tasks = (n1 - n0) * per_img;
+    for (int task = tid; task < tasks; task += 256) {
+        const int nn = task / per_img, r = task - nn * per_img;
+        const int oh = r / G8, cg = r - oh * G8;
+        const uint32_t n = (uint32_t)(n0 + nn);
+        const uint4 dv = bload16(dr, ((n * sh.Co + oc) * HW + (uint32_t)oh * W + 8 * cg) * 2, 0);
+        const uint32_t xb = (n * sh.C + ic) * HW;
+        uint4 xv[3][3];
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int ih = oh + (kh - 1) * DL;
+            const bool rin = 0 <= ih && ih < H;
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int cu = cg - 1 + u;
+                const bool in = rin && 0 <= cu && cu < G8;
+                xv[kh][u] = bload16(xr, in ? (xb + (uint32_t)ih * W + 8 * cu) * 2 : kOob, 0);
+            }
+        }
+        float d[8];
+        {
+            const uint32_t w4[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d[2 * j] = __uint_as_float(w4[j] << 16);
+                d[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            float xs[24];
+            const uint32_t w12[12] = {xv[kh][0].x, xv[kh][0].y, xv[kh][0].z, xv[kh][0].w,
+                                      xv[kh][1].x, xv[kh][1].y, xv[kh][1].z, xv[kh][1].w,
+                                      xv[kh][2].x, xv[kh][2].y, xv[kh][2].z, xv[kh][2].w};
+#pragma unroll
+            for (int j = 0; j < 12; ++j) {
+                xs[2 * j] = __uint_as_float(w12[j] << 16);
+                xs[2 * j + 1] = __uint_as_float(w12[j] & 0xffff0000u);
+            }
+            // tap (kh, kw) at output column 8cg + j reads input column 8cg + j + (kw - 1) DL,
+            // element 8 + j + (kw - 1) DL of the three units
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[kh * 3 + kw] = __builtin_fmaf(d[j], xs[8 + j + (kw - 1) * DL], acc[kh * 3 + kw]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 9; ++t) red[t][tid] = acc[t];
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) {
+#pragma unroll
+            for (int t = 0; t < 9; ++t) red[t][tid] += red[t][tid + h];
+        }
+        __syncthreads();
+    }
+    if (tid < 9) part[((int64_t)split * sh.Co + oc) * 9 + tid] = red[tid][0];
+}
+
 constexpr int kDwMaxTaps = 49;   // K <= 7
 
 bool wgrad_dw_ok(const Shape &sh) {
@@ -710,7 +796,16 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     if (wgrad_dw_ok(sh)) {
         const int per = (sh.N + splits - 1) / splits;
         const int used = (sh.N + per - 1) / per;          // ranges that hold images
-        if (sh.K == 3)
+        const bool dw3 = sh.K == 3 && sh.s == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil && sh.W % 8 == 0 &&
+                         (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0 &&
+                         sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
+        if (dw3 && sh.dil == 1)
+            hipLaunchKernelGGL((wgrad_dw3_kernel<1>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
+                               dout, part, per);
+        else if (dw3)
+            hipLaunchKernelGGL((wgrad_dw3_kernel<2>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
+                               dout, part, per);
+        else if (sh.K == 3)
             hipLaunchKernelGGL((wgrad_dw_kernel<3>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
                                dout, part, used, per);
         else

@@ -72,6 +72,10 @@ SMALL = [
     (2, 4, 256, (16, 16), 512, 1, 1, 0, 1, 1),    # two 128-column tiles, four channel tiles
     (2, 2, 64, (4, 8), 128, 1, 1, 0, 1, 4),       # groups of 16 input channels
     (3, 2, 32, (2, 4, 8), 48, 1, 1, 0, 1, 1),     # 3D pointwise
+    # depthwise 3x3, stride 1, pad = dilation, W % 8 == 0: dW from 16-byte loads of 8-column groups
+    (2, 3, 16, (10, 16), 16, 3, 1, 1, 1, 16),     # two column groups a row
+    (2, 2, 24, (9, 24), 48, 3, 1, 2, 2, 24),      # dilation 2, channel multiplier 2
+    (2, 1, 8, (7, 8), 8, 3, 1, 1, 1, 8),          # one column group: both neighbours outside the image
 ]
 
 
@@ -95,12 +99,13 @@ def test_backward_integer_exact(case):
     compare(db, rdb, None, 0, exact=True, label="db %s" % (case,))
 
 
-@pytest.mark.parametrize("name", ["conv3x3_bf16", "dilated3x3_bf16", "conv1x1_bf16"])
+@pytest.mark.parametrize("name", ["conv3x3_bf16", "dilated3x3_bf16", "conv1x1_bf16", "depthwise3x3_bf16"])
 @pytest.mark.parametrize("integer", [False, True])
 def test_backward_full_3x3_layer_sampled(name, integer):
-    """x (64,128,56,56), w (128,128,3,3), s1 p1 (and dilation 2, p2), and the
-    pointwise layer x (32,256,28,28), w (1024,256,1,1): every db entry, 256 dw
-    entries (each a sum over all N * H * W positions) and 4000 dx entries."""
+    """x (64,128,56,56), w (128,128,3,3), s1 p1 (and dilation 2, p2), the
+    pointwise layer x (32,256,28,28), w (1024,256,1,1), and the depthwise layer
+    x (64,128,56,56), w (128,1,3,3): every db entry, 256 dw entries (each a sum
+    over all N * H * W positions; all of them when fewer) and 4000 dx entries."""
     wl = synth.ALL_WORKLOADS[name]
     t = synth.make_inputs(wl, integer=integer)
     rng = np.random.default_rng(99)
@@ -109,7 +114,7 @@ def test_backward_full_3x3_layer_sampled(name, integer):
     else:
         dout = synth.f32_to_bf16_bits(rng.standard_normal(size=wl.y_shape, dtype=np.float32))
     dx, dw, db = _gpu(wl, t.x, t.w, dout)
-    iw = rng.choice(dw.size, size=256, replace=False)
+    iw = rng.choice(dw.size, size=min(256, dw.size), replace=False)
     ix = rng.choice(dx.size, size=4000, replace=False)
     (pdw, pSdw), (pdx, pSdx) = oracle.conv_backward_points(t.x, t.w, dout, wl.stride, wl.pad, wl.dilation,
                                                            wl.groups, iw, ix)
