@@ -449,7 +449,13 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
                 if (s + 2 < S) load_x(s + 2);
             }
         };
+        // raised priority over the MFMA columns: while this wave is between
+        // stages (loads, transposes, the barrier) the CU's other workgroup
+        // issues, and while both multiply the arbiter favours MFMA issue
+        // (1.8% faster on the 3x3 layer than without)
+        __builtin_amdgcn_s_setprio(1);
         cg_col<D, DL, 0>(acc, A, B0, T1, T2, ib, tb, ub, mid);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();            // this stage's buffers free, the next stage's visible
     }
 
@@ -593,7 +599,9 @@ void conv3x3cg_gp_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
         B0[0] = *reinterpret_cast<const uint4 *>(ib);
         T1[0] = *reinterpret_cast<const uint4 *>(tb);
         T2[0] = *reinterpret_cast<const uint4 *>(ub);
+        __builtin_amdgcn_s_setprio(1);
         cg_col<D, 1, 0>(acc, A, B0, T1, T2, ib, tb, ub, []() {});
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();            // buffers free for the next stage
     }
 
