@@ -299,11 +299,12 @@ void wgrad_dw_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *_
 }
 
 // The same for 3x3, stride 1, pad = dilation DL (1 or 2), W % 8 == 0, with
-// 16-byte loads: a thread task is (image, output row, 8-column group); it
-// reads the 8 dout values with one load and, per kernel row, the 8-pixel
-// unit under them and the units on either side (3 loads: the DL halo
-// columns of either side fall in the neighbours; units and rows outside the
-// image read zeros), then does the 72 FMAs of 9 taps x 8 positions.  One
+// 16-byte loads: a thread task is (image, 8-column group, 4 output rows DL
+// apart); per output row it reads the 8 dout values with one load and the
+// 8-pixel units of one new input row (the unit under them and its two
+// neighbours: the DL halo columns fall there; units and rows outside the
+// image read zeros), the other two input rows staying in registers from the
+// rows before, then does the 72 FMAs of 9 taps x 8 positions.  One
 // resource spans all of x (and of dout), below 2 GiB, so lanes of one wave
 // may sit in different images.  The 9 tap sums of the 256 threads meet in
 // one fixed tree in LDS.
@@ -323,52 +324,76 @@ void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *
     float acc[9];
 #pragma unroll
     for (int t = 0; t < 9; ++t) acc[t] = 0.f;
-    const int per_img = H * G8;
+    // task = (image, column group, band of kRB output rows DL apart): rows
+    // oh0 + DL*i, i < kRB, with oh0 = band*DL*kRB + phase.  The three input
+    // rows under output row oh are oh - DL, oh, oh + DL, so the window slides
+    // by one row per output row: kRB + 2 rows of 3 units a task.
+    constexpr int kRB = 4;
+    const int bands = (H + DL * kRB - 1) / (DL * kRB);
+    const int per_img = G8 * bands * DL;
     const int tasks = (n1 - n0) * per_img;
+    auto load_row = [&](uint32_t xb, int ih, int cg, uint4 (&u3)[3]) {
+        const bool rin = 0 <= ih && ih < H;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int cu = cg - 1 + u;
+            const bool in = rin && 0 <= cu && cu < G8;
+            u3[u] = bload16(xr, in ? (xb + (uint32_t)ih * W + 8 * cu) * 2 : kOob, 0);
+        }
+    };
+    auto unpack24 = [](const uint4 (&u3)[3], float (&xs)[24]) {
+        const uint32_t w12[12] = {u3[0].x, u3[0].y, u3[0].z, u3[0].w, u3[1].x, u3[1].y,
+                                  u3[1].z, u3[1].w, u3[2].x, u3[2].y, u3[2].z, u3[2].w};
+#pragma unroll
+        for (int j = 0; j < 12; ++j) {
+            xs[2 * j] = __uint_as_float(w12[j] << 16);
+            xs[2 * j + 1] = __uint_as_float(w12[j] & 0xffff0000u);
+        }
+    };
     for (int task = tid; task < tasks; task += 256) {
-        const int nn = task / per_img, r = task - nn * per_img;
-        const int oh = r / G8, cg = r - oh * G8;
+        const int nn = task / per_img;
+        int r = task - nn * per_img;
+        const int cg = r % G8;
+        r /= G8;
+        const int phase = r % DL, band = r / DL;
+        const int oh0 = band * DL * kRB + phase;
         const uint32_t n = (uint32_t)(n0 + nn);
-        const uint4 dv = bload16(dr, ((n * sh.Co + oc) * HW + (uint32_t)oh * W + 8 * cg) * 2, 0);
         const uint32_t xb = (n * sh.C + ic) * HW;
-        uint4 xv[3][3];
+        const uint32_t db = (n * sh.Co + oc) * HW + 8 * cg;
+        uint4 wa[3], wb[3], wc[3];
+        load_row(xb, oh0 - DL, cg, wa);
+        load_row(xb, oh0, cg, wb);
 #pragma unroll
-        for (int kh = 0; kh < 3; ++kh) {
-            const int ih = oh + (kh - 1) * DL;
-            const bool rin = 0 <= ih && ih < H;
+        for (int i = 0; i < kRB; ++i) {
+            const int oh = oh0 + DL * i;
+            load_row(xb, oh + DL, cg, wc);
+            const uint4 dv = bload16(dr, oh < H ? (db + (uint32_t)oh * W) * 2 : kOob, 0);
+            float d[8];
+            {
+                const uint32_t w4[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int cu = cg - 1 + u;
-                const bool in = rin && 0 <= cu && cu < G8;
-                xv[kh][u] = bload16(xr, in ? (xb + (uint32_t)ih * W + 8 * cu) * 2 : kOob, 0);
-            }
-        }
-        float d[8];
-        {
-            const uint32_t w4[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d[2 * j] = __uint_as_float(w4[j] << 16);
-                d[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
-            }
-        }
-#pragma unroll
-        for (int kh = 0; kh < 3; ++kh) {
-            float xs[24];
-            const uint32_t w12[12] = {xv[kh][0].x, xv[kh][0].y, xv[kh][0].z, xv[kh][0].w,
-                                      xv[kh][1].x, xv[kh][1].y, xv[kh][1].z, xv[kh][1].w,
-                                      xv[kh][2].x, xv[kh][2].y, xv[kh][2].z, xv[kh][2].w};
-#pragma unroll
-            for (int j = 0; j < 12; ++j) {
-                xs[2 * j] = __uint_as_float(w12[j] << 16);
-                xs[2 * j + 1] = __uint_as_float(w12[j] & 0xffff0000u);
+                for (int j = 0; j < 4; ++j) {
+                    d[2 * j] = __uint_as_float(w4[j] << 16);
+                    d[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+                }
             }
             // tap (kh, kw) at output column 8cg + j reads input column 8cg + j + (kw - 1) DL,
-            // element 8 + j + (kw - 1) DL of the three units
+            // element 8 + j + (kw - 1) DL of the three units of input row oh + (kh - 1) DL
 #pragma unroll
-            for (int kw = 0; kw < 3; ++kw)
+            for (int kh = 0; kh < 3; ++kh) {
+                float xs[24];
+                unpack24(kh == 0 ? wa : kh == 1 ? wb : wc, xs);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[kh * 3 + kw] = __builtin_fmaf(d[j], xs[8 + j + (kw - 1) * DL], acc[kh * 3 + kw]);
+                for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[kh * 3 + kw] = __builtin_fmaf(d[j], xs[8 + j + (kw - 1) * DL], acc[kh * 3 + kw]);
+            }
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                wa[u] = wb[u];
+                wb[u] = wc[u];
+            }
         }
     }
 #pragma unroll
