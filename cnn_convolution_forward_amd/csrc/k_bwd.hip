@@ -311,8 +311,10 @@ void wgrad_dw_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *_
 template <int DL>
 __global__ __launch_bounds__(256)
 void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
-                      float *__restrict__ part, int imgs_per_split) {
-    __shared__ float red[9][256];
+                      float *__restrict__ part, float *__restrict__ part_b, int imgs_per_split) {
+    // part_b (may be null): the bias gradient's partial sums [split][oc],
+    // from the same dout loads
+    __shared__ float red[10][256];
     const int oc = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
     const int M = sh.Co / sh.C, ic = oc / M;
     const int H = sh.H, W = sh.W, G8 = W / 8;
@@ -321,9 +323,9 @@ void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *
     const int n1 = n0 + imgs_per_split < sh.N ? n0 + imgs_per_split : sh.N;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)sh.N * sh.C * HW * 2));
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout, (uint32_t)((int64_t)sh.N * sh.Co * HW * 2));
-    float acc[9];
+    float acc[10];                     // 9 taps, then the bias
 #pragma unroll
-    for (int t = 0; t < 9; ++t) acc[t] = 0.f;
+    for (int t = 0; t < 10; ++t) acc[t] = 0.f;
     // task = (image, column group, band of kRB output rows DL apart): rows
     // oh0 + DL*i, i < kRB, with oh0 = band*DL*kRB + phase.  The three input
     // rows under output row oh are oh - DL, oh, oh + DL, so the window slides
@@ -377,6 +379,8 @@ void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *
                     d[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
                 }
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[9] += d[j];
             // tap (kh, kw) at output column 8cg + j reads input column 8cg + j + (kw - 1) DL,
             // element 8 + j + (kw - 1) DL of the three units of input row oh + (kh - 1) DL
 #pragma unroll
@@ -397,16 +401,17 @@ void wgrad_dw3_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *
         }
     }
 #pragma unroll
-    for (int t = 0; t < 9; ++t) red[t][tid] = acc[t];
+    for (int t = 0; t < 10; ++t) red[t][tid] = acc[t];
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
         if (tid < h) {
 #pragma unroll
-            for (int t = 0; t < 9; ++t) red[t][tid] += red[t][tid + h];
+            for (int t = 0; t < 10; ++t) red[t][tid] += red[t][tid + h];
         }
         __syncthreads();
     }
     if (tid < 9) part[((int64_t)split * sh.Co + oc) * 9 + tid] = red[tid][0];
+    if (tid == 9 && part_b) part_b[(int64_t)split * sh.Co + oc] = red[9][0];
 }
 
 constexpr int kDwMaxTaps = 49;   // K <= 7
@@ -769,8 +774,10 @@ int wgrad_splits(const Shape &sh, bool aligned) {
 int64_t wgrad_workspace_floats(const Shape &sh) {
     // the 3x3 kernel runs only on 16-byte aligned x and dout; size the
     // workspace for whichever route the pointers select
-    const int64_t a = (int64_t)wgrad_splits(sh, true) * sh.w_elems();
-    const int64_t b = (int64_t)wgrad_splits(sh, false) * sh.w_elems();
+    // (depthwise layers: room for the bias partials after the weight ones)
+    const int64_t per = sh.w_elems() + (wgrad_dw_ok(sh) ? sh.Co : 0);
+    const int64_t a = (int64_t)wgrad_splits(sh, true) * per;
+    const int64_t b = (int64_t)wgrad_splits(sh, false) * per;
     return a > b ? a : b;
 }
 
@@ -782,7 +789,12 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     // (the weight partials overwrite them afterwards, in stream order).  Folding
     // it into the 3x3 weight kernel measured slower (its channel-tile-0
     // workgroups, which set the makespan, took the extra LDS reads).
-    if (db) {
+    // depthwise 3x3, stride 1, pad = dilation, W % 8 == 0: the weight kernel
+    // also sums the bias gradient
+    const bool dw3 = wgrad_dw_ok(sh) && sh.K == 3 && sh.s == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil &&
+                     sh.W % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0 &&
+                     sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
+    if (db && !dw3) {
         const hipError_t e = launch_bias_grad_bf16(sh, dout, part, db, st);
         if (e != hipSuccess) return e;
     }
@@ -821,15 +833,13 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     if (wgrad_dw_ok(sh)) {
         const int per = (sh.N + splits - 1) / splits;
         const int used = (sh.N + per - 1) / per;          // ranges that hold images
-        const bool dw3 = sh.K == 3 && sh.s == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil && sh.W % 8 == 0 &&
-                         (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0 &&
-                         sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
+        float *part_b = part + (int64_t)used * sh.w_elems();      // bias partials after the weight ones
         if (dw3 && sh.dil == 1)
             hipLaunchKernelGGL((wgrad_dw3_kernel<1>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
-                               dout, part, per);
+                               dout, part, db ? part_b : nullptr, per);
         else if (dw3)
             hipLaunchKernelGGL((wgrad_dw3_kernel<2>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
-                               dout, part, per);
+                               dout, part, db ? part_b : nullptr, per);
         else if (sh.K == 3)
             hipLaunchKernelGGL((wgrad_dw_kernel<3>), dim3((unsigned)sh.Co, (unsigned)used), dim3(256), 0, st, sh, x,
                                dout, part, used, per);
@@ -841,6 +851,7 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
         const int64_t n = sh.w_elems();
         const hipError_t e2 = launch_sum_splits(part, dw, n, used, st);
         if (e2 != hipSuccess) return e2;
+        if (dw3 && db) return launch_sum_splits(part_b, db, (int64_t)sh.Co, used, st);
         return hipGetLastError();
     }
     const int64_t chunk = ((P + splits - 1) / splits + kBK - 1) / kBK * kBK;

@@ -354,8 +354,8 @@ CONV_API size_t conv_bwd_data_workspace_bytes(const conv_params_t *params);
 CONV_API conv_status_t conv_bwd_data_bf16(const conv_params_t *params, const uint16_t *dout, const uint16_t *w,
                                           float *dx, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device workspace for conv_bwd_weight_bf16: fp32 partial sums of dw over
- * ranges of output positions; 0 on invalid parameters. */
+/* Device workspace for conv_bwd_weight_bf16: fp32 partial sums of dw (and
+ * of db) over ranges of output positions; 0 on invalid parameters. */
 CONV_API size_t conv_bwd_weight_workspace_bytes(const conv_params_t *params);
 
 /* dw (C_out, C_in/G, K, K[, K]) and, when db is not NULL, db (C_out) from x
