@@ -40,9 +40,10 @@
 // Accumulator orientation D[px][oc]: lane l owns channel l % 32, and its 16
 // slots are pixels (rows 4*(l/32) .. +3) x (4 column groups); across its J
 // fragments a lane holds J consecutive columns of each (row, group).  The
-// epilogue stages 16 channels at a time in LDS as [channel][row][column] and
-// stores them back in 16-byte chunks as whole 8-row blocks of each channel,
-// contiguous in y (bias is the accumulators' initial value).
+// epilogue stages 32 channels at a time in LDS as [channel][row][column] and
+// stores each channel's 8 rows (contiguous in y) in 8-byte pieces,
+// consecutive lanes on consecutive pieces (bias is the accumulators' initial
+// value).
 //
 // Dilation d (1 or 2, with pad d): a tile's 8 output rows are r0 + d*i, one
 // row phase of a band of 8d rows, so kernel row kh of tile row i is again LDS
