@@ -54,10 +54,13 @@ void flip_weights_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ 
 // BVEC: a pointwise layer (K = 1, stride 1, pad 0, plane % 8 == 0, 16-byte
 // aligned x): X_col^T is x itself, so B loads like A -- 16 bytes of 8
 // consecutive positions, four lanes on one column's 32 positions.
+// part_b (may be null): the bias gradient's partial sums [split][oc], added up
+// by the column-tile-0 workgroups from the dout tiles already in LDS.
 template <int BM, int BVEC>
 __global__ __launch_bounds__(256)
 void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__restrict__ dout,
-                  float *__restrict__ part, int64_t P, int Kg, int64_t chunk, int splits, int g0, int a_vec) {
+                  float *__restrict__ part, float *__restrict__ part_b, int64_t P, int Kg, int64_t chunk, int splits,
+                  int g0, int a_vec) {
     constexpr int MI = BM / 64;
     __shared__ __align__(16) uint16_t As[2][BM][kLdk];
     __shared__ __align__(16) uint16_t Bs[2][kBN][kLdk];
@@ -184,6 +187,12 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int nk = k_end > k_begin ? (int)((k_end - k_begin + kBK - 1) / kBK) : 0;
+    // bias: thread tid adds row tid / TPR of each dout tile, positions
+    // (tid % TPR) * EPT .. +EPT-1 (positions past the range and rows past
+    // C_out/G are zeros in the tile)
+    constexpr int TPR = 256 / BM, EPT = kBK / TPR;
+    const bool do_b = part_b != nullptr && blockIdx.x == 0;
+    float bsum = 0.f;
     if (nk > 0) {
         load_stage(k_begin);
         store_stage(0);
@@ -192,6 +201,16 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_stage(k_begin + (int64_t)(kt + 1) * kBK);
+        if (do_b) {
+#pragma unroll
+            for (int v = 0; v < EPT / 8; ++v) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(&As[buf][tid / TPR][(tid % TPR) * EPT + 8 * v]);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bsum += __uint_as_float(w4[j] << 16) + __uint_as_float(w4[j] & 0xffff0000u);
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             uint4 a[MI], b[2];
@@ -211,6 +230,19 @@ void wgrad_kernel(Shape sh, const uint16_t *__restrict__ x, const uint16_t *__re
         __syncthreads();
     }
 
+    if (do_b) {
+        // the TPR partial sums of a row meet in LDS (the stage buffers are free)
+        float *red = reinterpret_cast<float *>(&As[0][0][0]);
+        red[tid] = bsum;
+        __syncthreads();
+        if (tid % TPR == 0) {
+            float r = 0.f;
+#pragma unroll
+            for (int k = 0; k < TPR; ++k) r += red[tid + k];
+            const int ocl = m0 + tid / TPR;
+            if (ocl < Cog) part_b[(int64_t)split * sh.Co + grp * Cog + ocl] = r;
+        }
+    }
     // partial[split][oc][jcol]: 32 lanes on 32 consecutive columns
     float *pp = part + (int64_t)split * sh.Co * Kg;
 #pragma unroll
@@ -774,8 +806,8 @@ int wgrad_splits(const Shape &sh, bool aligned) {
 int64_t wgrad_workspace_floats(const Shape &sh) {
     // the 3x3 kernel runs only on 16-byte aligned x and dout; size the
     // workspace for whichever route the pointers select
-    // (depthwise layers: room for the bias partials after the weight ones)
-    const int64_t per = sh.w_elems() + (wgrad_dw_ok(sh) ? sh.Co : 0);
+    // (and room for the bias partials after the weight ones)
+    const int64_t per = sh.w_elems() + sh.Co;
     const int64_t a = (int64_t)wgrad_splits(sh, true) * per;
     const int64_t b = (int64_t)wgrad_splits(sh, false) * per;
     return a > b ? a : b;
@@ -794,7 +826,11 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     const bool dw3 = wgrad_dw_ok(sh) && sh.K == 3 && sh.s == 1 && (sh.dil == 1 || sh.dil == 2) && sh.p == sh.dil &&
                      sh.W % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0 &&
                      sh.x_elems() * 2 < (INT64_C(1) << 31) && sh.y_elems() * 2 < (INT64_C(1) << 31);
-    if (db && !dw3) {
+    // the general weight kernel (neither the 3x3 nor the depthwise one) also
+    // sums the bias gradient from its dout tiles
+    const bool aligned0 = (uintptr_t)x % 16 == 0 && (uintptr_t)dout % 16 == 0;
+    const bool general = !(aligned0 && wgrad3x3_ok(sh)) && !wgrad_dw_ok(sh);
+    if (db && !dw3 && !general) {
         const hipError_t e = launch_bias_grad_bf16(sh, dout, part, db, st);
         if (e != hipSuccess) return e;
     }
@@ -860,12 +896,13 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
     const bool b_vec = a_vec && sh.K == 1 && sh.Kd == 1 && sh.s == 1 && sh.sd == 1 && sh.p == 0 && sh.pd == 0 &&
                        ((uintptr_t)x % 16 == 0);
     const unsigned gx = (unsigned)((Kg + kBN - 1) / kBN);
+    float *part_b = db ? part + (int64_t)splits * sh.w_elems() : nullptr;   // bias partials after the weight ones
     const int gmax = 65535 / splits;                    // groups per launch (grid z = splits * groups)
     for (int g0 = 0; g0 < sh.G; g0 += gmax) {
         const int ng = sh.G - g0 < gmax ? sh.G - g0 : gmax;
 #define WGRAD_GO(BMV, BV)                                                                                    \
     hipLaunchKernelGGL((wgrad_kernel<BMV, BV>), dim3(gx, (unsigned)((Cog + BMV - 1) / BMV), (unsigned)(splits * ng)), \
-                       dim3(256), 0, st, sh, x, dout, part, P, Kg, chunk, splits, g0, a_vec)
+                       dim3(256), 0, st, sh, x, dout, part, part_b, P, Kg, chunk, splits, g0, a_vec)
         if (Cog > 64) {
             if (b_vec) WGRAD_GO(128, 1); else WGRAD_GO(128, 0);
         } else {
@@ -876,7 +913,9 @@ hipError_t launch_wgrad_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
         if (e != hipSuccess) return e;
     }
     const int64_t n = sh.w_elems();
-    return launch_sum_splits(part, dw, n, splits, st);
+    const hipError_t e3 = launch_sum_splits(part, dw, n, splits, st);
+    if (e3 != hipSuccess || !db) return e3;
+    return launch_sum_splits(part_b, db, (int64_t)sh.Co, splits, st);
 }
 
 int bias_grad_ranges(const Shape &sh) {
