@@ -219,7 +219,8 @@ def test_general_xcol_bytes_and_explicit_validation():
 def test_backward_validation():
     prm = _gp()                       # (2,8,9,11), (16,2,3,3), s1 p1 d2 G4
     nd, nw = B.conv_bwd_data_workspace_bytes(prm), B.conv_bwd_weight_workspace_bytes(prm)
-    assert nd >= 16 * 2 * 9 * 2 and nw >= 16 * 2 * 9 * 4 and nw % (16 * 2 * 9 * 4) == 0
+    # dW workspace: per range of positions, the fp32 partials of dw (C_out x C_in/G x 9) and of db (C_out)
+    assert nd >= 16 * 2 * 9 * 2 and nw >= (16 * 2 * 9 + 16) * 4 and nw % ((16 * 2 * 9 + 16) * 4) == 0
     assert B.conv_bwd_data_workspace_bytes(None) == 0 and B.conv_bwd_weight_workspace_bytes(_gp(groups=3)) == 0
     DO = X + 0x01000000
     bd = lambda prm=prm, dout=DO, w=Wp, dx=Y, ws=WS, nb=nd: B.conv_bwd_data_bf16(prm, dout, w, dx, ws, nb, None)
