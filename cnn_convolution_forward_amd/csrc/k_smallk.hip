@@ -46,7 +46,7 @@ struct SmallKPlan {
 
 // KS: reduction steps of 16 (kpad / 16), a template parameter so the weight
 // operands take exactly 8 * KS registers.
-template <int KS>
+template <int KS, bool PAIR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KS <= 4 ? 4 : KS <= 6 ? 3 : 2, 8)))
 void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                    const float *__restrict__ bias, float *__restrict__ y) {
@@ -197,6 +197,41 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
         // rows), so it splits into soffset + voffset; bias comes from LDS in
         // the loop (volatile: not held in registers across fragments).
         const int hrow = 4 * (lane >> 5);
+        if constexpr (PAIR) {
+            // bf16, W_out even (which keeps q0, npx and plane even), y 4-byte aligned: lanes 2k, 2k+1 (pixels p, p + 1,
+            // consecutive in y and both inside the tile or both past it) swap
+            // one value; each stores a pixel pair as one 4-byte word, the even
+            // lane channel c, the odd lane channel c + 1
+            const uint32_t odd = lane & 1;
+            const uint32_t pv2 =
+                p < npx ? (q0 + (uint32_t)(p & ~1) + (uint32_t)(hrow + (int)odd) * (uint32_t)plane) * 2u : kOob;
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+                    const f32x4v_t b4 = *reinterpret_cast<const volatile f32x4v_t *>(bias_s + ob * 32 + 8 * g + hrow);
+                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        const int c = ob * 32 + 8 * g + e;
+                        const uint32_t vo = c + hrow + (int)odd < nch ? pv2 : kOob;
+                        const int so = (int)((uint32_t)c * (uint32_t)plane * 2u);
+                        float va = acc[ob][4 * g + e] + bb[e], vb = acc[ob][4 * g + e + 1] + bb[e + 1];
+                        if (sh.relu) {
+                            va = fmaxf(va, 0.f);
+                            vb = fmaxf(vb, 0.f);
+                        }
+                        // quad_perm [1, 0, 3, 2]: swap with the neighbouring lane
+                        const float got = __int_as_float(
+                            __builtin_amdgcn_mov_dpp(__float_as_int(odd ? va : vb), 0xB1, 0xF, 0xF, true));
+                        const uint32_t lo = f32_to_bf16_rne(odd ? got : va);
+                        const uint32_t hi = f32_to_bf16_rne(odd ? vb : got);
+                        __builtin_amdgcn_raw_buffer_store_b32(lo | (hi << 16), yr, (int)vo, so, 0);
+                    }
+                }
+            continue;
+        }
         const uint32_t pvo = p < npx ? (q0 + (uint32_t)p + (uint32_t)hrow * (uint32_t)plane) * (uint32_t)ob_ : kOob;
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
@@ -270,14 +305,14 @@ SmallKDevice smallk_device(int KS) {
         int n = 0;
         hipError_t e = hipErrorInvalidValue;
         switch (KS) {
-            case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<1>, 256, 0); break;
-            case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<2>, 256, 0); break;
-            case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<3>, 256, 0); break;
-            case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<4>, 256, 0); break;
-            case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<5>, 256, 0); break;
-            case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<6>, 256, 0); break;
-            case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<7>, 256, 0); break;
-            default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<8>, 256, 0); break;
+            case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<1, false>, 256, 0); break;
+            case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<2, false>, 256, 0); break;
+            case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<3, false>, 256, 0); break;
+            case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<4, false>, 256, 0); break;
+            case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<5, false>, 256, 0); break;
+            case 6: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<6, false>, 256, 0); break;
+            case 7: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<7, false>, 256, 0); break;
+            default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, smallk_kernel<8, false>, 256, 0); break;
         }
         r = (e == hipSuccess && n > 0) ? n : 1;
         reg_cache[KS].store(r, std::memory_order_relaxed);
@@ -345,8 +380,14 @@ hipError_t launch_smallk_bf16(const Shape &sh, const uint16_t *x, const uint16_t
     const SmallKPlan pl = make_smallk_plan(sh, vec);
     const int64_t tiles = (int64_t)sh.N * sh.Do * pl.tiles_h;
     dim3 grid((unsigned)tiles, (unsigned)((sh.Co + kOcBlock - 1) / kOcBlock));
-#define SMALLK_LAUNCH(KSV) \
-    hipLaunchKernelGGL((smallk_kernel<KSV>), grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y)
+    // bf16 output stored as pixel pairs (a separate instantiation, so the
+    // fp32 kernels carry none of it)
+    const bool pair = sh.out_bf16 && sh.Wo % 2 == 0 && ((uintptr_t)y & 3) == 0;
+#define SMALLK_LAUNCH(KSV)                                                                                          \
+    if (pair)                                                                                                       \
+        hipLaunchKernelGGL((smallk_kernel<KSV, true>), grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y); \
+    else                                                                                                            \
+        hipLaunchKernelGGL((smallk_kernel<KSV, false>), grid, dim3(256), smem_bytes(pl), st, sh, pl, x, w, bias, y)
     switch (pl.kpad / 16) {
         case 1: SMALLK_LAUNCH(1); break;
         case 2: SMALLK_LAUNCH(2); break;

@@ -77,7 +77,7 @@ CASES = [
     ("3x3 groups of 32 column-group", (2, 2, 128, (11, 40), 128, 3, 1, 1, 1, 4), "auto", True),
     ("pointwise", (2, 3, 64, (14, 16), 192, 1, 1, 0, 1, 1), "auto", False),
     ("depthwise", (2, 2, 24, (30, 40), 48, 3, 2, 1, 1, 24), "auto", False),
-    ("stem (direct VALU)", (2, 2, 3, (33, 35), 64, 3, 2, 1, 1, 1), "auto", False),
+    ("stem (short-reduction kernel)", (2, 2, 3, (33, 35), 64, 3, 2, 1, 1, 1), "auto", False),
     ("general MFMA, groups + dilation", (2, 2, 48, (17, 19), 96, 3, 1, 2, 2, 3), "mfma", False),
     ("general VALU", (2, 2, 6, (11, 9), 10, 3, 2, 1, 1, 2), "valu", False),
     ("3D general", (3, 1, 16, (5, 9, 10), 40, 3, 1, 1, 1, 1), "mfma", False),
