@@ -80,7 +80,25 @@ def algorithmic_bytes(wl, out_bytes=4):
     return x + w + b + y
 
 
+def xcol_bytes(wl):
+    """Bytes of the explicit route's patch matrix X_col (C_in*K^dims rows x
+    N*prod(out) columns, bf16)."""
+    rows = wl.C_in * wl.K ** wl.ndim          # every group's rows: C_in * K^dims whatever the groups
+    cols = wl.N * int(np.prod(wl.out_spatial()))
+    return rows * cols * 2
+
+
+def route_bytes(wl, route, out_bytes=4):
+    """Algorithmic bytes of one forward call on `route`: the implicit routes
+    read x, w, bias once and write y once; the explicit route also writes
+    X_col and reads it back (x + 2*X_col + w + bias + y)."""
+    ab = algorithmic_bytes(wl, out_bytes)
+    return ab + 2 * xcol_bytes(wl) if route == "explicit" else ab
+
+
 def bound_of(wl, route, out_bytes=4):
+    if route == "explicit":
+        return "hbm"                  # X_col written and read back: ~55 FLOP/byte on the 3x3 layer
     ab = algorithmic_bytes(wl, out_bytes)
     if wl.dtype == "f32" or route == "valu":
         return "alu" if wl.flops() / ab > PEAK_FP32_VALU_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
@@ -179,6 +197,7 @@ class Runner:
         algo = B.ALGO.get(self.route, 0)
         x, w, b, y = ptr(self.x), ptr(self.w), ptr(self.b), ptr(self.y)
         self._pre = None
+        self._im2col = None
         if self.options is not None:
             prm, opt = ctypes.byref(self.params), ctypes.byref(self.opts)
             if wl.dtype == "f32":
@@ -201,6 +220,12 @@ class Runner:
                 self._main = (fn, (prm, x, w, b, y, algo, st))
         elif self.route == "explicit":
             nb = self.ws.numel()
+            if wl.ndim == 2:
+                self._im2col = (L.conv2d_im2col_bf16, (x, ptr(self.ws), wl.N, wl.C_in, H, W, wl.K, wl.stride,
+                                                       wl.pad, st))
+            else:
+                self._im2col = (L.conv3d_im2col_bf16, (x, ptr(self.ws), wl.N, wl.C_in, D, H, W, wl.K, wl.stride,
+                                                       wl.pad, st))
             if wl.ndim == 2:
                 self._main = (L.conv2d_fwd_bf16_explicit,
                               (x, w, b, y, ptr(self.ws), nb, wl.N, wl.C_in, H, W, wl.C_out, wl.K, wl.stride, wl.pad, st))
@@ -240,16 +265,41 @@ class Runner:
         self.pre()
         self.main()
 
+    def im2col(self):
+        """The explicit route's first kernel alone (X_col written to the workspace)."""
+        self._call(self._im2col)
+
+
+def _batched(fn, steps, batches=5):
+    """GPU time per call of `fn` run `steps` times back to back, in `batches`
+    equal runs each bracketed by one pair of HIP events on the current stream
+    (the one the library launches on): no event packet between two calls.
+    Returns (mean, median of the batch means, min of the batch means), seconds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    per = max(1, steps // batches)
+    means = []
+    for _ in range(batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        means.append(a.elapsed_time(b) * 1e-3 / per)
+    return float(np.mean(means)), float(np.median(means)), float(np.min(means))
+
 
 def time_steps(runner, steps, warmup):
-    """Two passes over the same device-resident inputs, after `warmup` steps:
+    """After `warmup` untimed steps:
 
     A. exactly `steps` steps back to back, bracketed by synchronize (the wall
        clock, for `value`) and by one pair of HIP events (GPU time);
-    B. another `steps` steps with a pair of HIP events around each
-       convolution launch, recorded on the stream the library launches on
-       (per-launch durations, for the roofline).  Event packets between
-       launches cost a few microseconds each, so they stay out of pass A.
+    then, for the roofline, the measured launch alone (`runner.main`, e.g. the
+    convolution with weights already packed) `steps` times back to back, and
+    the step's other work (`runner.pre`, the weight repack) alone likewise,
+    each in batches bracketed by one event pair (no events between launches,
+    so the launch time cannot exceed the step's).
     """
     import torch
     for _ in range(warmup):
@@ -265,19 +315,10 @@ def time_steps(runner, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu = g0.elapsed_time(g1) * 1e-3
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        evp[i][0].record(stream)
-        runner.pre()
-        evp[i][1].record(stream)
-        ev[i][0].record(stream)
-        runner.main()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    runner.pre_per = np.array([a.elapsed_time(b) for a, b in evp]) * 1e-3
-    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3     # seconds
-    return wall, gpu, per
+    main = _batched(runner.main, steps)
+    pre = _batched(runner.pre, steps) if runner._pre is not None else (0.0, 0.0, 0.0)
+    runner.pre_per = pre
+    return wall, gpu, main
 
 
 def time_cold(runner, steps, flush_bytes=512 << 20):
@@ -318,7 +359,12 @@ def kernel_sources_sha(files):
     return h.hexdigest()
 
 
-def traffic_from_profiles(workload, route):
+def counters_from_profiles(workload, route):
+    """The committed counter summary for (workload, route), while the kernel
+    sources still hash to the value recorded with it: a dict with
+    hbm_bytes_per_dispatch and, where recorded, mfma_busy (SQ_VALU_MFMA_BUSY_CYCLES
+    over the SIMD cycles of the dispatch) and sclk_mhz (GRBM_GUI_ACTIVE cycles
+    over the dispatch duration)."""
     import glob
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.json"))):
         with open(f) as fh:
@@ -327,8 +373,43 @@ def traffic_from_profiles(workload, route):
             continue
         if kernel_sources_sha(c["sources"]) != c["sources_sha256"]:
             return None, "counters in %s predate the current kernel sources" % os.path.basename(f)
-        return c["hbm_bytes_per_dispatch"], os.path.basename(f)
+        return c, os.path.basename(f)
     return None, "no counter summary for this workload"
+
+
+def roofline_entry(wl, route, kernel_s, out_bytes=4, counters=None):
+    """The roofline object of the dominant launch: algorithmic FLOP (MFMA or
+    ALU bound) or bytes (HBM bound) per launch over its time, against the
+    MI355X peak of that resource."""
+    bound = bound_of(wl, route, out_bytes)
+    if bound == "mfma":
+        ach, peak, unit = wl.flops() / kernel_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "alu":
+        ach, peak, unit = wl.flops() / kernel_s / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
+    else:
+        ach, peak, unit = route_bytes(wl, route, out_bytes) / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    r = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+         "traffic": None, "algorithmic": wl.flops() if bound in ("mfma", "alu") else route_bytes(wl, route, out_bytes)}
+    if counters:
+        r["traffic"] = counters.get("hbm_bytes_per_dispatch")
+        for k in ("mfma_busy", "sclk_mhz"):
+            if k in counters:
+                r[k] = counters[k]
+        if "sclk_mhz" in counters and bound == "mfma":
+            # the same fraction against the peak at the clock the counters measured
+            r["frac_at_measured_sclk"] = round(ach / (peak * counters["sclk_mhz"] / 2400.0), 4)
+    return r
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, runner, sample_images):
@@ -365,7 +446,7 @@ def cpu_baseline(wl, runner, sample_images):
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = float(np.max(np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": "%d of %d images of the same seeded inputs (one full forward pass over them), "
                       "fp64" % (n, wl.N),
             "parity_on_sample": {"max_abs_delta_over_S": rel, "tau": tau, "pass": ok}}
@@ -388,7 +469,8 @@ def cpu_baseline_backward(wl, runner, sample_images):
     ok = bool(np.all(d <= 1e-3 * Sdx))
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = float(np.max(np.where(Sdx > 0, d / np.where(Sdx > 0, Sdx, 1), 0.0)))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle", "seconds": round(dt, 3),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
+            "seconds": round(dt, 3),
             "sample": "%d of %d images of the same seeded inputs and upstream gradient (dx, dW and db over "
                       "them, the scatter loop, one thread), fp64" % (n, wl.N),
             "parity_on_sample": {"dx_max_abs_delta_over_S": rel, "tau": 1e-3, "pass": ok}}
@@ -413,7 +495,7 @@ def report_all(steps, warmup):
         routes = ["valu"] if wl.dtype == "f32" else ["auto", "mfma", "valu", "explicit"]
         for route in routes:
             _, wall, gpu, per = measure(wl, route, steps, warmup)
-            t = float(np.mean(per))
+            t = per[0]
             line = {"workload": name, "route": route, "us_per_call": round(t * 1e6, 2),
                     "us_per_step": round(wall / steps * 1e6, 2),
                     "TFLOP/s": round(wl.flops() / t / 1e12, 2),
@@ -458,27 +540,29 @@ def main():
     if args.route == "explicit" and options != ("nchw", "f32", False):
         print("the explicit route takes NCHW, fp32 output, no ReLU", file=sys.stderr)
         sys.exit(2)
-    runner, wall, gpu, per = measure(wl, args.route, args.steps, args.warmup, backward=args.backward,
-                                     options=options)
+    runner, wall, gpu, main_t = measure(wl, args.route, args.steps, args.warmup, backward=args.backward,
+                                        options=options)
     # backward: the data and the weight gradient each cost the forward's FLOP
     flops = wl.flops() * (2 if args.backward else 1)
     value = flops * args.steps / wall / 1e12
-    kern_flops = wl.flops()
     dominant = "conv_bwd_weight_bf16" if args.backward else "convolution"
-    bwd_us = {"conv_bwd_data_bf16": round(float(np.mean(runner.pre_per)) * 1e6, 3),
-              "conv_bwd_weight_bf16": round(float(np.mean(per)) * 1e6, 3)}
-    if args.backward and bwd_us["conv_bwd_data_bf16"] > bwd_us["conv_bwd_weight_bf16"]:
-        per, dominant = runner.pre_per, "conv_bwd_data_bf16"
-    kern = float(np.mean(per))
-    traffic, traffic_src = traffic_from_profiles(wl.name + ("_backward" if args.backward else ""), args.route)
+    kern_t = main_t
+    if args.backward:
+        bwd_us = {"conv_bwd_data_bf16": round(runner.pre_per[0] * 1e6, 3),
+                  "conv_bwd_weight_bf16": round(main_t[0] * 1e6, 3)}
+        if runner.pre_per[0] > main_t[0]:
+            kern_t, dominant = runner.pre_per, "conv_bwd_data_bf16"
     out_bytes = 2 if args.out == "bf16" else 4
-    bound = bound_of(wl, args.route, out_bytes)
-    if bound == "mfma":
-        ach, peak, unit = kern_flops / kern / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
-    elif bound == "alu":
-        ach, peak, unit = kern_flops / kern / 1e12, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"
-    else:
-        ach, peak, unit = algorithmic_bytes(wl, out_bytes) / kern / 1e9, PEAK_HBM_GBS, "GB/s"
+    counters, counters_src = counters_from_profiles(wl.name + ("_backward" if args.backward else ""), args.route)
+    roof = roofline_entry(wl, args.route, kern_t[0], out_bytes, counters)
+    roof.update({"traffic_source": counters_src, "kernel": dominant,
+                 "kernel_avg_us": round(kern_t[0] * 1e6, 3),
+                 "kernel_median_us": round(kern_t[1] * 1e6, 3),
+                 "timing": ("the measured launch alone (%s), %d calls back to back in 5 batches, each batch "
+                            "bracketed by one pair of HIP events on the library's stream; avg = total GPU time / "
+                            "calls, median = median batch mean" % (
+                                "conv2d_fwd_bf16_prepacked: the step's weight repack excluded"
+                                if runner._pre is not None and not args.backward else dominant, args.steps))})
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
@@ -491,15 +575,18 @@ def main():
         "config": describe(wl) | {"route": args.route, "pass": "backward" if args.backward else "forward",
                                   "layout": args.layout, "out_dtype": args.out, "relu": args.relu},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                     "frac": round(ach / peak, 4), "traffic": traffic,
-                     "traffic_source": traffic_src,
-                     "kernel": dominant,
-                     "kernel_avg_us": round(kern * 1e6, 3), "kernel_median_us": round(float(np.median(per)) * 1e6, 3),
-                     "timing": "HIP events on the library's stream around each convolution launch of a "
-                               "second pass of the same steps (the weight repack before it is in the step, "
-                               "not in this figure)"},
+        "roofline": roof,
     }
+    if runner._pre is not None and not args.backward:
+        out["repack_us"] = round(runner.pre_per[0] * 1e6, 3)
+    if args.route == "explicit" and runner._im2col is not None:
+        im_t = _batched(runner.im2col, args.steps)
+        im_bytes = int(np.prod(wl.x_shape)) * 2 + xcol_bytes(wl)
+        out["im2col"] = {"bound": "hbm", "achieved": round(im_bytes / im_t[0] / 1e9, 2), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(im_bytes / im_t[0] / 1e9 / PEAK_HBM_GBS, 4),
+                         "kernel_avg_us": round(im_t[0] * 1e6, 3), "algorithmic_bytes": im_bytes,
+                         "xcol_over_x": round(xcol_bytes(wl) / (int(np.prod(wl.x_shape)) * 2), 3),
+                         "note": "the explicit route's im2col kernel alone: x read once, X_col written once"}
     if not args.no_cold:
         n_cold = min(args.steps, 50)
         c_step, c_main = time_cold(runner, n_cold)
@@ -513,9 +600,8 @@ def main():
             "note": "the same steps, each after a 512 MiB scratch buffer is read outside the events "
                     "(L2s and the memory-side cache evicted, clean); value from the median step"}
     if args.backward:
-        out["roofline"]["timing"] = ("HIP events on the library's stream around each call of a second pass of "
-                                     "the same steps; per call (us): %s; the longer call is the roofline's "
-                                     "kernel (db is inside conv_bwd_weight_bf16)" % json.dumps(bwd_us))
+        out["roofline"]["timing"] += ("; per call (us): %s; the longer call is the roofline's kernel (db is inside "
+                                      "conv_bwd_weight_bf16)" % json.dumps(bwd_us))
     if not args.no_cpu_baseline:
         if args.backward:
             out["cpu_baseline"] = cpu_baseline_backward(wl, runner, args.cpu_sample_images or 2)

@@ -68,9 +68,14 @@ typedef enum {
     CONV_ERR_HIP = 8         /* a HIP launch failed                                         */
 } conv_status_t;
 
-/* Kernel route.  AUTO picks by shape: bf16 with C_in*K^dims <= 32 (the thin
- * stem layer) -> VALU direct kernel; other bf16 -> MFMA implicit GEMM; fp32 ->
- * VALU.  MFMA is bf16-only (CONV_ERR_ALGO for fp32). */
+/* Kernel route.  AUTO picks by shape, for bf16: first the matrix cores'
+ * short-reduction kernel when C_in/groups*K^dims <= 128 and one output row's
+ * input patch fits its LDS tile (this takes the thin stem layer, 3 channels x
+ * 3x3, and the 3-channel 3D layer); else one input channel per group in 2D
+ * (depthwise) -> the VALU depthwise kernel; else a reduction of at most 32
+ * (C_in/groups*K^dims) -> the VALU direct kernel; else the MFMA implicit
+ * GEMM.  fp32 -> VALU.  MFMA is bf16-only (CONV_ERR_ALGO for fp32).
+ * CONV_ALGO_VALU forces the direct FMA route for any bf16 shape. */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_MFMA = 1,      /* implicit GEMM on bf16 matrix cores, fp32 accumulate */

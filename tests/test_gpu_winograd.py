@@ -1,18 +1,19 @@
 """GPU parity for Winograd F(2x2, 3x3) (conv_fwd_ex_bf16 with
-CONV_ALGO_WINOGRAD) against the oracle's Winograd (which equals the direct
-convolution in fp64).
+CONV_ALGO_WINOGRAD) against the oracle.
 
-Tolerance, derived from the arithmetic: the transformed filter U and input
-block V are rounded to fp16 (unit roundoff 2^-11) before the 16 products, so
-each product carries a relative error of at most 2^-10 (+2^-22), the fp32 sums
-over C_in add at most C_in * 2^-24 of the magnitude, and the output transform
-only adds and subtracts.  Per output
-    |gpu - y_ref| <= 2^-9 * Sw,
-Sw being the oracle's transform-domain magnitude sum (sum over channels and
-points of |A coeff| |U| |V|), which is about 1.7x (up to 4x) the direct
-S = sum |x w| on N(0,1) data.  On integer data every transformed value is
-exact in fp16 (multiples of 1/4 up to 4.5 and integers up to 8) and every sum
-exact in fp32, so the result must equal the direct convolution bit for bit.
+Acceptance is the same as every bf16 route: per output element
+    |gpu - y_ref| <= 1e-3 * S,   S = sum |x w| of the direct convolution,
+with y_ref and S from the direct fp64 oracle.  The bound the arithmetic
+guarantees is looser: U and V are rounded to fp16 (unit roundoff 2^-11)
+before the 16 products, so each product carries a relative error of at most
+2^-10 (+2^-22), the fp32 sums over C_in add at most C_in * 2^-24 of the
+magnitude and the output transform only adds and subtracts, which gives
+|gpu - y_ref| <= 2^-9 * Sw with Sw the oracle's transform-domain magnitude sum
+(about 1.7x, at most 4x, the direct S on N(0,1) data).  The tests assert the
+contract bound and print the measured error against both.  On integer data
+every transformed value is exact in fp16 (multiples of 1/4 up to 4.5 and
+integers up to 8) and every sum exact in fp32, so the result must equal the
+direct convolution bit for bit.
 """
 import numpy as np
 import pytest
@@ -24,7 +25,8 @@ from cnn_convolution_forward_amd import synth
 from parity import dev
 
 pytestmark = pytest.mark.gpu
-TAU_W = 2.0 ** -9
+TAU = 1e-3          # the bf16 contract, relative to the direct S
+TAU_W = 2.0 ** -9   # the derived transform-domain bound (diagnostic only)
 
 
 def _wl(N, C, H, W, Co, p, seed=700):
@@ -41,6 +43,23 @@ def _run(wl, t, out_dtype="f32", relu=False):
     if out_dtype == "bf16":
         y = synth.bf16_bits_to_f32(y.view(np.uint16))
     return y.astype(np.float64)
+
+
+def _check_contract(wl, t, got):
+    """|gpu - y_ref| <= 1e-3 * S element by element (direct oracle); the
+    transform-domain figure is printed beside it."""
+    y_ref, S = oracle.conv2d(t.x, t.w, t.b, 1, wl.pad)
+    assert got.shape == y_ref.shape
+    d = np.abs(got - y_ref)
+    bad = d > TAU * S
+    _, Sw = oracle.winograd_f2x2_3x3(t.x, t.w, t.b, wl.pad)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rs = float(np.max(np.where(S > 0, d / np.where(S > 0, S, 1), 0.0)))
+        rw = float(np.max(np.where(Sw > 0, d / np.where(Sw > 0, Sw, 1), 0.0)))
+    print("winograd %s: max |d|/S = %.3g (contract %g), max |d|/Sw = %.3g (derived bound %.3g)" % (
+        wl.x_shape, rs, TAU, rw, TAU_W))
+    assert not bad.any(), "%d exceed 1e-3*S; first %s: gpu %r ref %r S %r" % (
+        bad.sum(), tuple(np.argwhere(bad)[0]), got[bad][0], y_ref[bad][0], S[bad][0])
 
 
 SHAPES = [
@@ -62,13 +81,7 @@ SHAPES = [
 def test_winograd_small(shape):
     wl = _wl(*shape)
     t = synth.make_inputs(wl, seed=sum(shape))
-    y_ref, Sw = oracle.winograd_f2x2_3x3(t.x, t.w, t.b, wl.pad)
-    got = _run(wl, t)
-    assert got.shape == y_ref.shape
-    d = np.abs(got - y_ref)
-    bad = d > TAU_W * Sw
-    assert not bad.any(), "%d exceed; first %s: gpu %r ref %r Sw %r" % (
-        bad.sum(), tuple(np.argwhere(bad)[0]), got[bad][0], y_ref[bad][0], Sw[bad][0])
+    _check_contract(wl, t, _run(wl, t))
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -91,10 +104,7 @@ def test_winograd_epilogue_bf16_relu_integer_exact():
 def test_winograd_full_3x3_layer():
     wl = synth.WORKLOADS["conv3x3_bf16"]
     t = synth.make_inputs(wl)
-    y_ref, Sw = oracle.winograd_f2x2_3x3(t.x, t.w, t.b, 1)
-    got = _run(wl, t)
-    d = np.abs(got - y_ref)
-    assert np.all(d <= TAU_W * Sw), float(np.max(d / np.maximum(Sw, 1e-30)))
+    _check_contract(wl, t, _run(wl, t))
 
 
 def test_winograd_validation():
