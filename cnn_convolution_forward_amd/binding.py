@@ -19,14 +19,14 @@ LIB_PATH = os.path.join(PKG, "libconvfwd.so")
 CONV_OK = 0
 STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_NULL", 2: "CONV_ERR_PARAM", 3: "CONV_ERR_SHAPE",
                 4: "CONV_ERR_OVERFLOW", 5: "CONV_ERR_ALIAS", 6: "CONV_ERR_WORKSPACE",
-                7: "CONV_ERR_ALGO", 8: "CONV_ERR_HIP"}
+                7: "CONV_ERR_ALGO", 8: "CONV_ERR_HIP", 9: "CONV_ERR_SCRATCH"}
 ALGO = {"auto": 0, "mfma": 1, "valu": 2, "winograd": 3}
 
 # Every symbol include/conv_fwd.h declares.
 EXPORTS = ("conv_out_dim", "conv_status_str", "conv_version",
            "conv2d_fwd_bf16", "conv2d_fwd_f32", "conv3d_fwd_bf16", "conv3d_fwd_f32",
            "conv2d_fwd_workspace_bytes", "conv2d_fwd_bf16_ws",
-           "conv2d_pack_weights_bf16", "conv2d_fwd_bf16_prepacked",
+           "conv2d_pack_weights_bf16", "conv2d_fwd_bf16_prepacked", "conv2d_fwd_bf16_noalloc",
            "conv_im2col_bytes", "conv2d_im2col_bf16", "conv3d_im2col_bf16",
            "conv2d_fwd_bf16_explicit", "conv3d_fwd_bf16_explicit",
            "conv_out_dim_dilated", "conv_fwd_bf16", "conv_fwd_f32", "conv_xcol_bytes",
@@ -88,6 +88,8 @@ def lib():
         L.conv2d_pack_weights_bf16.argtypes = [_vp, _vp, _sz] + [_i] * 9 + [_vp]
         L.conv2d_fwd_bf16_prepacked.restype = _i
         L.conv2d_fwd_bf16_prepacked.argtypes = [_vp, _vp, _sz, _vp, _vp] + [_i] * 9 + [_vp]
+        L.conv2d_fwd_bf16_noalloc.restype = _i
+        L.conv2d_fwd_bf16_noalloc.argtypes = d2
         L.conv_im2col_bytes.restype = _sz
         L.conv_im2col_bytes.argtypes = [_i] * 9
         L.conv2d_im2col_bf16.restype = _i
@@ -180,6 +182,10 @@ def conv2d_fwd_bf16_ws(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, str
                        stream=None):
     return lib().conv2d_fwd_bf16_ws(x, w, bias, y, ws, ws_bytes, N, C_in, H, W, C_out, K, stride, pad,
                                     algo, stream)
+
+
+def conv2d_fwd_bf16_noalloc(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo=0, stream=None):
+    return lib().conv2d_fwd_bf16_noalloc(x, w, bias, y, N, C_in, H, W, C_out, K, stride, pad, algo, stream)
 
 
 def conv_im2col_bytes(ndim, N, C_in, D, H, W, K, stride, pad):

@@ -294,6 +294,7 @@ const char *conv_status_str(int status) {
         case CONV_ERR_WORKSPACE: return "workspace too small for X_col";
         case CONV_ERR_ALGO: return "algorithm not available for this dtype or shape";
         case CONV_ERR_HIP: return "HIP kernel launch failed";
+        case CONV_ERR_SCRATCH: return "problem needs more than the library's static scratch array (CONV_STATIC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -377,6 +378,21 @@ conv_status_t conv2d_fwd_bf16_prepacked(const uint16_t *x, const void *workspace
         return CONV_ERR_ALIAS;
     return to_status(convfwd::launch_igemm_prepacked_bf16(sh, x, (const uint16_t *)workspace, bias, y,
                                                           (hipStream_t)stream));
+}
+
+conv_status_t conv2d_fwd_bf16_noalloc(const uint16_t *x, const uint16_t *w, const float *bias, float *y,
+                                      int N, int C_in, int H, int W, int C_out, int K, int stride, int pad,
+                                      int algo, void *stream) {
+    if (!x || !w || !y) return CONV_ERR_NULL;
+    Shape sh;
+    conv_status_t st = make_shape(2, N, C_in, 1, H, W, C_out, K, stride, pad, sh);
+    if (st != CONV_OK) return st;
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_VALU) return CONV_ERR_ALGO;
+    const size_t need = pick_route(sh, algo) == CONV_ALGO_MFMA ? convfwd::igemm_workspace_bytes(sh, x, w) : 0;
+    if (need > convfwd::kStaticScratchBytes) return CONV_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need && convfwd::static_scratch(&ws) != hipSuccess) return CONV_ERR_HIP;
+    return fwd_bf16_sh(sh, x, w, bias, y, algo, stream, true, ws, need ? convfwd::kStaticScratchBytes : 0);
 }
 
 size_t conv_im2col_bytes(int ndim, int N, int C_in, int D, int H, int W, int K, int stride,

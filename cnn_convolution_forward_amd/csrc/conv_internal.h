@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "conv_fwd.h"
+
 namespace convfwd {
 
 // One convolution problem.  2D problems are carried as 3D with D = Do = 1,
@@ -119,5 +121,10 @@ hipError_t launch_depthwise_bf16(const Shape &sh, const uint16_t *x, const uint1
                                  float *y, hipStream_t st);
 hipError_t launch_depthwise_f32(const Shape &sh, const float *x, const float *w, const float *bias,
                                 float *y, hipStream_t st);
+
+// The library's own device scratch array (static_scratch.hip): its size, and
+// its address on the current device (looked up once per device, then kept).
+constexpr size_t kStaticScratchBytes = CONV_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void **ptr);
 
 }  // namespace convfwd

@@ -28,7 +28,8 @@
  *              The output is always fp32; accumulation is fp32; bias is fp32.
  *   Memory     every tensor pointer is a DEVICE pointer owned by the caller.
  *              The library allocates nothing, frees nothing and keeps no
- *              pointer after the call returns.
+ *              pointer after the call returns (conv2d_fwd_bf16_noalloc uses
+ *              a fixed array of its own instead of a workspace; see there).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Work is
  *              enqueued on it and the call returns before the work finishes;
  *              the caller synchronises.  Calls on one stream run in order.
@@ -65,7 +66,9 @@ typedef enum {
     CONV_ERR_ALIAS = 5,      /* y overlaps x, w, bias or the workspace                      */
     CONV_ERR_WORKSPACE = 6,  /* workspace smaller than conv*_im2col_bytes() requires        */
     CONV_ERR_ALGO = 7,       /* the requested algorithm does not exist for this dtype/shape */
-    CONV_ERR_HIP = 8         /* a HIP launch failed                                         */
+    CONV_ERR_HIP = 8,        /* a HIP launch failed                                         */
+    CONV_ERR_SCRATCH = 9     /* conv2d_fwd_bf16_noalloc: the problem needs more than
+                                CONV_STATIC_SCRATCH_BYTES of scratch                        */
 } conv_status_t;
 
 /* Kernel route.  AUTO picks by shape, for bf16: first the matrix cores'
@@ -169,6 +172,31 @@ CONV_API conv_status_t conv2d_fwd_bf16_prepacked(const uint16_t *x, const void *
                                                  size_t workspace_bytes, const float *bias, float *y,
                                                  int N, int C_in, int H, int W, int C_out,
                                                  int K, int stride, int pad, int algo, void *stream);
+
+/* ---- without allocation ------------------------------------------------- */
+
+/* Size of the library's own device scratch array (one per GPU, kept until
+ * the process ends), used by conv2d_fwd_bf16_noalloc. */
+#define CONV_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* For callers that cannot allocate device memory (code under stream or graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and result as conv2d_fwd_bf16_ws, with the workspace taken from
+ * a file-scope device array of CONV_STATIC_SCRATCH_BYTES inside the library
+ * instead of from the caller.  No hipMalloc, hipFree or other allocating call
+ * is made.  The array's address on the current device is looked up on the
+ * first call on that device.  Arguments, layouts, ownership and errors as
+ * conv2d_fwd_bf16_ws (minus the workspace pair), plus CONV_ERR_SCRATCH, before
+ * any launch, when conv2d_fwd_workspace_bytes() of these arguments exceeds
+ * CONV_STATIC_SCRATCH_BYTES (3x3 layers with C_out*C_in*9*2 > 8 MiB, e.g.
+ * C_in = C_out = 1024), and CONV_ERR_HIP if the address lookup fails.  All
+ * calls on one GPU share its one array and every call overwrites it (nothing
+ * in it needs to start at zero): two calls that can run at the same time on
+ * one GPU (different streams, or different host threads) race and may give
+ * wrong results; serialise them, e.g. on one stream. */
+CONV_API conv_status_t conv2d_fwd_bf16_noalloc(const uint16_t *x, const uint16_t *w, const float *bias,
+                                               float *y, int N, int C_in, int H, int W, int C_out,
+                                               int K, int stride, int pad, int algo, void *stream);
 
 /* ---- explicit im2col path ("Why use matrix multiplication for convolution",
  *      2.2 and 3.1): X_col is materialised in caller-owned device memory. ---- */

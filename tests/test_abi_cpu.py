@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert B.conv_version() >= 100
-    for s in range(9):
+    for s in range(10):
         assert B.status_str(s) and B.status_str(s) != "unknown status"
     assert B.status_str(99) == "unknown status"
 
