@@ -24,6 +24,7 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t a, int ha, uint32_t b, 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64).
 #define CONV3X3_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+
 // One wave copies 1 KB (64 lanes x 16 bytes) from buffer `rsrc` at byte
 // offset soff + 16*lane straight into LDS at `dst` + 16*lane.  Issued as
 // inline assembly: the instruction has no register result, and the

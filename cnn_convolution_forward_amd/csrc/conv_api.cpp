@@ -237,13 +237,16 @@ size_t wgrad_workspace(const Shape &fw) {
 namespace convfwd {
 
 // MFMA route: a specialised kernel when the shape matches one (3x3 stride 1
-// -- the column-group kernel when a weight workspace is given --, pointwise,
-// short reduction), else the general implicit GEMM.
+// -- the column-group kernel when a weight workspace is given, its persistent
+// variant for small batches --, pointwise, short reduction), else the general
+// implicit GEMM.
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,
                              const float *bias, float *y, hipStream_t st, void *ws, size_t ws_bytes) {
     if (ws && ws_bytes >= conv3x3s1_workspace_bytes(sh) && conv3x3cg_supported(sh, x, w)) {
         uint16_t *wp = (uint16_t *)ws;
         launch_pack_w3x3(sh, w, wp, st);
+        if (conv3x3cgp_supported(sh, x, w) && conv3x3cgp_preferred(sh))
+            return launch_conv3x3cgp_bf16(sh, x, wp, bias, y, st);
         return launch_conv3x3cg_bf16(sh, x, wp, bias, y, st);
     }
     if (conv3x3s1_supported(sh, x, w)) {
@@ -257,6 +260,8 @@ hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t 
 
 hipError_t launch_igemm_prepacked_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack,
                                        const float *bias, float *y, hipStream_t st) {
+    if (conv3x3cgp_supported(sh, x, wpack) && conv3x3cgp_preferred(sh))
+        return launch_conv3x3cgp_bf16(sh, x, wpack, bias, y, st);
     if (conv3x3cg_supported(sh, x, wpack)) return launch_conv3x3cg_bf16(sh, x, wpack, bias, y, st);
     if (conv3x3s1_supported(sh, x, wpack))
         return launch_conv3x3s1_bf16(sh, x, wpack, const_cast<uint16_t *>(wpack), bias, y, st, true);

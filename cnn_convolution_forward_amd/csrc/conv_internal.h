@@ -101,6 +101,12 @@ hipError_t launch_conv3x3s1_bf16(const Shape &sh, const uint16_t *x, const uint1
 void launch_pack_w3x3(const Shape &sh, const uint16_t *w, uint16_t *wpack, hipStream_t st);
 // Column-group 3x3 stride-1 kernel (packed weights only).
 bool conv3x3cg_supported(const Shape &sh, const void *x, const void *w);
+// persistent variant of the column-group kernel (NCHW, dilation 1, groups 1),
+// and whether to prefer it over one workgroup per tile for this shape
+bool conv3x3cgp_supported(const Shape &sh, const void *x, const void *w);
+bool conv3x3cgp_preferred(const Shape &sh);
+hipError_t launch_conv3x3cgp_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack, const float *bias,
+                                  float *y, hipStream_t st);
 hipError_t launch_conv3x3cg_bf16(const Shape &sh, const uint16_t *x, const uint16_t *wpack, const float *bias,
                                  float *y, hipStream_t st);
 // Pointwise (K = 1, stride 1, pad 0) GEMM kernel.

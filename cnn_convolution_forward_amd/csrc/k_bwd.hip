@@ -479,7 +479,12 @@ struct WgGeo {
     static constexpr int DU = (2 * KS) | 1;           // dout units per channel row
     static constexpr int XU = (W / 8 + 2) | 1;        // x units per (channel, kernel row)
     static constexpr int D_BYTES = 64 * DU * 16;
-    static constexpr int STAGE = D_BYTES + 64 * 3 * XU * 16;
+    // the x rows end in a zero unit, but the kw = 2 shift of a row's last
+    // unit also reads the first dword after it: for the stage's last row
+    // that is past the stage, so each stage ends in one more unit, zeroed
+    // once and never copied over
+    static constexpr int X_END = D_BYTES + 64 * 3 * XU * 16;
+    static constexpr int STAGE = X_END + 16;
     static constexpr int INSTS = DU + 3 * XU;         // 1 KB copy instructions per stage
     static constexpr int PER_WAVE = (INSTS + 3) / 4;  // instructions of waves 0 .. INSTS % 4 - 1
 };
@@ -599,6 +604,7 @@ void wgrad3x3_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict_
         }
     };
 
+    if (tid < 3) *reinterpret_cast<uint4 *>(smem + tid * G::STAGE + G::X_END) = make_uint4(0, 0, 0, 0);
     const int rows = row_end > row_begin ? row_end - row_begin : 0;
     if (rows > 0) issue(row_begin, 0);
     if (rows > 1) issue(row_begin + 1, 1);

@@ -149,6 +149,41 @@ def test_backward_misaligned_inputs():
     compare(db.cpu().numpy(), rdb, Sdb, TAU, label="db")
 
 
+def test_weight_gradient_ignores_stale_lds():
+    """The 3x3 weight-gradient kernel reads one dword past each stage's last
+    x row (the kw = 2 shift of its trailing zero unit); that dword must be
+    its own zero pad, not whatever an earlier kernel left in LDS.  A forward
+    pass with a NaN bias first fills the LDS of every CU with NaN (the
+    epilogue image), then dw of finite inputs must be finite and equal to
+    dw computed without it."""
+    wl = synth.ALL_WORKLOADS["conv3x3_bf16"]
+    t = synth.make_inputs(wl)
+    rng = np.random.default_rng(5)
+    dout = synth.f32_to_bf16_bits(rng.standard_normal(size=wl.y_shape, dtype=np.float32))
+    xt, wt, dt = dev(t.x, None), dev(t.w, None), dev(dout, None)
+    prm = B.make_params(tuple(xt.shape), tuple(wt.shape), 1, 1, 1, 1)
+    nw = B.conv_bwd_weight_workspace_bytes(prm)
+    ws = torch.empty(nw, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def dw_now():
+        dw = torch.full(wl.w_shape, float("nan"), device="cuda")
+        db = torch.full((wl.C_out,), float("nan"), device="cuda")
+        assert B.conv_bwd_weight_bf16(prm, xt.data_ptr(), dt.data_ptr(), dw.data_ptr(), db.data_ptr(),
+                                      ws.data_ptr(), nw, st) == 0
+        torch.cuda.synchronize()
+        return dw.cpu().numpy()
+
+    clean = dw_now()
+    nan_bias = torch.full((wl.C_out,), float("nan"), device="cuda")
+    y = B.conv(xt, wt, nan_bias, 1, 1, workspace=B.workspace_for(xt, wt, 1, 1))
+    torch.cuda.synchronize()
+    assert not torch.isfinite(y).any()
+    after = dw_now()
+    assert np.isfinite(clean).all() and np.isfinite(after).all()
+    np.testing.assert_array_equal(after, clean)
+
+
 def test_backward_deterministic():
     wl, x, w, dout = _inputs(2, 4, 64, (28, 28), 64, 3, 1, 1, 1, 1, seed=5)
     a = _gpu(wl, x, w, dout)
