@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first: about 40 ms of continuous work brings the clocks to steady state")
     ap.add_argument("--workload", default="conv3x3_bf16")
-    ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit", "winograd"])
+    ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit", "winograd", "plain"],
+                    help="plain: the 2D entry point without a workspace (conv2d_fwd_bf16), AUTO's kernel choice")
     ap.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"], help="layout of x and y (forward)")
     ap.add_argument("--out", default="f32", choices=["f32", "bf16"], help="output dtype (forward)")
     ap.add_argument("--relu", action="store_true", help="fused ReLU after the bias (forward)")
@@ -160,6 +161,7 @@ class Runner:
             self.ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
         elif route in ("auto", "mfma") and wl.ndim == 2 and wl.dtype == "bf16" and wl.plain:
             self.packed = B.workspace_for(self.x, self.w, wl.stride, wl.pad, route)
+        # route "plain": no workspace, no packed weights: the one conv2d_fwd_bf16 call
         if route == "explicit":
             if self.params is not None:
                 nbytes = B.conv_xcol_bytes(self.params)
@@ -492,7 +494,7 @@ def measure(wl, route, steps, warmup, backward=False, options=None):
 def report_all(steps, warmup):
     from cnn_convolution_forward_amd import synth
     for name, wl in synth.ALL_WORKLOADS.items():
-        routes = ["valu"] if wl.dtype == "f32" else ["auto", "mfma", "valu", "explicit"]
+        routes = ["valu"] if wl.dtype == "f32" else ["auto", "mfma", "valu", "explicit"] + (["plain"] if wl.plain and wl.ndim == 2 else [])
         for route in routes:
             _, wall, gpu, per = measure(wl, route, steps, warmup)
             t = per[0]

@@ -55,7 +55,8 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                     const float *__restrict__ bias, float *__restrict__ y,
-                    int C, int Co, int plane, int64_t P, int npt, int ncb, int remap, int out_bf16, int relu) {
+                    int C, int Co, int plane, int64_t P, int npt, int ncb, int remap, int out_bf16, int relu,
+                    int64_t xcs, int64_t xns) {
     __shared__ __align__(16) uint16_t As[2][kBM][kLdA];
     __shared__ __align__(16) uint16_t Bs[2][kBK][kLdB];
 
@@ -75,9 +76,12 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(P / plane * C * plane * 2));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)Co * C * 2));
 
-    // loader units: A u -> (row u/4, k-quad u%4); B u -> (k row u/16, 8-pixel group u%16)
+    // loader units: A u -> (row u/4, k-quad u%4); B u -> (k row u/16, 8-pixel group u%16).
+    // Element (k, image n, pixel q) of B is at x[k * xcs + n * xns + q]: NCHW
+    // has xcs = plane, xns = C * plane; the explicit route's X_col has xcs = N
+    // * plane (one row per reduction index), xns = plane.
     uint32_t a_off[2], b_off[2];
-    const uint32_t b_step = (uint32_t)kBK * plane * 2;
+    const uint32_t b_step = (uint32_t)(kBK * xcs * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = tid + 256 * i;
@@ -87,7 +91,7 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
         const int64_t px = j0 + pu * 8;
         if (px < P) {
             const int64_t n = px / plane, q = px - n * plane;
-            b_off[i] = (uint32_t)(((n * C + kr) * plane + q) * 2);
+            b_off[i] = (uint32_t)((n * xns + kr * xcs + q) * 2);
         } else {
             b_off[i] = kOob;
         }
@@ -534,7 +538,32 @@ hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_
         return hipGetLastError();
     }
     hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co,
-                       plane, P, npt, ncb, remap, sh.out_bf16, sh.relu);
+                       plane, P, npt, ncb, remap, sh.out_bf16, sh.relu, (int64_t)plane, (int64_t)sh.C * plane);
+    return hipGetLastError();
+}
+
+// The explicit route's GEMM on the tiled kernel: Y_n = W_row @ X_col[:, image
+// n's columns] ("Why use matrix multiplication for convolution", 2.3) is a
+// pointwise layer whose C_in * K^dims input "channels" are the X_col rows,
+// J = N * plane elements apart.  Groups 1, NCHW, an fp32 or bf16 output;
+// X_col, W_row and y below 2 GiB, 16-byte aligned X_col and w.
+bool gemm_xcol_pw_supported(const Shape &sh, const void *xcol, const void *w) {
+    const int64_t rows = sh.xcol_rows(), J = sh.pixels(), plane = sh.out_plane();
+    return sh.G == 1 && !sh.nhwc && rows % kBK == 0 && plane % 8 == 0 && plane < (INT64_C(1) << 31) &&
+           rows * J * 2 < (INT64_C(1) << 31) && (int64_t)sh.Co * rows * 2 < (INT64_C(1) << 31) &&
+           sh.y_elems() * 4 < (INT64_C(1) << 31) && ((uintptr_t)xcol % 16) == 0 && ((uintptr_t)w % 16) == 0;
+}
+
+hipError_t launch_gemm_xcol_pw_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,
+                                    float *y, hipStream_t st) {
+    const int64_t P = sh.pixels();
+    const int plane = (int)sh.out_plane();
+    const int npt = (int)((P + kBN - 1) / kBN);
+    const int ncb = (sh.Co + kBM - 1) / kBM;
+    const int64_t T = (int64_t)npt * ncb;
+    const int remap = (T % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, xcol, w, bias, y, (int)sh.xcol_rows(),
+                       sh.Co, plane, P, npt, ncb, remap, sh.out_bf16, sh.relu, P, (int64_t)plane);
     return hipGetLastError();
 }
 

@@ -72,11 +72,84 @@ void im2col_bf16_kernel(Shape sh, const uint16_t *__restrict__ x, uint16_t *__re
     }
 }
 
+// The five dwords that start q dwords into d[0..15] (q uniform across the
+// wave: one scalar branch, constant register indices in each arm).
+__device__ __forceinline__ void pick5(const uint32_t (&d)[16], int q, uint32_t (&o)[5]) {
+    switch (q) {
+#define IM2COL_PICK(Q) case Q: o[0] = d[Q]; o[1] = d[Q + 1]; o[2] = d[Q + 2]; o[3] = d[Q + 3]; o[4] = d[Q + 4]; break;
+        IM2COL_PICK(0) IM2COL_PICK(1) IM2COL_PICK(2) IM2COL_PICK(3) IM2COL_PICK(4) IM2COL_PICK(5)
+        IM2COL_PICK(6) IM2COL_PICK(7) IM2COL_PICK(8) IM2COL_PICK(9) IM2COL_PICK(10)
+        default: IM2COL_PICK(11)
+#undef IM2COL_PICK
+    }
+}
+
+// 2D, stride 1, W % 8 == 0, Wo % 8 == 0, (K - 1) * d <= 16, 16-byte aligned x
+// and X_col.  Row r = (ic, kh, kw) of X_col, over image n's columns, is input
+// plane (n, ic) shifted by (kh*d - p, kw*d - p), zeros outside it.  A thread
+// takes 8 consecutive columns (one output row oh, columns ow0 .. ow0 + 7;
+// they never straddle rows since Wo % 8 == 0) of all K*K rows of one input
+// channel: for each kh it loads input row ih = oh + kh*d - p as the four
+// aligned 16-byte chunks from a0 = floor((ow0 - p) / 8) * 8 on (32 elements,
+// enough for the 8 + (K-1)*d needed; a chunk lies wholly inside the row or
+// wholly outside since W % 8 == 0, and one outside, or a row outside the
+// image, reads as zeros), then writes the K rows kw as 16-byte stores of
+// the elements shifted by t = kw*d + (ow0 - p - a0) -- the same t for the
+// whole wave, since ow0 is a multiple of 8.  K*K stores and 4K loads a
+// thread (the loads mostly hit L2: the K*K rows of a channel reuse them).
+__global__ __launch_bounds__(kThreads)
+void im2col_s1_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xcol, int C, int H, int W, int Ho,
+                      int Wo, int K, int p, int d, int64_t J) {
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kColsPerThread;
+    if (j0 >= J) return;
+    const int ic = blockIdx.y;
+    const int64_t plane = (int64_t)Ho * Wo;
+    const int n = (int)(j0 / plane);
+    const int q0 = (int)(j0 - n * plane);
+    const int oh = q0 / Wo, ow0 = q0 - oh * Wo;
+    const int a0 = ((ow0 - p) >> 3) << 3;                 // floor to a multiple of 8 (arithmetic shift)
+    const int s0 = ow0 - p - a0;                          // 0 .. 7, uniform
+    const uint16_t *plane_x = x + (int64_t)(n * C + ic) * H * W;
+    uint16_t *dst = xcol + (int64_t)ic * K * K * J + j0;
+    for (int kh = 0; kh < K; ++kh) {
+        const int ih = oh + kh * d - p;
+        uint32_t dw[16];
+        const bool row_in = ih >= 0 && ih < H;
+        const uint16_t *row = plane_x + (int64_t)(row_in ? ih : 0) * W;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int a = a0 + 8 * c;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (row_in && a >= 0 && a < W) v = *reinterpret_cast<const uint4 *>(row + a);
+            dw[4 * c + 0] = v.x; dw[4 * c + 1] = v.y; dw[4 * c + 2] = v.z; dw[4 * c + 3] = v.w;
+        }
+        for (int kw = 0; kw < K; ++kw) {
+            const int t = kw * d + s0;                    // element shift, <= 16 + 7
+            uint32_t o[5];
+            pick5(dw, t >> 1, o);
+            const int sh = (t & 1) * 2;                   // bytes
+            const uint4 out = make_uint4(__builtin_amdgcn_alignbyte(o[1], o[0], sh),
+                                         __builtin_amdgcn_alignbyte(o[2], o[1], sh),
+                                         __builtin_amdgcn_alignbyte(o[3], o[2], sh),
+                                         __builtin_amdgcn_alignbyte(o[4], o[3], sh));
+            *reinterpret_cast<uint4 *>(dst + (int64_t)(kh * K + kw) * J) = out;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol, hipStream_t st) {
     const int64_t J = sh.pixels();
     const int rows = (int)sh.xcol_rows();
+    if (sh.ndim == 2 && sh.s == 1 && sh.W % 8 == 0 && sh.Wo % 8 == 0 && (sh.K - 1) * sh.dil <= 16 && !sh.nhwc &&
+        ((uintptr_t)x % 16) == 0 && ((uintptr_t)xcol % 16) == 0 && sh.C <= 65535) {
+        const int64_t groups = J / kColsPerThread;
+        dim3 grid((unsigned)((groups + kThreads - 1) / kThreads), (unsigned)sh.C);
+        hipLaunchKernelGGL(im2col_s1_kernel, grid, dim3(kThreads), 0, st, x, xcol, sh.C, sh.H, sh.W, sh.Ho, sh.Wo,
+                           sh.K, sh.p, sh.dil, J);
+        return hipGetLastError();
+    }
     const int64_t groups = (J + kColsPerThread - 1) / kColsPerThread;
     dim3 grid((unsigned)((groups + kThreads - 1) / kThreads), (unsigned)(rows < 65535 ? rows : 65535));
     hipLaunchKernelGGL(im2col_bf16_kernel, grid, dim3(kThreads), 0, st, sh, x, xcol, J, rows);

@@ -22,8 +22,15 @@
 // fp16 rather than bf16 for U and V: the transformed operands are rounded
 // before the products, and fp16's 11-bit significand keeps that error near
 // 2^-11 of the transform-domain magnitudes (bf16's 8 bits would be 8x worse,
-// the low-precision risk the page warns about).  N(0,1)-scale activations and
-// weights stay far inside fp16's range.
+// the low-precision risk the page warns about).  fp16 spans only 2^-24 ..
+// 65504 where bf16 spans fp32's range, so x and w are first scaled by powers
+// of two: a pass over both finds max|x| and max|w|, and the transforms
+// multiply by 2^kx and 2^kw chosen so that the transformed values stay below
+// 2^13 (|V| <= 4 max|x|, |U| <= 2.25 max|w|), and the output transform
+// multiplies by 2^-(kx + kw).  Scaling by a power of two is exact, so results
+// within fp16's normal range are those of the unscaled transforms; only
+// values more than ~2^27 below their tensor's largest magnitude become fp16
+// subnormals.
 //
 // A GEMM workgroup computes 32 output channels x 32 blocks for all 16
 // points: wave w owns points 4w..4w+3 (4 accumulator tiles), loads its
@@ -47,15 +54,103 @@ __device__ __forceinline__ uint16_t f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// 0. The scale exponents.  mag[0], mag[1] receive the bit patterns of max|x|
+// and max|w| as fp32 (non-negative floats order like their bit patterns, so
+// an integer maximum is exact).  Two kernels, no atomics: kMagGroups
+// workgroups each reduce a stripe to part[2 g], part[2 g + 1], then one
+// workgroup reduces those.
+constexpr int kMagGroups = 512;
+
+__device__ __forceinline__ uint32_t mag_of_bf16(uint32_t b) { return (b & 0x7fffu) << 16; }
+
+__device__ __forceinline__ uint32_t mag_of_pair(uint32_t v) { return max(mag_of_bf16(v), mag_of_bf16(v >> 16)); }
+
+// maximum of v over the workgroup (256 threads), in every thread
+__device__ __forceinline__ uint32_t wg_max(uint32_t v, uint32_t *red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = max(max(red[0], red[1]), max(red[2], red[3]));
+    __syncthreads();
+    return v;
+}
+
+__global__ __launch_bounds__(256)
+void wino_mag_kernel(const uint16_t *__restrict__ x, int64_t nx, const uint16_t *__restrict__ w, int64_t nw,
+                     uint32_t *__restrict__ part) {
+    __shared__ uint32_t red[4];
+    uint32_t mx = 0, mw = 0;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x, nt = (int64_t)gridDim.x * 256;
+    if (((uintptr_t)x & 15) == 0) {
+        // 16 bytes a lane, four loads in flight, then the elements past the last whole group of 8
+        const uint4 *x8 = reinterpret_cast<const uint4 *>(x);
+        const int64_t n8 = nx / 8;
+        int64_t i = tid;
+        for (; i + 3 * nt < n8; i += 4 * nt) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = x8[i + k * nt];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mx = max(mx, max(max(mag_of_pair(v[k].x), mag_of_pair(v[k].y)),
+                                 max(mag_of_pair(v[k].z), mag_of_pair(v[k].w))));
+        }
+        for (; i < n8; i += nt) {
+            const uint4 v = x8[i];
+            mx = max(mx, max(max(mag_of_pair(v.x), mag_of_pair(v.y)), max(mag_of_pair(v.z), mag_of_pair(v.w))));
+        }
+        for (int64_t j = 8 * n8 + tid; j < nx; j += nt) mx = max(mx, mag_of_bf16(x[j]));
+    } else {
+        for (int64_t j = tid; j < nx; j += nt) mx = max(mx, mag_of_bf16(x[j]));
+    }
+    for (int64_t j = tid; j < nw; j += nt) mw = max(mw, mag_of_bf16(w[j]));
+    mx = wg_max(mx, red);
+    mw = wg_max(mw, red);
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = mx;
+        part[2 * blockIdx.x + 1] = mw;
+    }
+}
+
+__global__ __launch_bounds__(256)
+void wino_mag_final_kernel(const uint32_t *__restrict__ part, uint32_t *__restrict__ mag) {
+    __shared__ uint32_t red[4];
+    uint32_t mx = 0, mw = 0;
+    for (int g = threadIdx.x; g < kMagGroups; g += 256) {
+        mx = max(mx, part[2 * g]);
+        mw = max(mw, part[2 * g + 1]);
+    }
+    mx = wg_max(mx, red);
+    mw = wg_max(mw, red);
+    if (threadIdx.x == 0) {
+        mag[0] = mx;
+        mag[1] = mw;
+    }
+}
+
+// 2^k with max * 2^k * 4 <= 2^13: k = 11 - E for max = m 2^E, m in [0.5, 1);
+// 0 for a zero, infinite or NaN maximum (nothing to scale, or nothing that
+// scaling could save).
+__device__ __forceinline__ int wino_scale_exp(uint32_t magbits) {
+    const float m = __uint_as_float(magbits);
+    if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;
+    int e;
+    (void)frexpf(m, &e);
+    return 11 - e;
+}
+
 // 1. U: one thread per (k, c).
 __global__ __launch_bounds__(256)
-void wino_weight_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ U, int Co, int C) {
+void wino_weight_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ U, int Co, int C,
+                        const uint32_t *__restrict__ mag) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)Co * C) return;
+    const int kw = wino_scale_exp(mag[1]);
     const uint16_t *g = w + e * 9;
     float gv[3][3];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) gv[i / 3][i % 3] = bf16_to_f32(g[i]);
+    for (int i = 0; i < 9; ++i) gv[i / 3][i % 3] = ldexpf(bf16_to_f32(g[i]), kw);
     // t = G g (4x3), u = t G^T (4x4)
     float t[4][3];
 #pragma unroll
@@ -82,10 +177,11 @@ void wino_weight_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ U
 // 2. V: one thread per (block t, 8 consecutive channels); 16 stores of 16 bytes.
 __global__ __launch_bounds__(256)
 void wino_input_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ V, int C, int H, int W, int p, int TH,
-                       int TW, int64_t T) {
+                       int TW, int64_t T, const uint32_t *__restrict__ mag) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int cgrp = C / 8;
     if (e >= T * cgrp) return;
+    const int kx = wino_scale_exp(mag[0]);
     const int64_t t = e / cgrp;
     const int c0 = (int)(e - t * cgrp) * 8;
     const int bw = (int)(t % TW);
@@ -104,8 +200,9 @@ void wino_input_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ V,
             for (int j = 0; j < 4; ++j) {
                 const int ih = ih0 + i, iw = iw0 + j;
                 const bool in = 0 <= ih && ih < H && 0 <= iw && iw < W;
-                d[i][j] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                    xr, (int)(in ? (uint32_t)(ih * W + iw) * 2u : kOob), 0, 0));
+                d[i][j] = ldexpf(bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                     xr, (int)(in ? (uint32_t)(ih * W + iw) * 2u : kOob), 0, 0)),
+                                 kx);
             }
         // s = B^T d, v = s B
         float s[4][4];
@@ -148,9 +245,10 @@ constexpr int kWiRow = 80;                // pixels per copied row (10 units)
 
 __global__ __launch_bounds__(256)
 void wino_input_tile_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ V, int C, int H, int W, int p,
-                            int TH, int TW, int64_t T, int nbw) {
+                            int TH, int TW, int64_t T, int nbw, const uint32_t *__restrict__ mag) {
     __shared__ __align__(16) uint16_t Xs[kWiC * 4 * kWiRow];
     const int tid = threadIdx.x;
+    const int kx = wino_scale_exp(mag[0]);
     const int c0 = blockIdx.x * kWiC;
     int r = blockIdx.y;
     const int bwg = r % nbw;
@@ -184,7 +282,7 @@ void wino_input_tile_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) d[i][j] = bf16_to_f32(Xs[(c * 4 + i) * kWiRow + col0 + j]);
+                for (int j = 0; j < 4; ++j) d[i][j] = ldexpf(bf16_to_f32(Xs[(c * 4 + i) * kWiRow + col0 + j]), kx);
             float s4[4][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -219,9 +317,11 @@ void wino_input_tile_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict
 // (64 KB; reads run along blocks, conflict-free).
 __global__ __launch_bounds__(256)
 void wino_gemm_kernel(const uint16_t *__restrict__ U, const uint16_t *__restrict__ V, const float *__restrict__ bias,
-                      float *__restrict__ y, Shape sh, int TH, int TW, int64_t T, int nkt, int remap) {
+                      float *__restrict__ y, Shape sh, int TH, int TW, int64_t T, int nkt, int remap,
+                      const uint32_t *__restrict__ mag) {
     __shared__ float Ms[16][32][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int unscale = -(wino_scale_exp(mag[0]) + wino_scale_exp(mag[1]));
     const int C = sh.C, Co = sh.Co;
     // block -> (channel tile, block tile): the channel tiles of one block tile
     // are consecutive logical tiles, and with remap each XCD (block % 8) runs a
@@ -311,8 +411,8 @@ void wino_gemm_kernel(const uint16_t *__restrict__ U, const uint16_t *__restrict
         const int64_t yb = ((int64_t)n * Co + k) * oplane;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const float y0 = r[i][0] + r[i][1] + r[i][2];
-            const float y1 = r[i][1] - r[i][2] - r[i][3];
+            const float y0 = ldexpf(r[i][0] + r[i][1] + r[i][2], unscale);
+            const float y1 = ldexpf(r[i][1] - r[i][2] - r[i][3], unscale);
             const int oh = 2 * bh + i, ow = 2 * bw;
             if (oh >= Ho) continue;
             store_out(y, yb + (int64_t)oh * Wo + ow, y0 + bv, sh.out_bf16, sh.relu);
@@ -325,6 +425,7 @@ struct WinoGeom {
     int TH, TW;
     int64_t T;
     size_t u_bytes, v_bytes;
+    static constexpr size_t kMagBytes = 256 + 8 * kMagGroups;   // the two magnitudes, then the partial maxima
 };
 
 WinoGeom wino_geom(const Shape &sh) {
@@ -351,7 +452,7 @@ bool winograd_supported(const Shape &sh) {
 
 size_t winograd_workspace_bytes(const Shape &sh) {
     const WinoGeom g = wino_geom(sh);
-    return g.u_bytes + g.v_bytes;
+    return g.u_bytes + g.v_bytes + WinoGeom::kMagBytes;
 }
 
 hipError_t launch_winograd_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w, const float *bias, float *y,
@@ -359,22 +460,27 @@ hipError_t launch_winograd_bf16(const Shape &sh, const uint16_t *x, const uint16
     const WinoGeom g = wino_geom(sh);
     uint16_t *U = (uint16_t *)ws;
     uint16_t *V = (uint16_t *)((char *)ws + g.u_bytes);
+    uint32_t *mag = (uint32_t *)((char *)ws + g.u_bytes + g.v_bytes);
     const int64_t nu = (int64_t)sh.Co * sh.C;
-    hipLaunchKernelGGL(wino_weight_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, w, U, sh.Co, sh.C);
+    uint32_t *part = mag + 64;
+    hipLaunchKernelGGL(wino_mag_kernel, dim3(kMagGroups), dim3(256), 0, st, x, sh.x_elems(), w, sh.w_elems(), part);
+    hipLaunchKernelGGL(wino_mag_final_kernel, dim3(1), dim3(256), 0, st, (const uint32_t *)part, mag);
+    hipLaunchKernelGGL(wino_weight_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, st, w, U, sh.Co, sh.C,
+                       (const uint32_t *)mag);
     if (sh.C % kWiC == 0 && sh.W % 8 == 0) {
         const int nbw = (g.TW + kWiB - 1) / kWiB;
         dim3 gi((unsigned)(sh.C / kWiC), (unsigned)((int64_t)sh.N * g.TH * nbw));
         hipLaunchKernelGGL(wino_input_tile_kernel, gi, dim3(256), 0, st, x, V, sh.C, sh.H, sh.W, sh.p, g.TH, g.TW, g.T,
-                           nbw);
+                           nbw, (const uint32_t *)mag);
     } else {
         const int64_t nv = g.T * (sh.C / 8);
         hipLaunchKernelGGL(wino_input_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, x, V, sh.C, sh.H,
-                           sh.W, sh.p, g.TH, g.TW, g.T);
+                           sh.W, sh.p, g.TH, g.TW, g.T, (const uint32_t *)mag);
     }
     const int nkt = (sh.Co + 31) / 32;
     const int64_t nblk = (int64_t)nkt * ((g.T + 31) / 32);
     hipLaunchKernelGGL(wino_gemm_kernel, dim3((unsigned)nblk), dim3(256), 0, st, U, V, bias, y, sh, g.TH, g.TW, g.T, nkt,
-                       nblk % 8 == 0 ? 1 : 0);
+                       nblk % 8 == 0 ? 1 : 0, (const uint32_t *)mag);
     return hipGetLastError();
 }
 

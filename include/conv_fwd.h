@@ -86,7 +86,12 @@ typedef enum {
     CONV_ALGO_WINOGRAD = 3   /* Winograd F(2x2,3x3) ("Why use matrix multiplication for
                                 convolution", 5.1): conv_fwd_ex_bf16 only, with a
                                 workspace; 3x3, stride 1, dilation 1, groups 1, NCHW,
-                                C_in % 16 == 0.  Never chosen by AUTO. */
+                                C_in % 16 == 0.  Never chosen by AUTO.  The transformed
+                                operands are fp16: x and w are first scaled by powers of
+                                two chosen from max|x| and max|w| (one pass over both), so
+                                any finite bf16 data fits; elements more than ~2^27 below
+                                their tensor's largest magnitude lose precision (fp16
+                                subnormals), which the 1e-3 * sum|x w| bound absorbs. */
 } conv_algo_t;
 
 /* floor((in + 2*pad - K)/stride) + 1, or -1 if in < 1, K < 1, stride < 1,

@@ -236,7 +236,8 @@ def test_general_entry_matches_plain_entry(name):
 
 # ---- dilated im2col ----------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [(2, 3, 9, 11, 3, 1, 2, 2), (1, 5, 12, 10, 3, 2, 3, 3), (2, 4, 8, 8, 2, 1, 1, 4)])
+@pytest.mark.parametrize("shape", [(2, 3, 9, 11, 3, 1, 2, 2), (1, 5, 12, 10, 3, 2, 3, 3), (2, 4, 8, 8, 2, 1, 1, 4),
+                                   (2, 4, 8, 16, 3, 1, 2, 2), (1, 3, 6, 24, 3, 1, 3, 3)])
 def test_im2col_dilated_bit_exact(shape):
     N, C, H, W, K, s, p, d = shape
     wl = _wl("col", 2, N, C, (H, W), 1, K, s, p, d, 1)

@@ -152,6 +152,35 @@ def test_im2col_bit_exact_2d(shape):
     np.testing.assert_array_equal(oracle.decode(col), ref)
 
 
+# The vectorised stride-1 path (W % 8 == 0, W_out % 8 == 0): every shift of
+# the 16-byte chunks (kw - p from -9 to +2), pads wider than a chunk, and
+# K = 1 with no shift at all.
+@pytest.mark.parametrize("shape", [(2, 5, 9, 16, 3, 1, 1), (1, 3, 7, 24, 5, 1, 2), (2, 2, 6, 32, 7, 1, 3),
+                                   (1, 2, 5, 16, 3, 1, 9), (3, 4, 4, 8, 1, 1, 0), (1, 3, 3, 8, 3, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_im2col_stride1_vector_path_bit_exact(shape):
+    N, C, H, W, K, s, p = shape
+    assert (W + 2 * p - K + 1) % 8 == 0 and W % 8 == 0
+    rng = np.random.default_rng(sum(shape) + 7)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((N, C, H, W)).astype(np.float32))
+    col = B.im2col(dev(x, None), K, s, p).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.decode(col), oracle.im2col2d(x, K, s, p))
+
+
+# The explicit route's GEMM on the tiled pointwise kernel (C_in * K^2 % 32 == 0,
+# output plane % 8 == 0): ragged output channels and pixel tiles.
+@pytest.mark.parametrize("shape", [(2, 32, 12, 16, 70, 3, 1, 1), (3, 64, 8, 24, 128, 3, 1, 1),
+                                   (1, 96, 5, 8, 200, 1, 1, 0), (2, 32, 7, 8, 16, 3, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+def test_explicit_pointwise_gemm(shape, integer):
+    N, C, H, W, Co, K, s, p = shape
+    wl = synth.Workload("xg", 2, N, C, (H, W), Co, K, s, p, "bf16", "normal", 300)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "explicit"), y_ref, S, TAU["bf16"], exact=integer, label="explicit pw %s" % (shape,))
+
+
 def test_im2col_bit_exact_3d():
     rng = np.random.default_rng(5)
     x = synth.f32_to_bf16_bits(rng.standard_normal((2, 3, 4, 6, 5)).astype(np.float32))

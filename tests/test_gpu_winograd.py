@@ -12,8 +12,11 @@ magnitude and the output transform only adds and subtracts, which gives
 (about 1.7x, at most 4x, the direct S on N(0,1) data).  The tests assert the
 contract bound and print the measured error against both.  On integer data
 every transformed value is exact in fp16 (multiples of 1/4 up to 4.5 and
-integers up to 8) and every sum exact in fp32, so the result must equal the
-direct convolution bit for bit.
+integers up to 8, times the power of two the route scales by) and every sum
+exact in fp32, so the result must equal the direct convolution bit for bit.
+The route scales x and w by powers of two chosen from their largest
+magnitudes before rounding to fp16; inputs that fp16 could not hold
+unscaled (|x| up to 2^22, or down at 2^-20) must meet the same contract.
 """
 import numpy as np
 import pytest
@@ -123,3 +126,21 @@ def test_winograd_validation():
     assert B.conv2d_fwd_bf16(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), 1, 16, 8, 8, 16, 3, 1, 1, 3, None) == 7
     torch.cuda.synchronize()
     assert torch.isnan(y).all()
+
+
+@pytest.mark.parametrize("xs,ws", [(2.0 ** 20, 2.0 ** 10), (2.0 ** -20, 2.0 ** -12), (3.0e4, 1.0), (1.0, 2.0 ** -30),
+                                   (2.0 ** 60, 2.0 ** -70)],
+                         ids=["huge", "tiny", "x_3e4", "w_2^-30", "x_2^60_w_2^-70"])
+def test_winograd_magnitudes_outside_fp16(xs, ws):
+    """x and w scaled far outside fp16's range (V would overflow to inf, or U
+    and V sink into fp16 subnormals, without the route's own power-of-two
+    scaling): the result still meets 1e-3 * S of the direct oracle."""
+    wl = _wl(2, 64, 10, 16, 40, 1, seed=77)
+    t = synth.make_inputs(wl)
+    x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(t.x) * np.float32(xs))
+    w = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(t.w) * np.float32(ws))
+    b = (t.b * np.float32(xs * ws)).astype(np.float32)
+    t2 = synth.Tensors(x, w, b, t.seed)
+    got = _run(wl, t2)
+    assert np.isfinite(got).all()
+    _check_contract(wl, t2, got)
