@@ -42,7 +42,27 @@ struct SmallKPlan {
     int E;           // patch elements: C_in*K_d*Rt*Wt input values, then Rt*Wt zeros
     int kg, kpad;    // reduction length and its multiple of 16
     int tiles_h;     // tiles per (image, output depth)
+    // reciprocals of the divisors of the prologue's index arithmetic (see
+    // div_small): 16-byte pieces per input row, patch rows, K_d, kg
+    float inv_cpr, inv_rt, inv_dt, inv_kg;
+    float inv_taps, inv_kk, inv_k;      // ... and of K_d*K^2, K^2 and K (the tap table)
 };
+
+// Weight rows in LDS: kpad elements plus 8 (16 bytes) of pitch, so that the
+// 16-byte operand reads of consecutive rows spread over the banks.
+__host__ __device__ constexpr int w_pitch(int kpad) { return kpad + 8; }
+
+// a / b for 0 <= a < 2^20 and 1 <= b < 2^12, with inv_b = 1.0f / b: the
+// float quotient is within one of the true one, and one correction step
+// makes it exact.  Full-rate instructions only (a 24-bit multiply), where the
+// compiler's general 32-bit division takes ~20, several at quarter rate.
+__device__ __forceinline__ int div_small(int a, int b, float inv_b) {
+    int q = (int)((float)a * inv_b);
+    const int r = a - (int)__umul24((unsigned)q, (unsigned)b);
+    q += r >= b ? 1 : 0;
+    q -= r < 0 ? 1 : 0;
+    return q;
+}
 
 // KS: reduction steps of 16 (kpad / 16), a template parameter so the weight
 // operands take exactly 8 * KS registers.
@@ -53,8 +73,9 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     extern __shared__ __align__(16) uint8_t smem[];
     float *bias_s = reinterpret_cast<float *>(smem);                                 // [64]
     uint16_t *koff = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4);              // [kpad]
-    uint16_t *ws = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4 + kMaxK * 2);    // [64][kg] (room for [64][kpad])
-    uint16_t *patch = ws + kOcBlock * pl.kpad;                                        // [E]
+    uint16_t *ws = reinterpret_cast<uint16_t *>(smem + kOcBlock * 4 + kMaxK * 2);    // [64][w_pitch(kpad)]
+    const int WP = w_pitch(pl.kpad);
+    uint16_t *patch = ws + kOcBlock * WP;                                             // [E]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,32 +92,79 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
 
     // ---- stage the patch: line li = (channel, depth, row) holds input row
     // (id, ih) at columns X0 + iw; everything else, and the lines after the
-    // C_in*K_d*Rt input lines (the zero region), is zero
+    // C_in*K_d*Rt input lines (the zero region), is zero.  Every global load
+    // of the prologue (patch pieces, weights, bias) is issued before the
+    // first LDS write, so the workgroup waits for memory once, and the index
+    // arithmetic avoids general divisions: all workgroups of a launch run
+    // this prologue at the same time, before any of them stores an output.
     const int Dt = sh.Kd;
-    const int64_t HW = (int64_t)sh.H * sh.W;
-    const uint16_t *xn = x + (int64_t)n * sh.C * sh.D * HW;
-    if (pl.vec) {
+    const int HW = sh.H * sh.W;                                     // < 2^31 (smallk_supported)
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(x + (int64_t)n * sh.C * sh.D * HW, (uint32_t)((int64_t)sh.C * sh.D * HW * 2));
+    const int cpr = sh.W / 8;                                       // 16-byte pieces per input row (vec)
+    const int pieces = pl.vec ? sh.C * Dt * pl.Rt * cpr : 0;
+    const int id0 = od * sh.sd - sh.pd, ih0 = oh0 * sh.s - sh.p;
+    constexpr int kPer = 4;                                         // pieces per thread per batch
+    uint4 pv[kPer];
+    int pdst[kPer];                                                 // LDS element index, or -1
+    auto load_pieces = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = i0 + u * 256 + tid;
+            const int li = div_small(i, cpr, pl.inv_cpr), pc = i - li * cpr;
+            const int cd = div_small(li, pl.Rt, pl.inv_rt), ry = li - cd * pl.Rt;
+            const int c = Dt == 1 ? cd : div_small(cd, Dt, pl.inv_dt), dz = cd - c * Dt;
+            const int id = id0 + dz, ih = ih0 + ry;
+            const bool ok = i < pieces && id >= 0 && id < sh.D && ih >= 0 && ih < sh.H;
+            pdst[u] = ok ? li * pl.Wt + pl.X0 + pc * 8 : -1;
+            pv[u] = bload16(xr, ok ? (uint32_t)(((c * sh.D + id) * HW + ih * sh.W + pc * 8) * 2) : kOob, 0);
+        }
+    };
+    auto store_pieces = [&]() {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            if (pdst[u] >= 0) *reinterpret_cast<uint4 *>(patch + pdst[u]) = pv[u];
+    };
+    if (pl.vec) load_pieces(0);
+    // this workgroup's weight rows are one contiguous run of W_row (oc0 ..
+    // oc0 + nch_w - 1, kg each): read flat in 16-byte pieces when the run is
+    // 16-byte aligned (as it is for an aligned w), then placed into rows of
+    // pitch WP, zero past kg and past C_out, so that an operand is one
+    // aligned 16-byte read
+    const int nch_w = min(kOcBlock, sh.Co - oc0);
+    const int nel = nch_w * pl.kg;
+    const uint16_t *wsrc = w + (int64_t)oc0 * pl.kg;
+    const bool w16 = ((uintptr_t)wsrc % 16) == 0;
+    const int nw16 = w16 ? nel / 8 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wsrc, (uint32_t)nel * 2);
+    constexpr int kWPer = kOcBlock * kMaxK / 8 / 256;               // 16-byte weight pieces per thread (at most)
+    uint4 wv[kWPer];
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u) {
+        const int i = u * 256 + tid;
+        wv[u] = bload16(wr, i < nw16 ? (uint32_t)i * 16 : kOob, 0);
+    }
+    const float bias_v = (tid < kOcBlock && bias && oc0 + tid < sh.Co) ? bias[oc0 + tid] : 0.f;
+
+    // zero: the weight rows (padding), and the whole patch when the pieces
+    // fill it; then the data goes in
+    for (int i = tid; i < kOcBlock * WP / 8; i += 256) reinterpret_cast<uint4 *>(ws)[i] = make_uint4(0, 0, 0, 0);
+    if (pl.vec)
         for (int i = tid; i < pl.E / 8; i += 256) reinterpret_cast<uint4 *>(patch)[i] = make_uint4(0, 0, 0, 0);
-        __syncthreads();
-        const int cpr = sh.W / 8;                                   // 16-byte pieces per input row
-        const int pieces = sh.C * Dt * pl.Rt * cpr;
-        for (int i = tid; i < pieces; i += 256) {
-            const int li = i / cpr, pc = i - li * cpr;
-            const int ry = li % pl.Rt, cd = li / pl.Rt;
-            const int dz = cd % Dt, c = cd / Dt;
-            const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
-            if (id >= 0 && id < sh.D && ih >= 0 && ih < sh.H) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(xn + ((int64_t)c * sh.D + id) * HW +
-                                                                   (int64_t)ih * sh.W + pc * 8);
-                *reinterpret_cast<uint4 *>(patch + li * pl.Wt + pl.X0 + pc * 8) = v;
-            }
+    __syncthreads();
+    if (pl.vec) {
+        store_pieces();
+        for (int i0 = kPer * 256; i0 < pieces; i0 += kPer * 256) {
+            load_pieces(i0);
+            store_pieces();
         }
     } else {
         const int lines = (sh.C * Dt + 1) * pl.Rt;
+        const uint16_t *xn = x + (int64_t)n * sh.C * sh.D * HW;
         for (int li = wave; li < lines; li += 4) {
             const int ry = li % pl.Rt, cd = li / pl.Rt;
             const int dz = cd % Dt, c = cd / Dt;
-            const int id = od * sh.sd - sh.pd + dz, ih = oh0 * sh.s - sh.p + ry;
+            const int id = id0 + dz, ih = ih0 + ry;
             const bool row_ok = c < sh.C && id >= 0 && id < sh.D && ih >= 0 && ih < sh.H;
             const uint16_t *src = xn + ((int64_t)c * sh.D + (row_ok ? id : 0)) * HW + (int64_t)(row_ok ? ih : 0) * sh.W;
             uint16_t *dst = patch + (int64_t)li * pl.Wt;
@@ -106,57 +174,50 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
             }
         }
     }
-    // ---- tap offsets (padding rows k >= kg point at the zero region, which is
-    // longer than any pixel origin), weights (zero beyond C_out and kg), bias
+    // weight pieces into their rows: flat element f is (oc, k) = (f / kg, f % kg)
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u) {
+        const int i = u * 256 + tid;
+        if (i < nw16) {
+            int oc = div_small(8 * i, pl.kg, pl.inv_kg), k = 8 * i - oc * pl.kg;
+            const uint32_t v[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ws[oc * WP + k] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                if (++k == pl.kg) { k = 0; ++oc; }
+            }
+        }
+    }
+    for (int f = nw16 * 8 + tid; f < nel; f += 256) {
+        const int oc = f / pl.kg;
+        ws[oc * WP + (f - oc * pl.kg)] = wsrc[f];
+    }
+    // tap offsets (padding rows k >= kg point at the zero region, which is
+    // longer than any pixel origin), bias
     const int KK = sh.K * sh.K, taps = Dt * KK;
     for (int k = tid; k < pl.kpad; k += 256) {
         int off = sh.C * Dt * pl.Rt * pl.Wt;
         if (k < pl.kg) {
-            const int ic = k / taps;
+            const int ic = div_small(k, taps, pl.inv_taps);
             int r = k - ic * taps;
-            const int kd = r / KK; r -= kd * KK;
-            const int kh = r / sh.K, kw = r - kh * sh.K;
+            const int kd = div_small(r, KK, pl.inv_kk); r -= kd * KK;
+            const int kh = div_small(r, sh.K, pl.inv_k), kw = r - kh * sh.K;
             off = ((ic * Dt + kd) * pl.Rt + kh) * pl.Wt + kw;
         }
         koff[k] = (uint16_t)off;
     }
-    // this workgroup's weight rows are one contiguous run of W_row: copy it
-    // flat (16-byte pieces when the run is 16-byte aligned, as it is for an
-    // aligned w), the fragments below index it as [oc][kg]
-    {
-        const int nch_w = min(kOcBlock, sh.Co - oc0);
-        const int nel = nch_w * pl.kg;
-        const uint16_t *wsrc = w + (int64_t)oc0 * pl.kg;
-        int done = 0;
-        if (((uintptr_t)wsrc % 16) == 0) {
-            for (int i = tid; i < nel / 8; i += 256)
-                reinterpret_cast<uint4 *>(ws)[i] = reinterpret_cast<const uint4 *>(wsrc)[i];
-            done = nel / 8 * 8;
-        }
-        for (int i = done + tid; i < nel; i += 256) ws[i] = wsrc[i];
-    }
-    if (tid < kOcBlock) bias_s[tid] = (bias && oc0 + tid < sh.Co) ? bias[oc0 + tid] : 0.f;
+    if (tid < kOcBlock) bias_s[tid] = bias_v;
     __syncthreads();
 
     const int khalf = 8 * (lane >> 5);
-    // A operands: rows oc0 + ob*32 + lane%32, k = 16t + khalf .. +7, zero
-    // past C_out and past kg
-    const int nch_a = min(kOcBlock, sh.Co - oc0);
+    // A operands: rows ob*32 + lane%32 of the workgroup's block, k = 16s +
+    // khalf .. +7 (zero past C_out and past kg)
     uint4 a[2][KS];
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob) {
-        const int ocl = ob * 32 + (lane & 31);
+    for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            uint16_t e8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = 16 * s + khalf + e;
-                e8[e] = (ocl < nch_a && k < pl.kg) ? ws[ocl * pl.kg + k] : (uint16_t)0;
-            }
-            a[ob][s] = pack8(e8);
-        }
-    }
+        for (int s = 0; s < KS; ++s)
+            a[ob][s] = *reinterpret_cast<const uint4 *>(ws + (ob * 32 + (lane & 31)) * WP + 16 * s + khalf);
 
     const int64_t plane = sh.out_plane();
     const uint32_t q0 = (uint32_t)(((int64_t)od * sh.Ho + oh0) * sh.Wo);
@@ -281,7 +342,7 @@ bool vec_ok(const Shape &sh, const void *x) {
 }
 
 size_t smem_bytes_for(int kpad, int64_t E) {
-    return (size_t)kOcBlock * 4 + kMaxK * 2 + (size_t)kOcBlock * kpad * 2 + (size_t)E * 2;
+    return (size_t)kOcBlock * 4 + kMaxK * 2 + (size_t)kOcBlock * w_pitch(kpad) * 2 + (size_t)E * 2;
 }
 
 // Workgroups of smallk_kernel<KS> one CU holds by registers (the occupancy
@@ -360,6 +421,13 @@ SmallKPlan make_smallk_plan(const Shape &sh, bool vec) {
     patch_geom(sh, vec, pl.X0, pl.Wt);
     pl.E = (int)patch_elems(sh, TR, vec);
     pl.tiles_h = tiles;
+    pl.inv_cpr = 1.0f / (float)(sh.W / 8 > 0 ? sh.W / 8 : 1);
+    pl.inv_rt = 1.0f / (float)pl.Rt;
+    pl.inv_dt = 1.0f / (float)sh.Kd;
+    pl.inv_kg = 1.0f / (float)pl.kg;
+    pl.inv_taps = 1.0f / (float)(sh.Kd * sh.K * sh.K);
+    pl.inv_kk = 1.0f / (float)(sh.K * sh.K);
+    pl.inv_k = 1.0f / (float)sh.K;
     return pl;
 }
 
@@ -371,6 +439,7 @@ bool smallk_supported(const Shape &sh) {
     if (!sh.plain() || sh.nhwc || sh.kgemm() > kMaxK) return false;
     if (patch_elems(sh, 1, false) > kPatchElems) return false;
     if ((int64_t)kOcBlock * sh.out_plane() * 4 >= (INT64_C(1) << 31)) return false;   // one output block per buffer range
+    if ((int64_t)sh.C * sh.D * sh.H * sh.W * 2 >= (INT64_C(1) << 31)) return false;   // one input image per buffer range
     return (int64_t)sh.N * sh.Do * sh.Ho < (INT64_C(1) << 31);
 }
 
