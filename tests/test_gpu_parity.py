@@ -302,6 +302,11 @@ POINTWISE = [
     (2, 1, 96, (16, 16), 64),      # C_out below one channel block
     (2, 4, 256, (28, 28), 1024),   # the 1x1 workload's layer at N = 4
     (3, 2, 32, (2, 3, 4), 96),     # 3D pointwise
+    # the streaming kernel (C in {64, 128, 256}, C_out / 128 dividing 32): the
+    # pixels split evenly over 256 / (C_out / 128) contiguous ranges
+    (2, 1, 64, (8, 8), 128),       # 64 pixels over 256 ranges: most workgroups have none
+    (2, 3, 128, (10, 12), 256),    # 360 pixels over 128 ranges of 0 or 8
+    (2, 5, 64, (24, 40), 512),     # ranges of 72 or 80 pixels across image boundaries
 ]
 
 
