@@ -335,6 +335,10 @@ SMALL_K = [
     (2, 1, 2, (30, 32), 64, 7, 2, 3),      # W % 8 == 0: rows staged in 16-byte pieces, pad 3, K = 7
     (2, 2, 3, (17, 40), 96, 5, 1, 2),      # 16-byte staging, pad 2, ragged rows and channel block
     (3, 2, 4, (5, 8, 16), 64, 3, 2, 1),    # 3D, 16-byte staging, stride 2
+    (2, 1, 3, (6, 1024), 64, 3, 1, 1),     # 128 pieces a row: more patch pieces than one batch of loads
+    (2, 1, 2, (16, 24), 48, 8, 1, 0),      # 128 reduction rows (the limit), weights 3 pieces a thread
+    (3, 1, 1, (4, 6, 16), 32, 5, 1, 2),    # 3D K = 5: 125 rows, K_d = 5 patch planes
+    (2, 1, 3, (12, 16), 37, 3, 1, 1),      # 999 weights: a tail past the last 16-byte piece
 ]
 
 
@@ -346,6 +350,27 @@ def test_small_reduction_kernel(shape, integer):
     t = synth.make_inputs(wl, seed=N * 100 + C * 10 + K, integer=integer, with_bias=(Co % 2 == 0))
     y_ref, S = reference(wl, t)
     compare(_go(wl, t, "auto"), y_ref, S, TAU["bf16"], exact=integer, label="%s int=%s" % (shape, integer))
+
+
+def test_small_reduction_kernel_misaligned():
+    """x and w 2 bytes past a 16-byte boundary: the patch rows go element by
+    element and the weights through the element-wise path."""
+    wl = synth.Workload("smallk", 2, 2, 3, (20, 24), 64, 3, 1, 1, "bf16", "normal", 601)
+    t = synth.make_inputs(wl, seed=601, integer=True)
+
+    def mis(a):
+        buf = torch.empty(a.size + 8, dtype=torch.int16, device="cuda")
+        v = buf[1:1 + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda())
+        assert v.data_ptr() % 16 == 2
+        return v
+
+    x, w, b = mis(t.x), mis(t.w), dev(t.b, np.float32)
+    y = poisoned(wl.y_shape)
+    B.conv(x, w, b, 1, 1, out=y)
+    torch.cuda.synchronize()
+    y_ref, S = reference(wl, t)
+    compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], exact=True, label="smallk misaligned")
 
 
 # ---- packed weights reused across calls (conv2d_pack_weights_bf16 + _prepacked) ----
