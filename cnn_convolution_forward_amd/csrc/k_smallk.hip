@@ -95,8 +95,9 @@ void smallk_kernel(Shape sh, SmallKPlan pl, const uint16_t *__restrict__ x, cons
     // C_in*K_d*Rt input lines (the zero region), is zero.  Every global load
     // of the prologue (patch pieces, weights, bias) is issued before the
     // first LDS write, so the workgroup waits for memory once, and the index
-    // arithmetic avoids general divisions: all workgroups of a launch run
-    // this prologue at the same time, before any of them stores an output.
+    // arithmetic of the 16-byte path, the weights and the tap table avoids
+    // general divisions: all workgroups of a launch run this prologue at the
+    // same time, before any of them stores an output.
     const int Dt = sh.Kd;
     const int HW = sh.H * sh.W;                                     // < 2^31 (smallk_supported)
     const __amdgpu_buffer_rsrc_t xr =
