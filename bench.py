@@ -50,7 +50,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed steps first: about 40 ms of continuous work brings the clocks to steady state")
+                    help="untimed steps before the timed ones (after the clock-settling phase)")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="before the warm-up steps, run whole steps untimed until this much GPU time has passed: "
+                         "an idle GPU starts at a low clock and reaches its loaded clock after ~40 ms of "
+                         "continuous work (reported as clock_settle; 0 disables)")
     ap.add_argument("--workload", default="conv3x3_bf16")
     ap.add_argument("--route", default="auto", choices=["auto", "mfma", "valu", "explicit", "winograd", "plain"],
                     help="plain: the 2D entry point without a workspace (conv2d_fwd_bf16), AUTO's kernel choice")
@@ -292,8 +296,28 @@ def _batched(fn, steps, batches=5):
     return float(np.mean(means)), float(np.median(means)), float(np.min(means))
 
 
-def time_steps(runner, steps, warmup):
-    """After `warmup` untimed steps:
+def settle_clock(runner, ms):
+    """Run whole steps, untimed, in chunks of 16 until `ms` of GPU time has
+    passed (HIP events around each chunk); returns (steps run, GPU ms)."""
+    import torch
+    if ms <= 0:
+        return 0, 0.0
+    stream = torch.cuda.current_stream()
+    n, total = 0, 0.0
+    while total < ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(16):
+            runner.step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+        n += 16
+    return n, total
+
+
+def time_steps(runner, steps, warmup, settle_ms=0.0):
+    """After the clock-settling phase (settle_clock) and `warmup` untimed steps:
 
     A. exactly `steps` steps back to back, bracketed by synchronize (the wall
        clock, for `value`) and by one pair of HIP events (GPU time);
@@ -304,6 +328,7 @@ def time_steps(runner, steps, warmup):
     so the launch time cannot exceed the step's).
     """
     import torch
+    runner.settle = settle_clock(runner, settle_ms)
     for _ in range(warmup):
         runner.step()
     stream = torch.cuda.current_stream()
@@ -485,9 +510,9 @@ def describe(wl):
             "seed": wl.seed, "flop_per_step": wl.flops(), "algorithmic_bytes_per_step": algorithmic_bytes(wl)}
 
 
-def measure(wl, route, steps, warmup, backward=False, options=None):
+def measure(wl, route, steps, warmup, backward=False, options=None, settle_ms=0.0):
     runner = Runner(wl, route, backward=backward, options=options)
-    wall, gpu, per = time_steps(runner, steps, warmup)
+    wall, gpu, per = time_steps(runner, steps, warmup, settle_ms)
     return runner, wall, gpu, per
 
 
@@ -543,7 +568,7 @@ def main():
         print("the explicit route takes NCHW, fp32 output, no ReLU", file=sys.stderr)
         sys.exit(2)
     runner, wall, gpu, main_t = measure(wl, args.route, args.steps, args.warmup, backward=args.backward,
-                                        options=options)
+                                        options=options, settle_ms=args.settle_ms)
     # backward: the data and the weight gradient each cost the forward's FLOP
     flops = wl.flops() * (2 if args.backward else 1)
     value = flops * args.steps / wall / 1e12
@@ -567,7 +592,11 @@ def main():
                                 if runner._pre is not None and not args.backward else dominant, args.steps))})
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "steps": args.steps, "warmup": args.warmup,
+        "clock_settle": {"steps": runner.settle[0], "gpu_ms": round(runner.settle[1], 2),
+                         "note": "untimed whole steps run before the warm-up steps until the GPU had been busy "
+                                 "for --settle-ms (an idle GPU starts at a low clock)"},
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
         "gpu_ms_per_step": round(gpu / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded PCG64; x %s, w %s, b U[-1,1]%s)" % (
