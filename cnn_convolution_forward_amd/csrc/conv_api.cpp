@@ -179,6 +179,8 @@ conv_status_t explicit_bf16_sh(const Shape &sh, const uint16_t *x, const uint16_
     uint16_t *xcol = (uint16_t *)ws;
     hipError_t e = convfwd::launch_im2col_bf16(sh, x, xcol, hs);
     if (e != hipSuccess) return CONV_ERR_HIP;
+    if (convfwd::gemm_xcol_dma_supported(sh, xcol, w))
+        return to_status(convfwd::launch_gemm_xcol_dma_bf16(sh, w, xcol, bias, y, hs));
     if (convfwd::gemm_xcol_pw_supported(sh, xcol, w))
         return to_status(convfwd::launch_gemm_xcol_pw_bf16(sh, w, xcol, bias, y, hs));
     return to_status(convfwd::launch_gemm_xcol_bf16(sh, w, xcol, bias, y, hs));

@@ -51,6 +51,10 @@ hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol
 bool gemm_xcol_pw_supported(const Shape &sh, const void *xcol, const void *w);
 hipError_t launch_gemm_xcol_pw_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,
                                     float *y, hipStream_t st);
+// the explicit GEMM with direct-to-LDS loads in a ring of stage buffers (k_xcol_gemm.hip)
+bool gemm_xcol_dma_supported(const Shape &sh, const void *xcol, const void *w);
+hipError_t launch_gemm_xcol_dma_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,
+                                     float *y, hipStream_t st);
 hipError_t launch_gemm_xcol_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol,
                                  const float *bias, float *y, hipStream_t st);
 hipError_t launch_igemm_bf16(const Shape &sh, const uint16_t *x, const uint16_t *w,

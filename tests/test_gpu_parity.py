@@ -397,3 +397,35 @@ def test_pack_once_run_twice(shape):
         y_ref, S = reference(wl, tt)
         compare(y.cpu().numpy(), y_ref, S, TAU["bf16"], label="prepacked %s" % (shape,))
         assert torch.equal(y, y_ws)
+
+
+# ---- the explicit route's X_col GEMM (direct-to-LDS stage ring): reductions of
+# 1 to 18 stages (fewer stages than the ring holds, too), ragged pixel tiles,
+# tiles that straddle two images, C_out below, at and above one 128-row block
+
+XCOL_GEMM_2D = [
+    # (N, C, H, W, Co, K, s, p): C*K*K % 32 == 0 and N*Ho*Wo % 8 == 0
+    (3, 32, 12, 14, 70, 3, 1, 1),     # 9 stages, 504 pixels: last tile 120 wide
+    (2, 64, 10, 12, 200, 1, 1, 0),    # 2 stages, two channel blocks, the second ragged
+    (1, 32, 8, 8, 256, 1, 1, 0),      # 1 stage
+    (4, 32, 16, 16, 128, 3, 2, 1),    # stride 2
+    (8, 64, 7, 7, 96, 3, 1, 1),       # plane 49: tiles straddle images; 18 stages
+]
+
+
+@pytest.mark.parametrize("shape", XCOL_GEMM_2D, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("integer", [False, True])
+def test_explicit_xcol_gemm(shape, integer):
+    N, C, H, W, Co, K, s, p = shape
+    wl = synth.Workload("xcolgemm", 2, N, C, (H, W), Co, K, s, p, "bf16", "normal", 400)
+    t = synth.make_inputs(wl, seed=sum(shape), integer=integer)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "explicit"), y_ref, S, 0 if integer else TAU["bf16"], exact=integer,
+            label="%s explicit%s" % (shape, " int" if integer else ""))
+
+
+def test_explicit_xcol_gemm_3d():
+    wl = synth.Workload("xcolgemm3d", 3, 2, 32, (4, 6, 8), 40, 1, 1, 0, "bf16", "uniform", 401)
+    t = synth.make_inputs(wl, seed=7)
+    y_ref, S = reference(wl, t)
+    compare(_go(wl, t, "explicit"), y_ref, S, TAU["bf16"], label="3d explicit")
