@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--cpu-sample-images", type=int, default=0,
                     help="images in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--report", action="store_true", help="also time every workload/route (stderr)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only time plain streaming kernels (torch's fill, bf16 -> fp32 conversion, copy and sum, "
+                         "and hipMemsetAsync) at the 3x3 layer's byte counts: the HBM rates a plain kernel reaches "
+                         "on this chip, beside the 8 TB/s peak")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times): the "
                          "reference dispatch for scaling HBM byte counters")
@@ -532,6 +536,48 @@ def report_all(steps, warmup):
             print(json.dumps(line), file=sys.stderr, flush=True)
 
 
+def stream_probe(reps=50):
+    """HBM rates of plain streaming kernels on the 3x3 layer's buffers: x is
+    51.4 MB of bf16, y 102.8 MB of fp32.  Each op runs `reps` times back to
+    back between one pair of HIP events, after 20 untimed runs; one JSON line
+    per op with its bytes moved and TB/s."""
+    import torch
+    stream = torch.cuda.current_stream()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemsetAsync.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+    ops = []
+    # the 3x3 layer's sizes (x and y together fit the 256 MB memory-side
+    # cache, as in back-to-back launches of the layer), then 8x larger
+    # buffers that do not
+    for scale, tag in ((1, "3x3-layer size"), (8, "8x the 3x3 layer")):
+        n_x = 64 * 128 * 56 * 56 * scale
+        xb = torch.ones(n_x, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty(n_x, dtype=torch.float32, device="cuda")
+        y2 = torch.empty_like(y)
+        ops += [
+            ("fill fp32 y (write only), " + tag, lambda y=y: y.fill_(1.0), 4 * n_x),
+            ("hipMemsetAsync y (write only), " + tag,
+             lambda y=y, n=n_x: hip.hipMemsetAsync(ctypes.c_void_p(y.data_ptr()), 0, 4 * n,
+                                                    ctypes.c_void_p(stream.cuda_stream)), 4 * n_x),
+            ("copy fp32 y -> y2 (read 1 : write 1), " + tag, lambda y=y, y2=y2: y2.copy_(y), 8 * n_x),
+            ("convert bf16 x -> fp32 y (read 1 : write 2), " + tag, lambda y=y, xb=xb: y.copy_(xb), 6 * n_x),
+        ]
+    for name, fn, nbytes in ops:
+        for _ in range(20):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / reps
+        print(json.dumps({"op": name, "bytes": nbytes, "us": round(t * 1e6, 2),
+                          "TB/s": round(nbytes / t / 1e12, 3), "frac_of_8TB/s": round(nbytes / t / 8e12, 3)}),
+              flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -542,6 +588,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.stream_probe:
+        stream_probe()
+        return
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

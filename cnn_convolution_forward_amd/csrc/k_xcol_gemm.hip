@@ -11,8 +11,7 @@
 // ahead of the MFMAs.  On the 3x3 layer (462 MB of X_col) this takes 148 us
 // against 187 us on the tiled pointwise kernel, which loads one stage ahead
 // through registers.  A deeper ring (4 or 5 stages) did not help, and a build
-// without the output stores took 129 us: the X_col reads run at ~3.6 TB/s,
-// about the rate of a plain 512 MiB reduction on the same chip (3.7 TB/s).
+// without the output stores took 129 us (X_col read at ~3.6 TB/s).
 //
 // Tile: 128 output channels x up to TN = 256 pixels (8 columns of 32), four
 // waves in a 2 x 2 grid, each 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (64 x 128).
