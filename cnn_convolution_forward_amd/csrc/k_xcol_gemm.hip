@@ -9,8 +9,8 @@
 // input's bytes.  Both operands travel global -> LDS by direct-to-LDS loads
 // (no registers, no VALU work) into a ring of NS stage buffers, NS - 1 stages
 // ahead of the MFMAs.  On the 3x3 layer (462 MB of X_col) this takes 148 us
-// against 187 us on the tiled pointwise kernel, which loads one stage ahead
-// through registers.  A deeper ring (4 or 5 stages) did not help, and a build
+// by events (160 us, the rocprofv3 median) against 187 us on the tiled
+// pointwise kernel, which loads one stage ahead through registers.  A deeper ring (4 or 5 stages) did not help, and a build
 // without the output stores took 129 us (X_col read at ~3.6 TB/s).
 //
 // Tile: 128 output channels x up to TN = 256 pixels (8 columns of 32), four
