@@ -120,7 +120,10 @@ __device__ __forceinline__ void cg_mfma(f32x16_t (&acc)[(Geo<D, DL>::J)], const 
 // Column step q.  The fragments of kernel rows 0, 1 and 2 of column q are
 // three LDS reads, one input row apart (ib, tb, ub).  A step first issues
 // the reads of column q + 1, then the 9 (or fewer) MFMAs of column q, so the
-// reads have a column of MFMA work to arrive.
+// reads have a column of MFMA work to arrive.  A scheduling barrier keeps the
+// compiler from sinking those reads between the column's MFMAs, where they
+// had only one or two MFMAs to arrive (0.8% faster on the 3x3 layer, five
+// alternating rounds on one box).
 template <int D, int DL, int q, class Mid>
 __device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const uint4 (&A)[9], uint4 (&B0)[2],
                                        uint4 (&T1)[2], uint4 (&T2)[2], const uint8_t *ib, const uint8_t *tb,
@@ -130,6 +133,7 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const u
         B0[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ib + (q + 1) * kPix);
         T1[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(tb + (q + 1) * kPix);
         T2[(q + 1) & 1] = *reinterpret_cast<const uint4 *>(ub + (q + 1) * kPix);
+        __builtin_amdgcn_sched_barrier(0);
     }
     cg_mfma<D, DL, 0>(acc, A, B0[q & 1], q);
     cg_mfma<D, DL, 1>(acc, A, T1[q & 1], q);
