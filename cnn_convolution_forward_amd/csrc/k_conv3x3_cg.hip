@@ -104,6 +104,15 @@ __device__ __forceinline__ void zero_halo(uint8_t *dst, int nb, int tid) {
     }
 }
 
+template <bool V>
+struct BoolC {
+    static constexpr bool value = V;
+};
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 // The MFMAs of input-fragment column q (column c0 - 1 + q of this wave's
 // range) and kernel row rr: the fragment serves output fragment j = q - kw
 // for the three horizontal taps kw.
@@ -138,7 +147,16 @@ __device__ __forceinline__ void cg_col(f32x16_t (&acc)[(Geo<D, DL>::J)], const u
     cg_mfma<D, DL, 0>(acc, A, B0[q & 1], q);
     cg_mfma<D, DL, 1>(acc, A, T1[q & 1], q);
     cg_mfma<D, DL, 2>(acc, A, T2[q & 1], q);
-    if constexpr (q == Q / 2) mid();
+    // the middle-of-stage work in five parts over the columns from Q/2 - 1
+    // (the last ones share the final column when Q is small): the input
+    // fragments' transposing writes in two halves, the next weights' copies,
+    // the input loads in two halves.  In one piece at column Q/2 the stage
+    // took 0.5-1% longer (five alternating rounds on one box).
+    if constexpr (q == (Q / 2 - 1 < Q - 1 ? Q / 2 - 1 : Q - 1)) mid(IntC<0>{});
+    if constexpr (q == (Q / 2 < Q - 1 ? Q / 2 : Q - 1)) mid(IntC<1>{});
+    if constexpr (q == (Q / 2 + 1 < Q - 1 ? Q / 2 + 1 : Q - 1)) mid(IntC<2>{});
+    if constexpr (q == (Q / 2 + 2 < Q - 1 ? Q / 2 + 2 : Q - 1)) mid(IntC<3>{});
+    if constexpr (q == (Q / 2 + 3 < Q - 1 ? Q / 2 + 3 : Q - 1)) mid(IntC<4>{});
     if constexpr (q + 1 < Q) cg_col<D, DL, q + 1>(acc, A, B0, T1, T2, ib, tb, ub, mid);
 }
 
@@ -171,10 +189,6 @@ struct EpiGeo {
     static constexpr int BYTES = (kEpiOc - 1) * P * 4 + TAIL;
 };
 
-template <bool V>
-struct BoolC {
-    static constexpr bool value = V;
-};
 
 template <int D, int OUT, int NHWC, int DL>
 __device__ __forceinline__ void cg_epilogue(uint8_t *smem, const f32x16_t (&acc)[(Geo<D, DL>::J)], float *y, int n,
@@ -358,23 +372,23 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
     uint4 xin[8];
     // only the lanes that own a unit load (a wave with none issues nothing:
     // the loads of idle lanes would still occupy the address units)
-    auto load_x = [&](int s) {
+    auto load_x = [&](int s, int e0 = 0, int e1 = 8) {
         if (!in_active) return;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xin[e] = bload16(xr, ivoff + e * e_bytes, (uint32_t)s * stage_bytes);
+        for (int e = e0; e < e1; ++e) xin[e] = bload16(xr, ivoff + e * e_bytes, (uint32_t)s * stage_bytes);
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](int buf, int j0 = 0, int j1 = 8) {
         if (!in_active) return;
         if (NHWC) {
             uint8_t *dst = ibuf + buf * G::IN_BYTES + idst;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(dst + j * kPix) = xin[j];
+            for (int j = j0; j < j1; ++j) *reinterpret_cast<uint4 *>(dst + j * kPix) = xin[j];
             return;
         }
         const uint32_t *v = reinterpret_cast<const uint32_t *>(xin);   // v[e*4 + j/2]: channel e, pixels j, j+1
         uint8_t *dst = ibuf + buf * G::IN_BYTES + idst;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = j0; j < j1; ++j) {
             const int dj = j >> 1, hj = j & 1;
             uint4 o;
             o.x = pack_halves(v[0 * 4 + dj], hj, v[1 * 4 + dj], hj);
@@ -457,12 +471,21 @@ void conv3x3cg_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict
         // is used only has to cover the input loads, and loads complete in
         // issue order, so the copies are waited for separately at the end
         // of the stage, with the next input still in flight.
-        auto mid = [&]() {
+        auto mid = [&](auto ph) {
+            constexpr int P = decltype(ph)::value;
             if (more) {
-                CONV3X3_WAIT_VMCNT(0);
-                store_x(b ^ 1);
-                dma_w(s + 1, b ^ 1);
-                if (s + 2 < S) load_x(s + 2);
+                if constexpr (P == 0) {
+                    CONV3X3_WAIT_VMCNT(0);
+                    store_x(b ^ 1, 0, 4);
+                }
+                if constexpr (P == 1) store_x(b ^ 1, 4, 8);
+                if constexpr (P == 2) dma_w(s + 1, b ^ 1);
+                if constexpr (P == 3) {
+                    if (s + 2 < S) load_x(s + 2, 0, 4);
+                }
+                if constexpr (P == 4) {
+                    if (s + 2 < S) load_x(s + 2, 4, 8);
+                }
             }
         };
         // raised priority over the MFMA columns: while this wave is between
@@ -623,7 +646,7 @@ void conv3x3cg_gp_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
         T1[0] = *reinterpret_cast<const uint4 *>(tb);
         T2[0] = *reinterpret_cast<const uint4 *>(ub);
         __builtin_amdgcn_s_setprio(1);
-        cg_col<D, 1, 0>(acc, A, B0, T1, T2, ib, tb, ub, []() {});
+        cg_col<D, 1, 0>(acc, A, B0, T1, T2, ib, tb, ub, [](auto) {});
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();            // buffers free for the next stage
     }
@@ -762,11 +785,6 @@ __device__ __forceinline__ void cgp_epilogue(float *epi, const f32x16_t (&acc)[J
         if (p + 1 < NP) __syncthreads();
     }
 }
-
-template <int V>
-struct IntC {
-    static constexpr int value = V;
-};
 
 // LDS of the persistent kernel: weight buffers 0 and 1, input buffers 0 and
 // 1, and the epilogue image from EPI on (above weight buffer 0 when that fits
