@@ -71,7 +71,7 @@ template <int NS, int TN>
 __global__ __launch_bounds__(256, 2)
 void xcol_gemm_kernel(const uint16_t *__restrict__ xcol, const uint16_t *__restrict__ w,
                       const float *__restrict__ bias, float *__restrict__ y,
-                      int K, int Co, int plane, int J, int NC, int NR, int ncb, int out_bf16, int relu) {
+                      int K, int Co, int plane, int J, int NC, int NR, int ncb, int remap, int out_bf16, int relu) {
     constexpr int kBStage = kXK * TN * 2;          // 16 KB at TN = 256
     constexpr int kStage = kAStage + kBStage;
     constexpr int TC = TN / 32;                    // 32-pixel columns per full tile
@@ -91,7 +91,13 @@ void xcol_gemm_kernel(const uint16_t *__restrict__ xcol, const uint16_t *__restr
     // walked in tiles of at most TC columns.  The launcher makes each range
     // one tile; 512 workgroups walking two or three tiles each (no partly
     // filled last round) measured slower on the 3x3 layer (157 against 148 us)
-    const int ob = (int)blockIdx.x % ncb, r = (int)blockIdx.x / ncb;
+    // with remap, XCD x (block b runs on XCD b % 8) takes the contiguous
+    // logical range [x T/8, (x+1) T/8), so the ncb channel blocks of a column
+    // range share one XCD's L2 and read their X_col tile from HBM once
+    const int T = NR * ncb;
+    int L = (int)blockIdx.x;
+    if (remap) L = (L & 7) * (T >> 3) + (L >> 3);
+    const int ob = L % ncb, r = L / ncb;
     const int c_begin = (int)((int64_t)r * NC / NR), c_end = (int)((int64_t)(r + 1) * NC / NR);
     const int m0 = ob * kXM;
     const int S = K / kXK;
@@ -261,8 +267,9 @@ hipError_t launch_gemm_xcol_dma_bf16(const Shape &sh, const uint16_t *w, const u
     // one range of at most kTN / 32 columns per workgroup (ranges balanced
     // when NC is not a multiple of 8)
     const int NR = (NC + kTN / 32 - 1) / (kTN / 32);
+    const int remap = (ncb > 1 && (NR * ncb) % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((xcol_gemm_kernel<kNS, kTN>), dim3((unsigned)(NR * ncb)), dim3(256), 0, st, xcol, w, bias, y,
-                       (int)sh.xcol_rows(), sh.Co, (int)sh.out_plane(), J, NC, NR, ncb, sh.out_bf16, sh.relu);
+                       (int)sh.xcol_rows(), sh.Co, (int)sh.out_plane(), J, NC, NR, ncb, remap, sh.out_bf16, sh.relu);
     return hipGetLastError();
 }
 

@@ -410,6 +410,8 @@ XCOL_GEMM_2D = [
     (1, 32, 8, 8, 256, 1, 1, 0),      # 1 stage
     (4, 32, 16, 16, 128, 3, 2, 1),    # stride 2
     (8, 64, 7, 7, 96, 3, 1, 1),       # plane 49: tiles straddle images; 18 stages
+    (4, 32, 16, 16, 256, 1, 1, 0),    # two channel blocks, 8 workgroups: XCD-contiguous block order
+    (8, 32, 16, 16, 384, 3, 1, 1),    # three channel blocks, 24 workgroups, XCD-contiguous order
 ]
 
 
