@@ -181,8 +181,6 @@ conv_status_t explicit_bf16_sh(const Shape &sh, const uint16_t *x, const uint16_
     if (e != hipSuccess) return CONV_ERR_HIP;
     if (convfwd::gemm_xcol_dma_supported(sh, xcol, w))
         return to_status(convfwd::launch_gemm_xcol_dma_bf16(sh, w, xcol, bias, y, hs));
-    if (convfwd::gemm_xcol_pw_supported(sh, xcol, w))
-        return to_status(convfwd::launch_gemm_xcol_pw_bf16(sh, w, xcol, bias, y, hs));
     return to_status(convfwd::launch_gemm_xcol_bf16(sh, w, xcol, bias, y, hs));
 }
 

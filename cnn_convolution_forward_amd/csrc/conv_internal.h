@@ -47,10 +47,6 @@ struct Shape {
 
 // Kernel launchers.  Each enqueues on `st` and returns hipGetLastError().
 hipError_t launch_im2col_bf16(const Shape &sh, const uint16_t *x, uint16_t *xcol, hipStream_t st);
-// the explicit GEMM on the tiled pointwise kernel (X_col rows as its channels)
-bool gemm_xcol_pw_supported(const Shape &sh, const void *xcol, const void *w);
-hipError_t launch_gemm_xcol_pw_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,
-                                    float *y, hipStream_t st);
 // the explicit GEMM with direct-to-LDS loads in a ring of stage buffers (k_xcol_gemm.hip)
 bool gemm_xcol_dma_supported(const Shape &sh, const void *xcol, const void *w);
 hipError_t launch_gemm_xcol_dma_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,

@@ -78,8 +78,7 @@ void conv1x1_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__
 
     // loader units: A u -> (row u/4, k-quad u%4); B u -> (k row u/16, 8-pixel group u%16).
     // Element (k, image n, pixel q) of B is at x[k * xcs + n * xns + q]: NCHW
-    // has xcs = plane, xns = C * plane; the explicit route's X_col has xcs = N
-    // * plane (one row per reduction index), xns = plane.
+    // has xcs = plane, xns = C * plane.
     uint32_t a_off[2], b_off[2];
     const uint32_t b_step = (uint32_t)(kBK * xcs * 2);
 #pragma unroll
@@ -539,31 +538,6 @@ hipError_t launch_conv1x1_bf16(const Shape &sh, const uint16_t *x, const uint16_
     }
     hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, x, w, bias, y, sh.C, sh.Co,
                        plane, P, npt, ncb, remap, sh.out_bf16, sh.relu, (int64_t)plane, (int64_t)sh.C * plane);
-    return hipGetLastError();
-}
-
-// The explicit route's GEMM on the tiled kernel: Y_n = W_row @ X_col[:, image
-// n's columns] ("Why use matrix multiplication for convolution", 2.3) is a
-// pointwise layer whose C_in * K^dims input "channels" are the X_col rows,
-// J = N * plane elements apart.  Groups 1, NCHW, an fp32 or bf16 output;
-// X_col, W_row and y below 2 GiB, 16-byte aligned X_col and w.
-bool gemm_xcol_pw_supported(const Shape &sh, const void *xcol, const void *w) {
-    const int64_t rows = sh.xcol_rows(), J = sh.pixels(), plane = sh.out_plane();
-    return sh.G == 1 && !sh.nhwc && rows % kBK == 0 && plane % 8 == 0 && plane < (INT64_C(1) << 31) &&
-           rows * J * 2 < (INT64_C(1) << 31) && (int64_t)sh.Co * rows * 2 < (INT64_C(1) << 31) &&
-           sh.y_elems() * 4 < (INT64_C(1) << 31) && ((uintptr_t)xcol % 16) == 0 && ((uintptr_t)w % 16) == 0;
-}
-
-hipError_t launch_gemm_xcol_pw_bf16(const Shape &sh, const uint16_t *w, const uint16_t *xcol, const float *bias,
-                                    float *y, hipStream_t st) {
-    const int64_t P = sh.pixels();
-    const int plane = (int)sh.out_plane();
-    const int npt = (int)((P + kBN - 1) / kBN);
-    const int ncb = (sh.Co + kBM - 1) / kBM;
-    const int64_t T = (int64_t)npt * ncb;
-    const int remap = (T % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(conv1x1_kernel, dim3((unsigned)T), dim3(256), 0, st, xcol, w, bias, y, (int)sh.xcol_rows(),
-                       sh.Co, plane, P, npt, ncb, remap, sh.out_bf16, sh.relu, P, (int64_t)plane);
     return hipGetLastError();
 }
 
