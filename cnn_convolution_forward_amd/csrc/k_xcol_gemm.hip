@@ -10,8 +10,9 @@
 // (no registers, no VALU work) into a ring of NS stage buffers, NS - 1 stages
 // ahead of the MFMAs.  On the 3x3 layer (462 MB of X_col) this takes 148 us
 // by events (160 us, the rocprofv3 median) against 187 us on the tiled
-// pointwise kernel, which loads one stage ahead through registers.  A deeper ring (4 or 5 stages) did not help, and a build
-// without the output stores took 129 us (X_col read at ~3.6 TB/s).
+// pointwise kernel, which loads one stage ahead through registers.  A deeper
+// ring (4 or 5 stages) did not help, and a build without the output stores
+// took 129 us (X_col read at ~3.6 TB/s).
 //
 // Tile: 128 output channels x up to TN = 256 pixels (8 columns of 32), four
 // waves in a 2 x 2 grid, each 2 x 4 v_mfma_f32_32x32x16_bf16 tiles (64 x 128).
@@ -22,8 +23,9 @@
 // bank groups).  Three stage buffers (72 KB): two workgroups per CU, each
 // with two stages in flight.  The swizzles are applied on the global side:
 // each lane of a direct-to-LDS load picks the global 16 bytes that belong at
-// its fixed LDS slot.  B fragments come from ds_read_b64_tr_b16 transposing reads (pixels
-// contiguous in X_col, the operand wants 8 consecutive k per pixel).
+// its fixed LDS slot.  B fragments come from ds_read_b64_tr_b16 transposing
+// reads (pixels contiguous in X_col, the operand wants 8 consecutive k per
+// pixel).
 //
 // Epilogue: accumulators start at the bias; fp32 (or bf16) stores from the
 // accumulators, 32 lanes on 32 consecutive pixels of one channel (y is NCHW:
@@ -90,8 +92,8 @@ void xcol_gemm_kernel(const uint16_t *__restrict__ xcol, const uint16_t *__restr
     // are split into NR contiguous ranges of floor or ceil(NC / NR) columns,
     // walked in tiles of at most TC columns.  The launcher makes each range
     // one tile; 512 workgroups walking two or three tiles each (no partly
-    // filled last round) measured slower on the 3x3 layer (157 against 148 us)
-    // with remap, XCD x (block b runs on XCD b % 8) takes the contiguous
+    // filled last round) measured slower on the 3x3 layer (157 against 148 us).
+    // With remap, XCD x (block b runs on XCD b % 8) takes the contiguous
     // logical range [x T/8, (x+1) T/8), so the ncb channel blocks of a column
     // range share one XCD's L2 and read their X_col tile from HBM once
     const int T = NR * ncb;
